@@ -1,0 +1,184 @@
+/*
+ * mm.h -- C ABI of the MI355X (gfx950) quantized skinny MUL_MAT library.
+ *
+ * The library computes the ggml-style MUL_MAT at LLM-decode shapes,
+ *
+ *     dst[M x N] = src1[M x K] . src0[N x K]^T        (row-major, contiguous)
+ *
+ * for the three kinds named in llama.cpp PR 1632 "mulmat tune", Introduction:
+ * F32 x F32, F16 x F32 and quantized (here Q4_0) x F32.  For the quantized
+ * kind, src1 is first quantized to Q8_0 (the INIT stage of that page; the
+ * "wdata" buffer of the Arm China NUMA article, MulMat operator section) and
+ * the product is taken between the Q4_0 weights and that Q8_0 copy.
+ *
+ * Block formats (not printed on the pages, which only name the types; the
+ * library is specified against the ggml layouts):
+ *   Q4_0: 18 bytes per 32 values: fp16 d (little endian), then 16 bytes;
+ *         byte i holds code q[i] in its low nibble and q[i+16] in its high
+ *         nibble; value = d * (q - 8).
+ *         d = (signed absmax) / -8, q = clamp(floor(x/d + 8.5), 0, 15).
+ *   Q8_0: 34 bytes per 32 values: fp16 d, then 32 int8 codes; value = d * q.
+ *         d = absmax / 127, q = round(x/d) (half away from zero).
+ *   In both, x/d is evaluated as x * (1/d) with one correctly rounded fp32
+ *   reciprocal per block, codes come from the fp32 d, and only the stored d
+ *   is rounded to fp16 (round to nearest even).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA
+ *     memory).  Sizes are element counts.  Calls are asynchronous on
+ *     `stream` (a hipStream_t; NULL = the null stream) and never synchronise.
+ *   - The caller owns every buffer, including the workspace `ws`; the
+ *     library allocates no device memory and keeps no per-call state.  Calls
+ *     on different streams may run concurrently if their buffers differ.
+ *   - Arguments are validated on the host before any HIP call; on error the
+ *     function returns a negative mm_status and launches nothing.
+ *   - dst is overwritten (never accumulated into).  M == 0 or N == 0 is a
+ *     no-op; K == 0 writes zeros (the empty sum).
+ *   - Results are deterministic run to run: there are no floating-point
+ *     atomics; split-K partial sums are added in a fixed order.
+ */
+#ifndef QSG_MM_H
+#define QSG_MM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mm_status {
+    MM_OK = 0,
+    MM_ERR_NULL = -1,      /* a required pointer is NULL                         */
+    MM_ERR_SHAPE = -2,     /* negative size, K % 32 != 0 for a block type, or a size too large */
+    MM_ERR_ALIGN = -3,     /* pointer not aligned as documented per entry point  */
+    MM_ERR_WORKSPACE = -4, /* ws_bytes smaller than mm_mul_mat_workspace_size()  */
+    MM_ERR_ALIAS = -5,     /* dst (or ws) overlaps an input, or ws overlaps dst  */
+    MM_ERR_DEVICE = -6,    /* current device is not gfx950                       */
+    MM_ERR_HIP = -7,       /* a HIP runtime call or launch failed                */
+    MM_ERR_ARG = -8        /* unknown type or variant                            */
+} mm_status;
+
+typedef enum mm_type {
+    MM_TYPE_F32 = 0,
+    MM_TYPE_F16 = 1,
+    MM_TYPE_Q4_0 = 2,
+    MM_TYPE_Q8_0 = 3
+} mm_type;
+
+/*
+ * mm_quantize_q4_0 -- x[nrows][k] (f32) -> y[nrows][k/32] Q4_0 blocks (18 B each).
+ * Weight quantisation (setup, outside the decode loop): the Q4_0 encoding
+ * above.  k % 32 == 0.  x must be 16-byte aligned; y needs 2-byte alignment.
+ * y must not overlap x.
+ */
+int mm_quantize_q4_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream);
+
+/*
+ * mm_quantize_q8_0 -- x[nrows][k] (f32) -> y[nrows][k/32] Q8_0 blocks (34 B each).
+ * The activation quantisation that the Q4_0 product applies to src1 (the
+ * INIT stage / wdata): its bytes are identical to the Q8_0 content
+ * mm_mul_mat_q4_0_f32 computes internally.  k % 32 == 0.  x 16-byte aligned,
+ * y 2-byte aligned, no overlap.
+ */
+int mm_quantize_q8_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream);
+
+/*
+ * mm_mul_mat_q4_0_f32 -- dst[M][N] (f32) = Q8_0(src1)[M][K] . Q4_0 src0[N][K]^T.
+ *   src0: N rows of K/32 Q4_0 blocks (row pitch 18*K/32 bytes), 2-byte aligned
+ *         (4-byte alignment and an even K/32 select the fast load path).
+ *   src1: f32 [M][K], 16-byte aligned.  dst: f32 [M][N], 4-byte aligned.
+ *   K % 32 == 0.
+ *   ws:   workspace of at least mm_mul_mat_workspace_size(MM_TYPE_Q4_0, M, N, K)
+ *         bytes, 256-byte aligned; holds the Q8_0 wdata and any split-K
+ *         partial sums.  Its content on entry is irrelevant.
+ * dst[m][n] = sum_b f32(d_w[n][b]) * f32(d_a[m][b]) * S_b[m][n], with the
+ * int32 block dot S_b = sum_j (q4 - 8) * q8, accumulated in fp32.
+ */
+int mm_mul_mat_q4_0_f32(const void* src0, const float* src1, float* dst,
+                        int64_t M, int64_t N, int64_t K,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The two stages of mm_mul_mat_q4_0_f32, exposed separately (llama.cpp PR
+ * 1632 "mulmat tune", Introduction: the quantized kind runs an INIT stage
+ * that converts src1, then the COMPUTE stage).  mm_mul_mat_q4_0_f32 is
+ * exactly mm_q4_0_init followed by mm_q4_0_compute on the same stream.
+ *
+ * mm_q4_0_init: quantizes src1 f32 [M][K] (16-byte aligned) to Q8_0 into the
+ *   workspace (layout private to the library; the content equals
+ *   mm_quantize_q8_0 of src1) and prepares the split-K state.  ws as for
+ *   mm_mul_mat_q4_0_f32 with the same (M, N, K).
+ * mm_q4_0_compute: dst[M][N] = wdata . src0^T from a workspace that an
+ *   mm_q4_0_init with the SAME (M, N, K) filled earlier on this stream (or
+ *   that a completed mm_q4_0_compute left behind: compute leaves the wdata
+ *   unchanged).  One init can thus serve several src0 of the same shape
+ *   (e.g. the q, k and v projections of one activation).  Calls that share a
+ *   workspace must not overlap in time.
+ */
+int mm_q4_0_init(const float* src1, void* ws, int64_t M, int64_t N, int64_t K,
+                 size_t ws_bytes, void* stream);
+int mm_q4_0_compute(const void* src0, float* dst, int64_t M, int64_t N, int64_t K,
+                    const void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mm_mul_mat_f16_f32 -- dst[M][N] = src1[M][K] . f32(src0[N][K])^T, fp32 accumulation.
+ *   src0: IEEE binary16 [N][K], 2-byte aligned.  src1: f32 [M][K], 4-byte
+ *   aligned.  dst: f32, 4-byte aligned.  Any K >= 0.  For M <= 16 src1 is
+ *   used in f32; for larger M it is rounded to binary16 for the f16 MFMA
+ *   (relative effect about 1e-4, inside the 1e-3 bound of this kind).
+ *   ws: mm_mul_mat_workspace_size(MM_TYPE_F16, ...) bytes (may be 0).
+ */
+int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst,
+                       int64_t M, int64_t N, int64_t K,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mm_mul_mat_f32 -- dst[M][N] = src1[M][K] . src0[N][K]^T, all f32, fp32 FMA.
+ *   All pointers 4-byte aligned.  Any K >= 0.
+ *   ws: mm_mul_mat_workspace_size(MM_TYPE_F32, ...) bytes (may be 0).
+ */
+int mm_mul_mat_f32(const float* src0, const float* src1, float* dst,
+                   int64_t M, int64_t N, int64_t K,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace the product of `type` (F32, F16 or Q4_0) needs at this
+ * shape; 0 for an invalid shape or type.  Pure host function. */
+size_t mm_mul_mat_workspace_size(int type, int64_t M, int64_t N, int64_t K);
+
+/* Bytes of one row of K values of `type`; -1 if K is invalid for it. */
+int64_t mm_row_bytes(int type, int64_t K);
+
+/* Static description of a status code.  Never NULL. */
+const char* mm_status_string(int status);
+
+/*
+ * mm_dispatch -- the kernel choice mm_mul_mat_* makes at this shape (pure
+ * host function).  Writes up to 4 ints to out (may be NULL):
+ *   out[0] variant: 1 = narrow-M kernel, 2 = wide-M (MFMA) kernel
+ *   out[1] split-K factor (1 = none)
+ *   out[2] rows of src1 per pass (narrow) or output tile rows (wide)
+ *   out[3] output tile columns (wide) or src0 rows per wave (narrow)
+ * Returns MM_OK or MM_ERR_SHAPE / MM_ERR_ARG.
+ */
+int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);
+
+/*
+ * mm_debug_mul_mat -- test entry: the same product as mm_mul_mat_<type>,
+ * with the kernel forced (variant 0 = as dispatched, 1 = narrow, 2 = wide)
+ * and, for Q4_0, the int32 block dots S_b[m][n][b] of output columns
+ * n0 <= n < n1 also written to `dots` ([M][n1-n0][K/32] int32, may be NULL)
+ * by the production kernel itself.  Workspace: mm_debug_workspace_size().
+ */
+int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst,
+                     int32_t* dots, int64_t M, int64_t N, int64_t K,
+                     int64_t n0, int64_t n1, int variant,
+                     void* ws, size_t ws_bytes, void* stream);
+
+size_t mm_debug_workspace_size(int type, int64_t M, int64_t N, int64_t K, int variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSG_MM_H */

@@ -1,0 +1,220 @@
+// extern "C" entry points declared in include/mm.h.
+//
+// Each entry point validates its arguments on the host (plan.cpp) before any
+// HIP call, checks once per device that it runs on gfx950, then enqueues the
+// kernels on the caller's stream without synchronising.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/mm.h"
+#include "kernels.h"
+#include "plan.h"
+
+using namespace qsg;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MM_ERR_DEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MM_ERR_HIP;
+    state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? MM_OK : MM_ERR_DEVICE;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MM_OK : MM_ERR_HIP; }
+
+Q4Args q4_args(const Plan& p, const void* src0, float* dst, int32_t* dots, int64_t M,
+               int64_t N, int64_t K, int64_t n0, int64_t n1, void* ws) {
+  uint8_t* base = (uint8_t*)ws;
+  Q4Args a;
+  a.w = (const uint8_t*)src0;
+  a.aq = (const int8_t*)(base + p.off_aq);
+  a.ad = (const float*)(base + p.off_ad);
+  a.ab = (const int32_t*)(base + p.off_ab);
+  a.dst = dst;
+  a.part = p.split > 1 ? (float*)(base + p.off_part) : nullptr;
+  a.tick = p.split > 1 ? (uint32_t*)(base + p.off_tick) : nullptr;
+  a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  a.dots = dots; a.n0 = (int)n0; a.n1 = (int)n1;
+  return a;
+}
+
+// INIT: src1 -> Q8_0 wdata in the workspace (and zeroed split-K tickets).
+int q4_init(const Plan& p, const float* src1, int64_t M, int64_t K, void* ws, hipStream_t s) {
+  uint8_t* base = (uint8_t*)ws;
+  const int64_t nticks = p.split > 1 ? p.tiles_m * p.tiles_n : 0;
+  return hip_status(launch_quantize_q8_0(src1, M, K, nullptr, (int8_t*)(base + p.off_aq),
+                                         (float*)(base + p.off_ad), (int32_t*)(base + p.off_ab),
+                                         nticks ? (uint32_t*)(base + p.off_tick) : nullptr,
+                                         nticks, s));
+}
+
+// COMPUTE: src0 x wdata -> dst.
+int q4_compute(const Plan& p, const Q4Args& a, hipStream_t s) {
+  return hip_status(p.kind == KK_Q4_NARROW ? launch_q4_narrow(p, a, s) : launch_q4_wide(p, a, s));
+}
+
+int run_q4_0(const Plan& p, const void* src0, const float* src1, float* dst, int32_t* dots,
+             int64_t M, int64_t N, int64_t K, int64_t n0, int64_t n1, void* ws, hipStream_t s) {
+  const int st = q4_init(p, src1, M, K, ws, s);
+  if (st != MM_OK) return st;
+  return q4_compute(p, q4_args(p, src0, dst, dots, M, N, K, n0, n1, ws), s);
+}
+
+int mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* dots,
+            int64_t M, int64_t N, int64_t K, int64_t n0, int64_t n1, int variant, void* ws,
+            size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(type, M, N, K, variant, &p);
+  if (st != MM_OK) return st;
+  st = validate_mul_mat(type, src0, src1, dst, M, N, K, ws, ws_bytes, p);
+  if (st != MM_OK) return st;
+  if (p.kind == KK_NONE) return MM_OK;
+  st = check_device();
+  if (st != MM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  switch (p.kind) {
+    case KK_ZERO: return hip_status(launch_zero(dst, M * N, s));
+    case KK_Q4_NARROW:
+    case KK_Q4_WIDE: return run_q4_0(p, src0, src1, dst, dots, M, N, K, n0, n1, ws, s);
+    case KK_F_NARROW:
+      return hip_status(launch_f_narrow(p, type, src0, src1, dst, (int)M, (int)N, (int)K, s));
+    case KK_F16_WIDE:
+      return hip_status(launch_f16_wide(p, (const uint16_t*)src0, src1, dst, (int)M, (int)N,
+                                        (int)K, s));
+    default: return MM_ERR_ARG;
+  }
+}
+
+int quantize(int out_type, const float* x, void* y, int64_t nrows, int64_t k, void* stream) {
+  int st = validate_quantize(out_type, x, y, nrows, k);
+  if (st != MM_OK) return st;
+  if (nrows == 0 || k == 0) return MM_OK;
+  st = check_device();
+  if (st != MM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (out_type == MM_TYPE_Q4_0) return hip_status(launch_quantize_q4_0(x, nrows, k, (uint8_t*)y, s));
+  return hip_status(launch_quantize_q8_0(x, nrows, k, (uint8_t*)y, nullptr, nullptr, nullptr,
+                                         nullptr, 0, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mm_quantize_q4_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream) {
+  return quantize(MM_TYPE_Q4_0, x, y, nrows, k, stream);
+}
+
+int mm_quantize_q8_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream) {
+  return quantize(MM_TYPE_Q8_0, x, y, nrows, k, stream);
+}
+
+int mm_mul_mat_q4_0_f32(const void* src0, const float* src1, float* dst, int64_t M, int64_t N,
+                        int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  return mul_mat(MM_TYPE_Q4_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+}
+
+int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst, int64_t M,
+                       int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  return mul_mat(MM_TYPE_F16, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+}
+
+int mm_mul_mat_f32(const float* src0, const float* src1, float* dst, int64_t M, int64_t N,
+                   int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  return mul_mat(MM_TYPE_F32, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+}
+
+int mm_q4_0_init(const float* src1, void* ws, int64_t M, int64_t N, int64_t K, size_t ws_bytes,
+                 void* stream) {
+  Plan p;
+  int st = make_plan(MM_TYPE_Q4_0, M, N, K, 0, &p);
+  if (st != MM_OK) return st;
+  st = validate_mul_mat(MM_TYPE_Q4_0, nullptr, src1, nullptr, M, N, K, ws, ws_bytes, p, STAGE_INIT);
+  if (st != MM_OK) return st;
+  if (p.kind == KK_NONE || p.kind == KK_ZERO) return MM_OK;
+  st = check_device();
+  if (st != MM_OK) return st;
+  return q4_init(p, src1, M, K, ws, (hipStream_t)stream);
+}
+
+int mm_q4_0_compute(const void* src0, float* dst, int64_t M, int64_t N, int64_t K,
+                    const void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(MM_TYPE_Q4_0, M, N, K, 0, &p);
+  if (st != MM_OK) return st;
+  st = validate_mul_mat(MM_TYPE_Q4_0, src0, nullptr, dst, M, N, K, ws, ws_bytes, p, STAGE_COMPUTE);
+  if (st != MM_OK) return st;
+  if (p.kind == KK_NONE) return MM_OK;
+  st = check_device();
+  if (st != MM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.kind == KK_ZERO) return hip_status(launch_zero(dst, M * N, s));
+  return q4_compute(p, q4_args(p, src0, dst, nullptr, M, N, K, 0, 0, (void*)ws), s);
+}
+
+size_t mm_mul_mat_workspace_size(int type, int64_t M, int64_t N, int64_t K) {
+  Plan p;
+  if (make_plan(type, M, N, K, 0, &p) != MM_OK) return 0;
+  return p.ws_bytes;
+}
+
+size_t mm_debug_workspace_size(int type, int64_t M, int64_t N, int64_t K, int variant) {
+  Plan p;
+  if (make_plan(type, M, N, K, variant, &p) != MM_OK) return 0;
+  return p.ws_bytes;
+}
+
+int64_t mm_row_bytes(int type, int64_t K) { return row_bytes(type, K); }
+
+int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
+  Plan p;
+  const int st = make_plan(type, M, N, K, 0, &p);
+  if (st != MM_OK) return st;
+  if (out) {
+    out[0] = p.variant;
+    out[1] = p.split;
+    out[2] = p.variant == 2 ? p.bm : p.mt;
+    out[3] = p.variant == 2 ? p.bn : p.rpw;
+  }
+  return MM_OK;
+}
+
+int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* dots,
+                     int64_t M, int64_t N, int64_t K, int64_t n0, int64_t n1, int variant,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (variant < 0 || variant > 2) return MM_ERR_ARG;
+  if (n0 < 0 || n1 < n0 || n1 > N) return MM_ERR_SHAPE;
+  if (type != MM_TYPE_Q4_0 || n1 == n0) dots = nullptr;
+  else if (!dots) return MM_ERR_NULL;
+  return mul_mat(type, src0, src1, dst, dots, M, N, K, n0, n1, variant, ws, ws_bytes, stream);
+}
+
+const char* mm_status_string(int status) {
+  switch (status) {
+    case MM_OK: return "ok";
+    case MM_ERR_NULL: return "a required pointer is NULL";
+    case MM_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 32 for a block type, or too large)";
+    case MM_ERR_ALIGN: return "pointer not aligned as required";
+    case MM_ERR_WORKSPACE: return "workspace missing or smaller than mm_mul_mat_workspace_size()";
+    case MM_ERR_ALIAS: return "output or workspace overlaps another operand";
+    case MM_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+    case MM_ERR_HIP: return "HIP runtime error";
+    case MM_ERR_ARG: return "unknown type or variant";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

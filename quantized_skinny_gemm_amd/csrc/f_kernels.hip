@@ -1,0 +1,269 @@
+// mul_mat_f32 and mul_mat_f16_f32 for gfx950 (llama.cpp PR 1632 "mulmat
+// tune", Introduction: the two unquantized MUL_MAT kinds).
+//
+// Narrow (VALU) kernel: each weight row is streamed once with 16-byte loads
+// and widened to fp32 in registers; src1 stays fp32; fp32 FMA accumulation;
+// 64-lane butterfly reduction.  Rows of src1 beyond 16 are handled by further
+// passes (grid.y).
+//
+// Wide f16 kernel (M > 16): a dense contraction on v_mfma_f32_32x32x16_f16
+// with src1 rounded to binary16 while staging into LDS and fp32 accumulation.
+// bf16 is avoided: the pages note that at small sizes converting operands to
+// bf16 costs more than it gains (smallbard "Generer a plusieurs"), and its
+// 8-bit mantissa would also sit too close to the 1e-3 accuracy bound.
+#include "device.h"
+#include "kernels.h"
+#include "../../include/mm.h"
+
+namespace qsg {
+
+namespace {
+
+template <typename WT>
+struct WLoad;
+
+template <>
+struct WLoad<uint16_t> {   // binary16 weights: 8 values per 16-byte load
+  static __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = f16_bits_to_f32(w[i]);
+      v[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
+    }
+  }
+  static __device__ __forceinline__ float load1(const uint16_t* p) { return f16_bits_to_f32(*p); }
+};
+
+template <>
+struct WLoad<float> {
+  static __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ float load1(const float* p) { return *p; }
+};
+
+template <typename WT, int MT, int R, bool kVec>
+__global__ __launch_bounds__(256) void k_f_narrow(const WT* __restrict__ w,
+                                                  const float* __restrict__ x,
+                                                  float* __restrict__ dst, int M, int N, int K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.y * MT;
+  const int nw = (blockIdx.x * 4 + wave) * R;
+  const WT* rowp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rowp[r] = w + (int64_t)((nw + r < N) ? nw + r : N - 1) * K;
+  const float* xp[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xp[m] = x + (int64_t)((m0 + m < M) ? m0 + m : M - 1) * K;
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+  int kdone = 0;
+  if (kVec) {
+    const int nchunks = K / 8;
+    for (int c = lane; c < nchunks; c += 64) {
+      float wv[R][8];
+#pragma unroll
+      for (int r = 0; r < R; ++r) WLoad<WT>::load8(rowp[r] + 8 * c, wv[r]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float4 xa = reinterpret_cast<const float4*>(xp[m] + 8 * c)[0];
+        const float4 xb = reinterpret_cast<const float4*>(xp[m] + 8 * c)[1];
+        const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][m] = fmaf(wv[r][e], xv[e], acc[r][m]);
+      }
+    }
+    kdone = nchunks * 8;
+  }
+  for (int k = kdone + lane; k < K; k += 64) {
+    float wv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wv[r] = WLoad<WT>::load1(rowp[r] + k);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float xv = xp[m][k];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][m] = fmaf(wv[r], xv, acc[r][m]);
+    }
+  }
+
+  float mine = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float v = wave_sum(acc[r][m]);
+      if (lane == r * MT + m) mine = v;
+    }
+  const int r = lane / MT, m = lane % MT;
+  if (lane < R * MT && m0 + m < M && nw + r < N) dst[(int64_t)(m0 + m) * N + nw + r] = mine;
+}
+
+template <typename WT, int MT, int R>
+hipError_t launch_f_mt(const Plan& p, const WT* w, const float* x, float* dst, int M, int N,
+                       int K, bool vec, hipStream_t s) {
+  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m);
+  if (vec) hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
+  else hipLaunchKernelGGL((k_f_narrow<WT, MT, R, false>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
+  return hipGetLastError();
+}
+
+template <typename WT>
+hipError_t launch_f_typed(const Plan& p, const WT* w, const float* x, float* dst, int M, int N,
+                          int K, hipStream_t s) {
+  const bool vec = (K % 8 == 0) && ((uintptr_t)w % 16 == 0) && ((uintptr_t)x % 16 == 0);
+  switch (p.mt) {
+    case 1: return launch_f_mt<WT, 1, 4>(p, w, x, dst, M, N, K, vec, s);
+    case 2: return launch_f_mt<WT, 2, 4>(p, w, x, dst, M, N, K, vec, s);
+    case 4: return launch_f_mt<WT, 4, 4>(p, w, x, dst, M, N, K, vec, s);
+    case 8: return launch_f_mt<WT, 8, 2>(p, w, x, dst, M, N, K, vec, s);
+    case 16: return launch_f_mt<WT, 16, 2>(p, w, x, dst, M, N, K, vec, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ------------------------------------------------------------ wide f16
+constexpr int KS = kF16WideKS;       // k per stage
+constexpr int HP = KS + 8;           // halves per LDS row (pad)
+
+template <int BM, int BN, bool kVec>
+__global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w,
+                                                  const float* __restrict__ x,
+                                                  float* __restrict__ dst, int M, int N, int K,
+                                                  int tiles_m, int tiles_n) {
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int WM = WTM / 32, WN = WTN / 32;
+  __shared__ __attribute__((aligned(16))) _Float16 sA[BM * HP];
+  __shared__ __attribute__((aligned(16))) _Float16 sB[BN * HP];
+  const int tiles = tiles_m * tiles_n;
+  const int t = xcd_remap(blockIdx.x, tiles);
+  const int tm = t % tiles_m, tn = t / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / 2, wn = wave % 2;
+  const int h = lane >> 5, l32 = lane & 31;
+
+  v16f acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = v16f{};
+
+  for (int k0 = 0; k0 < K; k0 += KS) {
+    __syncthreads();
+    // src1 tile: BM x KS floats -> binary16 (round to nearest even)
+    for (int i = tid; i < BM * (KS / 4); i += 256) {
+      const int r = i / (KS / 4), c = i % (KS / 4);
+      const int m = m0 + r, k = k0 + 4 * c;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (m < M) {
+        if (kVec && k + 4 <= K) {
+          const float4 f = *reinterpret_cast<const float4*>(x + (int64_t)m * K + k);
+          v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? x[(int64_t)m * K + k + e] : 0.0f;
+        }
+      }
+      v4h hv;
+      hv.x = (_Float16)v[0]; hv.y = (_Float16)v[1]; hv.z = (_Float16)v[2]; hv.w = (_Float16)v[3];
+      *reinterpret_cast<v4h*>(sA + r * HP + 4 * c) = hv;
+    }
+    // src0 tile: BN x KS halves
+    for (int i = tid; i < BN * (KS / 8); i += 256) {
+      const int r = i / (KS / 8), c = i % (KS / 8);
+      const int n = n0 + r, k = k0 + 8 * c;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (n < N) {
+        if (kVec && k + 8 <= K) {
+          u = *reinterpret_cast<const uint4*>(w + (int64_t)n * K + k);
+        } else {
+          uint32_t hw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hw[e] = (k + e < K) ? w[(int64_t)n * K + k + e] : 0u;
+          u = make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16),
+                         hw[6] | (hw[7] << 16));
+        }
+      }
+      *reinterpret_cast<uint4*>(sB + r * HP + 8 * c) = u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KS / 16; ++s) {
+      v8h A[WM], B[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        A[i] = *reinterpret_cast<const v8h*>(sA + (wm * WTM + 32 * i + l32) * HP + 16 * s + 8 * h);
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        B[j] = *reinterpret_cast<const v8h*>(sB + (wn * WTN + 32 * j + l32) * HP + 16 * s + 8 * h);
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int n = n0 + wn * WTN + 32 * j + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * WTM + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+        if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][j][r];
+      }
+    }
+}
+
+__global__ void k_zero(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* x, float* dst,
+                           int M, int N, int K, hipStream_t s) {
+  if (type == MM_TYPE_F16)
+    return launch_f_typed<uint16_t>(p, (const uint16_t*)w, x, dst, M, N, K, s);
+  return launch_f_typed<float>(p, (const float*)w, x, dst, M, N, K, s);
+}
+
+hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, float* dst, int M,
+                           int N, int K, hipStream_t s) {
+  const bool vec = (K % 8 == 0) && ((uintptr_t)w % 16 == 0) && ((uintptr_t)x % 16 == 0);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+  const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
+  if (p.bm == 128) {
+    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<128, 128, false>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<64, 64, false>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* dst, int64_t n, hipStream_t s) {
+  int64_t grid = (n + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) return hipSuccess;
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)grid), dim3(256), 0, s, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace qsg

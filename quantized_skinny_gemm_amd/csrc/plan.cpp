@@ -1,0 +1,191 @@
+// Host-only dispatch plan, workspace layout and argument validation.
+#include "plan.h"
+
+#include <stdint.h>
+
+#include "../../include/mm.h"
+
+namespace qsg {
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int narrow_mt(int64_t M, int cap) {
+  int mt = 1;
+  while (mt < M && mt < cap) mt <<= 1;
+  return mt;
+}
+
+}  // namespace
+
+int64_t row_bytes(int type, int64_t K) {
+  if (K < 0) return -1;
+  switch (type) {
+    case MM_TYPE_F32: return 4 * K;
+    case MM_TYPE_F16: return 2 * K;
+    case MM_TYPE_Q4_0: return (K % kQK) ? -1 : K / kQK * kQ4Bytes;
+    case MM_TYPE_Q8_0: return (K % kQK) ? -1 : K / kQK * kQ8Bytes;
+    default: return -1;
+  }
+}
+
+int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p) {
+  *p = Plan();
+  p->type = type;
+  if (type != MM_TYPE_F32 && type != MM_TYPE_F16 && type != MM_TYPE_Q4_0) return MM_ERR_ARG;
+  if (variant < 0 || variant > 2) return MM_ERR_ARG;
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MM_ERR_SHAPE;
+  if (type == MM_TYPE_Q4_0 && (K % kQK)) return MM_ERR_SHAPE;
+  if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
+  if (K == 0) { p->kind = KK_ZERO; return MM_OK; }
+
+  if (type == MM_TYPE_Q4_0) {
+    const int64_t nb = K / kQK;
+    const bool narrow = variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM);
+    size_t off = 0;
+    p->off_aq = off; off = align_up(off + (size_t)M * (size_t)K, 256);
+    p->off_ad = off; off = align_up(off + (size_t)M * (size_t)nb * 4, 256);
+    p->off_ab = off; off = align_up(off + (size_t)M * (size_t)nb * 4, 256);
+    if (narrow) {
+      p->kind = KK_Q4_NARROW;
+      p->variant = 1;
+      p->mt = narrow_mt(M, kNarrowQ4MaxM);
+      p->rpw = p->mt <= 2 ? 2 : 4;
+      p->tiles_m = ceil_div(M, p->mt);
+      p->tiles_n = ceil_div(N, 4 * p->rpw);
+      // K units of the narrow kernel are block pairs (blocks when K/32 is odd).
+      const int64_t units = (nb % 2 == 0) ? nb / 2 : nb;
+      const int64_t wgs = p->tiles_m * p->tiles_n;
+      int64_t split = 1;
+      if (wgs < 2 * kCUs) {
+        const int64_t max_split = units / 64;        // keep every lane busy
+        split = ceil_div(2 * kCUs, wgs);
+        if (split > max_split) split = max_split;
+        if (split > 16) split = 16;
+        if (split < 1) split = 1;
+      }
+      p->kchunk = ceil_div(units, split);
+      p->split = (int)ceil_div(units, p->kchunk);
+    } else {
+      p->kind = KK_Q4_WIDE;
+      p->variant = 2;
+      // Output tile by M; shrink while the grid cannot fill the device.
+      if (M <= 32) { p->bm = 32; p->bn = 64; p->waves_m = 1; p->waves_n = 2; }
+      else if (M <= 64) { p->bm = 64; p->bn = 64; p->waves_m = 2; p->waves_n = 2; }
+      else { p->bm = 128; p->bn = 128; p->waves_m = 2; p->waves_n = 2; }
+      for (;;) {
+        p->tiles_m = ceil_div(M, p->bm);
+        p->tiles_n = ceil_div(N, p->bn);
+        if (p->tiles_m * p->tiles_n >= kCUs) break;
+        if (p->bn == 128) { p->bn = 64; continue; }
+        if (p->bm == 128) { p->bm = 64; continue; }
+        break;
+      }
+      const int64_t tiles = p->tiles_m * p->tiles_n;
+      const int64_t stages = ceil_div(nb, kWideKB);
+      int64_t split = 1;
+      if (tiles < kCUs) {
+        split = ceil_div(kCUs, tiles);
+        const int64_t max_split = stages / 2;          // >= 2 stages per split
+        if (split > max_split) split = max_split;
+        if (split > 16) split = 16;
+        if (split < 1) split = 1;
+      }
+      p->kchunk = ceil_div(stages, split) * kWideKB;   // blocks per split
+      p->split = (int)ceil_div(nb, p->kchunk);
+    }
+    if (p->split > 1) {
+      p->off_part = off; off = align_up(off + (size_t)p->split * (size_t)M * (size_t)N * 4, 256);
+      p->off_tick = off; off = align_up(off + (size_t)(p->tiles_m * p->tiles_n) * 4, 256);
+    }
+    p->ws_bytes = off;
+    return MM_OK;
+  }
+
+  // F16 / F32
+  const bool wide = type == MM_TYPE_F16 && (variant == 2 || (variant == 0 && M > kNarrowFMaxM));
+  if (!wide) {
+    p->kind = KK_F_NARROW;
+    p->variant = 1;
+    p->mt = narrow_mt(M, kNarrowFMaxM);
+    p->rpw = p->mt >= 8 ? 2 : 4;
+    p->tiles_m = ceil_div(M, p->mt);
+    p->tiles_n = ceil_div(N, 4 * p->rpw);
+  } else {
+    p->kind = KK_F16_WIDE;
+    p->variant = 2;
+    p->bm = 128; p->bn = 128; p->waves_m = 2; p->waves_n = 2;
+    p->tiles_m = ceil_div(M, p->bm);
+    p->tiles_n = ceil_div(N, p->bn);
+    if (p->tiles_m * p->tiles_n < kCUs) {
+      p->bm = 64; p->bn = 64;
+      p->tiles_m = ceil_div(M, p->bm);
+      p->tiles_n = ceil_div(N, p->bn);
+    }
+    p->kchunk = K;
+  }
+  p->ws_bytes = 0;
+  return MM_OK;
+}
+
+int validate_mul_mat(int type, const void* src0, const void* src1, const void* dst,
+                     int64_t M, int64_t N, int64_t K, const void* ws, size_t ws_bytes,
+                     const Plan& p, int stage) {
+  if (p.kind == KK_NONE) return MM_OK;
+  const bool need_src0 = stage != STAGE_INIT && K > 0;
+  const bool need_src1 = stage != STAGE_COMPUTE && K > 0;
+  const bool need_dst = stage != STAGE_INIT;
+  if (need_dst && !dst) return MM_ERR_NULL;
+  if ((need_src0 && !src0) || (need_src1 && !src1)) return MM_ERR_NULL;
+  if (!need_src0) src0 = nullptr;
+  if (!need_src1) src1 = nullptr;
+  if (!need_dst) dst = nullptr;
+  const uintptr_t s0 = (uintptr_t)src0, s1 = (uintptr_t)src1, d = (uintptr_t)dst;
+  if (d % 4) return MM_ERR_ALIGN;
+  if (type == MM_TYPE_Q4_0) {
+    if (s0 % 2 || s1 % 16) return MM_ERR_ALIGN;
+  } else if (type == MM_TYPE_F16) {
+    if (s0 % 2 || s1 % 4) return MM_ERR_ALIGN;
+  } else {
+    if (s0 % 4 || s1 % 4) return MM_ERR_ALIGN;
+  }
+  if (p.ws_bytes > 0) {
+    if (!ws || ws_bytes < p.ws_bytes) return MM_ERR_WORKSPACE;
+    if ((uintptr_t)ws % 256) return MM_ERR_ALIGN;
+  }
+  const size_t dst_bytes = dst ? (size_t)M * (size_t)N * 4 : 0;
+  const size_t s0_bytes = src0 ? (size_t)N * (size_t)row_bytes(type, K) : 0;
+  const size_t s1_bytes = src1 ? (size_t)M * (size_t)K * 4 : 0;
+  if (overlaps(dst, dst_bytes, src0, s0_bytes) || overlaps(dst, dst_bytes, src1, s1_bytes))
+    return MM_ERR_ALIAS;
+  if (p.ws_bytes > 0 &&
+      (overlaps(ws, p.ws_bytes, dst, dst_bytes) || overlaps(ws, p.ws_bytes, src0, s0_bytes) ||
+       overlaps(ws, p.ws_bytes, src1, s1_bytes)))
+    return MM_ERR_ALIAS;
+  return MM_OK;
+}
+
+int validate_quantize(int out_type, const void* x, const void* y, int64_t nrows, int64_t k) {
+  if (nrows < 0 || k < 0 || nrows > kMaxDim || k > kMaxDim) return MM_ERR_SHAPE;
+  if (k % kQK) return MM_ERR_SHAPE;
+  if (nrows == 0 || k == 0) return MM_OK;
+  if (!x || !y) return MM_ERR_NULL;
+  if ((uintptr_t)x % 16 || (uintptr_t)y % 2) return MM_ERR_ALIGN;
+  const size_t xb = (size_t)nrows * (size_t)k * 4;
+  const size_t yb = (size_t)nrows * (size_t)row_bytes(out_type, k);
+  if (overlaps(x, xb, y, yb)) return MM_ERR_ALIAS;
+  return MM_OK;
+}
+
+}  // namespace qsg

@@ -1,0 +1,74 @@
+// Host-only dispatch plan and argument validation (no HIP calls).
+//
+// The plan is a pure function of (type, M, N, K, variant): the workspace
+// size a caller is told to allocate and the kernels the entry point launches
+// always agree.  Tile and split choices follow two observations from the
+// pages: a narrow-M kernel that streams each weight once beats tiled kernels
+// for small M but loses quickly past its threshold (smallbard "Generer a
+// plusieurs", "La courbe, une premiere fois"), and a product whose output
+// tiles are too few to fill the device is split along the common dimension
+// with the partial sums added afterwards (same section; DeepSpeed-Inference
+// notes, SBI-GeMM tiling strategy).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsg {
+
+constexpr int kQK = 32;            // values per Q4_0 / Q8_0 block
+constexpr int kQ4Bytes = 18;       // bytes per Q4_0 block
+constexpr int kQ8Bytes = 34;       // bytes per Q8_0 block
+constexpr int kCUs = 256;          // MI355X compute units
+constexpr int kWideKB = 4;         // Q4_0 blocks per LDS stage in the wide kernel
+constexpr int kF16WideKS = 32;     // k elements per LDS stage in the f16 wide kernel
+constexpr int kNarrowQ4MaxM = 8;   // largest M the Q4_0 narrow kernel takes in one pass
+constexpr int kNarrowFMaxM = 16;   // largest M the f16/f32 narrow kernel takes in one pass
+
+enum KernelKind {
+  KK_NONE = 0,      // nothing to do (M == 0 or N == 0)
+  KK_ZERO = 1,      // K == 0: dst = 0
+  KK_Q4_NARROW = 2,
+  KK_Q4_WIDE = 3,
+  KK_F_NARROW = 4,  // f16 or f32 src0
+  KK_F16_WIDE = 5,
+};
+
+struct Plan {
+  int type = 0;
+  int kind = KK_NONE;
+  int variant = 0;          // 1 narrow, 2 wide
+  // narrow kernels
+  int mt = 1;               // src1 rows per pass (compile-time tile)
+  int rpw = 1;              // src0 rows per wave
+  // wide kernels
+  int bm = 0, bn = 0, waves_m = 0, waves_n = 0;
+  // grid
+  int64_t tiles_m = 1;      // wide: output tile rows; narrow: passes over M
+  int64_t tiles_n = 1;      // output tile columns (narrow: groups of 4*rpw src0 rows)
+  int split = 1;            // split-K factor
+  int64_t kchunk = 0;       // K units per split (Q4_0: blocks; f16: elements)
+  // workspace layout (bytes)
+  size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0, off_tick = 0;
+  size_t ws_bytes = 0;
+};
+
+// Builds the plan; returns 0 (MM_OK) or a negative mm_status.
+int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p);
+
+// Which operands a call takes: the whole product, or one of the two stages
+// of the quantized product (INIT: src1 -> wdata; COMPUTE: src0 x wdata -> dst).
+enum Stage { STAGE_ALL = 0, STAGE_INIT = 1, STAGE_COMPUTE = 2 };
+
+// Argument checks of mm_mul_mat_* / mm_q4_0_init / mm_q4_0_compute /
+// mm_debug_mul_mat; no HIP calls.
+int validate_mul_mat(int type, const void* src0, const void* src1, const void* dst,
+                     int64_t M, int64_t N, int64_t K, const void* ws, size_t ws_bytes,
+                     const Plan& p, int stage = STAGE_ALL);
+
+// Argument checks of mm_quantize_q4_0 / mm_quantize_q8_0; no HIP calls.
+int validate_quantize(int out_type, const void* x, const void* y, int64_t nrows, int64_t k);
+
+int64_t row_bytes(int type, int64_t K);
+
+}  // namespace qsg

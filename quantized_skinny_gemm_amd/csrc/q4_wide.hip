@@ -1,0 +1,254 @@
+// Wide-M Q4_0 x Q8_0 product for gfx950 on int8 MFMA.
+//
+// Past the narrow kernel's threshold the product is a dense contraction (the
+// first-token / prefill regime, arXiv 2407.07304 section 2.2), so it runs on
+// v_mfma_i32_32x32x32_i8: K = 32 is exactly one Q4_0/Q8_0 block, hence one
+// (d_w, d_a) pair per MFMA output and the int32 block dot S_b comes out of
+// the matrix core unchanged.  The weights are dequantized to int8 codes in
+// LDS, not to floats (llama.cpp PR 1632, "Parallel de-quantizing": turning
+// the weights into floats ahead of the product can cost as much as the
+// product itself at these M).
+//
+// Per workgroup: an output tile BM x BN; per stage, KB = 4 blocks (128 k):
+//   * weight rows are loaded as 36-byte block pairs (4-byte aligned when K/32
+//     is even), the nibbles unpacked to signed int8 (q - 8) and the scales to
+//     fp32, both into LDS;
+//   * the Q8_0 activation codes (wdata) and scales are copied into LDS;
+//   * each wave runs WM x WN MFMAs per block and applies the fp32 scale
+//     epilogue acc += f32(S_b) * (d_a * d_w);
+// and, when the tiles cannot fill the device, K is split across workgroups
+// whose partial tiles the last arriving workgroup adds in fixed order
+// (smallbard "Generer a plusieurs", "La courbe, une premiere fois";
+// DeepSpeed-Inference notes, III.C SBI-GeMM tiling).
+#include "device.h"
+#include "kernels.h"
+
+namespace qsg {
+
+namespace {
+
+constexpr int KB = kWideKB;          // blocks per stage
+constexpr int PITCH = KB * 32 + 8;   // bytes per LDS row of codes (pad against bank conflicts)
+
+__device__ __forceinline__ uint32_t nib_lo_signed(uint32_t q) {
+  // per byte: (q & 15) - 8 as int8: add 0x78 (no carry out of a byte), flip bit 7
+  return ((q & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+}
+__device__ __forceinline__ uint32_t nib_hi_signed(uint32_t q) {
+  return (((q >> 4) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+}
+
+// Writes one decoded block (scale + 32 signed codes) into LDS.
+__device__ __forceinline__ void put_block(int8_t* sB, float* sBd, int bn, int r, int bb, float d,
+                                          const uint32_t (&q)[4]) {
+  uint2* p = reinterpret_cast<uint2*>(sB + r * PITCH + bb * 32);
+  p[0] = make_uint2(nib_lo_signed(q[0]), nib_lo_signed(q[1]));   // elements 0..7
+  p[1] = make_uint2(nib_lo_signed(q[2]), nib_lo_signed(q[3]));   // elements 8..15
+  p[2] = make_uint2(nib_hi_signed(q[0]), nib_hi_signed(q[1]));   // elements 16..23
+  p[3] = make_uint2(nib_hi_signed(q[2]), nib_hi_signed(q[3]));   // elements 24..31
+  sBd[bb * bn + r] = d;
+}
+
+__device__ __forceinline__ v4i lds_operand(const int8_t* row, int bb, int h) {
+  // lane half h supplies elements 8h..8h+7 and 16+8h..16+8h+7 of the block;
+  // the A and B operands use the same assignment, so the MFMA's k-sum runs
+  // over all 32 elements of the block.
+  const uint2 x = *reinterpret_cast<const uint2*>(row + bb * 32 + 8 * h);
+  const uint2 y = *reinterpret_cast<const uint2*>(row + bb * 32 + 16 + 8 * h);
+  v4i v;
+  v.x = (int)x.x; v.y = (int)x.y; v.z = (int)y.x; v.w = (int)y.y;
+  return v;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool kPairs, bool kDump>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, int tiles_m,
+                                                                   int tiles_n, int kchunk,
+                                                                   int split) {
+  constexpr int NT = 64 * WAVES_M * WAVES_N;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int WM = WTM / 32, WN = WTN / 32;
+  static_assert(WM >= 1 && WN >= 1, "wave tile must be a multiple of 32x32");
+  __shared__ __attribute__((aligned(16))) int8_t sA[BM * PITCH];
+  __shared__ __attribute__((aligned(16))) int8_t sB[BN * PITCH];
+  __shared__ __attribute__((aligned(16))) float sAd[KB * BM];
+  __shared__ __attribute__((aligned(16))) float sBd[KB * BN];
+
+  const int M = a.M, N = a.N, K = a.K;
+  const int nb = K / 32;
+  const int64_t rb = (int64_t)nb * 18;
+  const int tiles = tiles_m * tiles_n;
+  const int t = xcd_remap(blockIdx.x, tiles * split);
+  const int z = t / tiles;
+  const int tt = t % tiles;
+  const int tm = tt % tiles_m, tn = tt / tiles_m;     // m fastest: same weight tile adjacent
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb0 = z * kchunk;
+  const int kb1 = (kb0 + kchunk < nb) ? kb0 + kchunk : nb;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int h = lane >> 5, l32 = lane & 31;
+
+  float acc[WM][WN][16];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  for (int kb = kb0; kb < kb1; kb += KB) {
+    __syncthreads();
+    // ---- stage weights: BN rows x KB blocks, decoded
+    if (kPairs) {
+      for (int i = tid; i < BN * (KB / 2); i += NT) {
+        const int r = i / (KB / 2), pp = i % (KB / 2);
+        const int n = n0 + r, b = kb + 2 * pp;
+        uint32_t wv[9];
+        if (n < N && b < kb1) {
+          const uint32_t* p = reinterpret_cast<const uint32_t*>(a.w + (int64_t)n * rb + (int64_t)b * 18);
+#pragma unroll
+          for (int j = 0; j < 9; ++j) wv[j] = p[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 9; ++j) wv[j] = 0x88888888u;
+          wv[0] = 0x88880000u; wv[4] = 0x00008888u;    // zero scales
+        }
+        uint32_t q0[4], q1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          q0[j] = __builtin_amdgcn_alignbit(wv[j + 1], wv[j], 16);
+          q1[j] = wv[5 + j];
+        }
+        const float d0 = f16_bits_to_f32(wv[0]);
+        float d1 = f16_bits_to_f32(wv[4] >> 16);
+        if (b + 1 >= kb1) {                              // odd tail: block b+1 is not ours
+          d1 = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) q1[j] = 0x88888888u;
+        }
+        put_block(sB, sBd, BN, r, 2 * pp, d0, q0);
+        put_block(sB, sBd, BN, r, 2 * pp + 1, d1, q1);
+      }
+    } else {
+      for (int i = tid; i < BN * KB; i += NT) {
+        const int r = i / KB, bb = i % KB;
+        const int n = n0 + r, b = kb + bb;
+        uint32_t q[4] = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+        float d = 0.0f;
+        if (n < N && b < kb1) {
+          const uint16_t* p = reinterpret_cast<const uint16_t*>(a.w + (int64_t)n * rb + (int64_t)b * 18);
+          uint32_t hw[9];
+#pragma unroll
+          for (int j = 0; j < 9; ++j) hw[j] = p[j];
+          d = f16_bits_to_f32(hw[0]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) q[j] = hw[1 + 2 * j] | (hw[2 + 2 * j] << 16);
+        }
+        put_block(sB, sBd, BN, r, bb, d, q);
+      }
+    }
+    // ---- stage activations: BM rows x KB*32 codes + scales
+    for (int i = tid; i < BM * KB * 2; i += NT) {
+      const int r = i / (KB * 2), c = i % (KB * 2);
+      const int m = m0 + r, b = kb + c / 2;
+      v4i v = {0, 0, 0, 0};
+      if (m < M && b < kb1)
+        v = *reinterpret_cast<const v4i*>(a.aq + (int64_t)m * K + (int64_t)kb * 32 + c * 16);
+      uint2* p = reinterpret_cast<uint2*>(sA + r * PITCH + c * 16);
+      p[0] = make_uint2((uint32_t)v.x, (uint32_t)v.y);
+      p[1] = make_uint2((uint32_t)v.z, (uint32_t)v.w);
+    }
+    for (int i = tid; i < BM * KB; i += NT) {
+      const int r = i % BM, bb = i / BM;
+      const int m = m0 + r, b = kb + bb;
+      sAd[bb * BM + r] = (m < M && b < kb1) ? a.ad[(int64_t)m * nb + b] : 0.0f;
+    }
+    __syncthreads();
+
+    // ---- MFMA over the stage's blocks
+    const int nblk = (kb1 - kb < KB) ? kb1 - kb : KB;
+    for (int bb = 0; bb < nblk; ++bb) {
+      v4i A[WM], B[WN];
+      float dw[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i) A[i] = lds_operand(sA + (wm * WTM + 32 * i + l32) * PITCH, bb, h);
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        B[j] = lds_operand(sB + (wn * WTN + 32 * j + l32) * PITCH, bb, h);
+        dw[j] = sBd[bb * BN + wn * WTN + 32 * j + l32];
+      }
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        // output row of accumulator r: 8*(r/4) + 4*h + (r%4) within the 32x32 tile
+        float da[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 v = *reinterpret_cast<const float4*>(sAd + bb * BM + wm * WTM + 32 * i + 8 * g + 4 * h);
+          da[4 * g + 0] = v.x; da[4 * g + 1] = v.y; da[4 * g + 2] = v.z; da[4 * g + 3] = v.w;
+        }
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const v16i zero = {};
+          const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[i], B[j], zero, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf((float)c[r], da[r] * dw[j], acc[i][j][r]);
+          if (kDump) {
+            const int n = n0 + wn * WTN + 32 * j + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = m0 + wm * WTM + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+              if (m < M && n >= a.n0 && n < a.n1)
+                a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + kb + bb] = c[r];
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- store (or split-K partials)
+  float* out = split == 1 ? a.dst : a.part + (int64_t)z * M * N;
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int n = n0 + wn * WTN + 32 * j + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * WTM + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+        if (m < M && n < N) out[(int64_t)m * N + n] = acc[i][j][r];
+      }
+    }
+  if (split > 1 && splitk_arrive(a.tick + tt, split))
+    splitk_reduce_tile(a.part, a.dst, M, N, m0, BM, n0, BN, split);
+}
+
+template <int BM, int BN, int WMS, int WNS>
+hipError_t launch_cfg(const Plan& p, const Q4Args& a, bool pairs, hipStream_t s) {
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * p.split));
+  const dim3 block(64 * WMS * WNS);
+  const int tm = (int)p.tiles_m, tn = (int)p.tiles_n, kc = (int)p.kchunk, sp = p.split;
+  const bool dump = a.dots != nullptr;
+  if (pairs) {
+    if (dump) hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, true, true>), grid, block, 0, s, a, tm, tn, kc, sp);
+    else hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, true, false>), grid, block, 0, s, a, tm, tn, kc, sp);
+  } else {
+    if (dump) hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, false, true>), grid, block, 0, s, a, tm, tn, kc, sp);
+    else hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, false, false>), grid, block, 0, s, a, tm, tn, kc, sp);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_q4_wide(const Plan& p, const Q4Args& a, hipStream_t s) {
+  const bool pairs = ((a.K / 32) % 2 == 0) && ((uintptr_t)a.w % 4 == 0);
+  if (p.bm == 32 && p.bn == 64) return launch_cfg<32, 64, 1, 2>(p, a, pairs, s);
+  if (p.bm == 64 && p.bn == 64) return launch_cfg<64, 64, 2, 2>(p, a, pairs, s);
+  if (p.bm == 128 && p.bn == 64) return launch_cfg<128, 64, 2, 2>(p, a, pairs, s);
+  if (p.bm == 128 && p.bn == 128) return launch_cfg<128, 128, 2, 2>(p, a, pairs, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qsg

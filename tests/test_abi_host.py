@@ -1,0 +1,157 @@
+"""Host-side tests of the C ABI (no GPU, no compute calls).
+
+The library must load, export every function include/mm.h declares, and
+reject bad arguments on the host before touching HIP.  Pointers passed here
+are never dereferenced: validation fails first.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_skinny_gemm_amd as qs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mm.h")
+
+OK, NULL, SHAPE, ALIGN, WS, ALIAS, DEVICE, HIP, ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+F32, F16, Q4, Q8 = qs.MM_TYPE_F32, qs.MM_TYPE_F16, qs.MM_TYPE_Q4_0, qs.MM_TYPE_Q8_0
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared()
+    for n in ("mm_quantize_q4_0", "mm_quantize_q8_0", "mm_mul_mat_q4_0_f32",
+              "mm_mul_mat_f16_f32", "mm_mul_mat_f32"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(qs.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in (OK, NULL, SHAPE, ALIGN, WS, ALIAS, DEVICE, HIP, ARG):
+        assert qs.status_string(s)
+    assert qs.status_string(12345) == "unknown status"
+
+
+def test_row_bytes():
+    assert qs.row_bytes(Q4, 4096) == 4096 // 32 * 18
+    assert qs.row_bytes(Q8, 4096) == 4096 // 32 * 34
+    assert qs.row_bytes(F16, 37) == 74
+    assert qs.row_bytes(F32, 37) == 148
+    assert qs.row_bytes(Q4, 48) == -1
+    assert qs.row_bytes(99, 32) == -1
+
+
+FAKE = 0x7f0000000000      # 256-byte aligned, never dereferenced
+
+
+def _mm_q4(src0, src1, dst, m, n, k, ws, wsb):
+    return qs.lib.mm_mul_mat_q4_0_f32(src0, src1, dst, m, n, k, ws, wsb, None)
+
+
+def test_q4_shape_errors():
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 2**31, 1, 16, 48, None, 0) == SHAPE
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 2**31, -1, 16, 64, None, 0) == SHAPE
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 2**31, 1, -3, 64, None, 0) == SHAPE
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 2**31, 1, 16, -32, None, 0) == SHAPE
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 2**31, 1, 2**31, 64, None, 0) == SHAPE
+
+
+def test_empty_problems_are_noops():
+    # M == 0 or N == 0: nothing to do, no pointer is looked at
+    assert _mm_q4(None, None, None, 0, 16, 64, None, 0) == OK
+    assert _mm_q4(None, None, None, 4, 0, 64, None, 0) == OK
+    assert qs.lib.mm_mul_mat_f32(None, None, None, 0, 0, 0, None, 0, None) == OK
+    assert qs.lib.mm_quantize_q4_0(None, None, 0, 64, None) == OK
+    assert qs.lib.mm_quantize_q8_0(None, None, 5, 0, None) == OK
+
+
+def test_null_pointers():
+    ws = qs.workspace_size(Q4, 1, 64, 64)
+    assert _mm_q4(FAKE, FAKE + 2**30, None, 1, 64, 64, FAKE + 2**32, ws) == NULL
+    assert _mm_q4(None, FAKE + 2**30, FAKE + 2**31, 1, 64, 64, FAKE + 2**32, ws) == NULL
+    assert _mm_q4(FAKE, None, FAKE + 2**31, 1, 64, 64, FAKE + 2**32, ws) == NULL
+    assert qs.lib.mm_quantize_q8_0(None, FAKE, 1, 64, None) == NULL
+
+
+def test_alignment():
+    ws = qs.workspace_size(Q4, 1, 64, 64)
+    args = dict(src0=FAKE, src1=FAKE + 2**30, dst=FAKE + 2**31, ws=FAKE + 2**32)
+    assert _mm_q4(FAKE + 1, args["src1"], args["dst"], 1, 64, 64, args["ws"], ws) == ALIGN
+    assert _mm_q4(FAKE, args["src1"] + 4, args["dst"], 1, 64, 64, args["ws"], ws) == ALIGN
+    assert _mm_q4(FAKE, args["src1"], args["dst"] + 2, 1, 64, 64, args["ws"], ws) == ALIGN
+    assert _mm_q4(FAKE, args["src1"], args["dst"], 1, 64, 64, args["ws"] + 64, ws) == ALIGN
+    assert qs.lib.mm_quantize_q4_0(FAKE + 4, FAKE + 2**30, 1, 64, None) == ALIGN
+    assert qs.lib.mm_quantize_q8_0(FAKE, FAKE + 2**30 + 1, 1, 64, None) == ALIGN
+    assert qs.lib.mm_mul_mat_f16_f32(FAKE + 1, FAKE + 2**30, FAKE + 2**31, 1, 8, 8, None, 0, None) == ALIGN
+    assert qs.lib.mm_mul_mat_f32(FAKE + 2, FAKE + 2**30, FAKE + 2**31, 1, 8, 8, None, 0, None) == ALIGN
+
+
+def test_workspace_too_small():
+    need = qs.workspace_size(Q4, 4, 256, 512)
+    assert need > 0
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 2**31, 4, 256, 512, FAKE + 2**32, need - 1) == WS
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 2**31, 4, 256, 512, None, need) == WS
+
+
+def test_aliasing():
+    need = qs.workspace_size(Q4, 4, 256, 512)
+    # dst overlapping src1
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 2**30 + 256, 4, 256, 512, FAKE + 2**32, need) == ALIAS
+    # dst overlapping src0
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 1024, 4, 256, 512, FAKE + 2**32, need) == ALIAS
+    # workspace overlapping dst
+    assert _mm_q4(FAKE, FAKE + 2**30, FAKE + 2**31, 4, 256, 512, FAKE + 2**31, need) == ALIAS
+    # quantize output overlapping its input
+    assert qs.lib.mm_quantize_q8_0(FAKE, FAKE + 64, 4, 64, None) == ALIAS
+
+
+def test_debug_entry_argument_checks():
+    assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 7, None, 0, None) == ARG
+    assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 5, 3, 0, None, 0, None) == SHAPE
+    assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 65, 0, None, 0, None) == SHAPE
+    assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 8, 0, None, 0, None) == NULL
+    assert qs.lib.mm_debug_mul_mat(9, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 0, None, 0, None) == ARG
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 64, 100, 128, 512])
+def test_dispatch_threshold_and_workspace(m):
+    variant, split, rows, cols = qs.dispatch(Q4, m, 4096, 4096)
+    assert variant == (1 if m <= 8 else 2)
+    assert split >= 1
+    ws = qs.workspace_size(Q4, m, 4096, 4096)
+    # at least the wdata: codes + scale + bias per block
+    assert ws >= m * 4096 + 2 * 4 * m * 128
+    if variant == 1:
+        assert rows >= m or rows == 8
+    f16 = qs.dispatch(F16, m, 4096, 4096)
+    assert f16[0] == (1 if m <= 16 else 2)
+    assert qs.workspace_size(F16, m, 4096, 4096) == 0
+    assert qs.dispatch(F32, m, 4096, 4096)[0] == 1
+
+
+def test_split_k_when_grid_is_small():
+    # the tiny workload (N = 256) and a narrow N at the wide kernel must split K
+    v, split, _, _ = qs.dispatch(Q4, 32, 64, 14336)
+    assert v == 2 and split > 1
+    assert qs.workspace_size(Q4, 32, 64, 14336) >= split * 32 * 64 * 4
+    # large grids do not split
+    assert qs.dispatch(Q4, 512, 14336, 4096)[1] == 1
+    assert qs.dispatch(Q4, 1, 11008, 4096)[1] == 1
+
+
+def test_workspace_size_of_invalid_shapes_is_zero():
+    assert qs.workspace_size(Q4, 1, 16, 48) == 0
+    assert qs.workspace_size(7, 1, 16, 64) == 0

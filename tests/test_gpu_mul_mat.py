@@ -1,0 +1,308 @@
+"""GPU parity of the MUL_MAT kernels against the float64 oracle.
+
+Q4_0: the int32 block dots S_b written by the production kernels must equal
+the oracle's exactly; dst must match within 1e-5 normwise (over the matrix
+and over each row).  F16 / F32: dst within 1e-3 normwise.  Full outputs are
+compared where the oracle finishes in seconds; at the 128256-column prefill
+shape, sampled columns (all rows) are compared.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import codec, mul_mat
+from tests.gpu_util import TOL_F, TOL_Q4_0, assert_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _qs():
+    import quantized_skinny_gemm_amd as qs
+    return qs
+
+
+def _q4_weights(wl, j, n, k):
+    """Seeded weights quantized on the GPU; the bytes are checked against the oracle."""
+    w = workloads.weights_f32(workloads.weight_seed(wl, j), n, k)
+    wq_dev = _qs().quantize_q4_0(to_dev(w))
+    wq = codec.quantize_q4_0(w)
+    assert np.array_equal(to_host(wq_dev), wq)
+    return wq_dev, wq
+
+
+def _check_q4_product(wq_dev, wq, x, what, variant=0, dots_cols=None):
+    qs = _qs()
+    m, k = x.shape
+    n = wq.shape[0]
+    nb = k // 32
+    n0, n1 = dots_cols if dots_cols is not None else (0, n)
+    say("mul_mat_q4_0", what, f"M={m} N={n} K={k} variant={variant} dots=[{n0},{n1})")
+    y, dots = qs.debug_mul_mat(qs.MM_TYPE_Q4_0, wq_dev, to_dev(x), variant, n0, n1)
+    y = to_host(y)
+    ref = mul_mat.mul_mat_q4_0_f32_dequant(wq, x)
+    assert_close(y, ref, TOL_Q4_0, what)
+    if dots is not None:
+        want = codec.block_dots(wq[n0:n1], codec.quantize_q8_0(x), k)
+        got = to_host(dots)
+        assert got.shape == (m, n1 - n0, nb)
+        assert np.array_equal(got, want), f"{what}: block dots differ"
+    return y
+
+
+def test_tiny_workload_all_paths():
+    wq_dev, wq = _q4_weights(0, 0, 256, 512)
+    x = workloads.activations(workloads.activation_seed(0, 1), 1, 512)
+    y0 = _check_q4_product(wq_dev, wq, x, "tiny auto", 0)
+    y1 = _check_q4_product(wq_dev, wq, x, "tiny narrow", 1)
+    y2 = _check_q4_product(wq_dev, wq, x, "tiny wide", 2)
+    assert np.array_equal(y0, y1)
+    # the production entry point gives the same bits as the debug one
+    y = to_host(_qs().mul_mat_q4_0_f32(wq_dev, to_dev(x)))
+    assert np.array_equal(y, y0)
+
+
+@pytest.mark.parametrize("j", [0, 1, 2])
+def test_llama7b_decode_m1(j):
+    n, k = workloads.WORKLOADS[1]["shapes"][j]
+    wq_dev, wq = _q4_weights(1, j, n, k)
+    x = workloads.activations(workloads.activation_seed(1, 1), 1, k)
+    _check_q4_product(wq_dev, wq, x, f"7B decode w{j}", 0, (0, n))
+
+
+@pytest.mark.parametrize("j", [0, 1])
+def test_llama3_ffn_batched(j):
+    n, k = workloads.WORKLOADS[3]["shapes"][j]
+    wq_dev, wq = _q4_weights(3, j, n, k)
+    for m in workloads.WORKLOADS[3]["ms"]:
+        x = workloads.activations(workloads.activation_seed(3, m), m, k)
+        cols = (n - 200, n) if m >= 32 else (0, 256)
+        _check_q4_product(wq_dev, wq, x, f"ffn w{j} M={m}", 0, cols)
+
+
+def test_threshold_both_kernels_agree_with_oracle():
+    """Around the narrow/wide threshold, both kernels on the same inputs."""
+    n, k = 4096, 14336
+    wq_dev, wq = _q4_weights(3, 1, n, k)
+    for m in (1, 4, 8, 9, 16):
+        x = workloads.activations(workloads.activation_seed(3, m), m, k)
+        for v in (1, 2):
+            _check_q4_product(wq_dev, wq, x, f"threshold M={m}", v, (0, 64))
+
+
+def _sampled_cols(n, seed, count=384):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(0, 64), np.arange(n - 64, n),
+                                     rng.integers(0, n, count)]))
+
+
+@pytest.mark.parametrize("j", [0, 1, 2])
+def test_prefill_m512_q4_0(j):
+    import torch
+    qs = _qs()
+    n, k = workloads.WORKLOADS[4]["shapes"][j]
+    seed = workloads.weight_seed(4, j)
+    w = workloads.weights_f32(seed, n, k)
+    say("prefill q4_0 quantize", j, n, k)
+    wq_dev = qs.quantize_q4_0(to_dev(w))
+    del w
+    x = workloads.activations(workloads.activation_seed(4, 512), 512, k)
+    say("prefill q4_0 mul_mat", j)
+    cols = _sampled_cols(n, 40 + j)
+    y, dots = qs.debug_mul_mat(qs.MM_TYPE_Q4_0, wq_dev, to_dev(x), 0, n - 32, n)
+    ysel = to_host(y[:, torch.from_numpy(cols).cuda()])
+    wsel = codec.quantize_q4_0(workloads.weights_f32(seed, n, k, rows=cols))
+    assert np.array_equal(to_host(wq_dev[torch.from_numpy(cols).cuda()]), wsel)
+    ref = mul_mat.mul_mat_q4_0_f32_dequant(wsel, x)
+    assert_close(ysel, ref, TOL_Q4_0, f"prefill q4_0 w{j}")
+    wtail = codec.quantize_q4_0(workloads.weights_f32(seed, n, k, rows=np.arange(n - 32, n)))
+    assert np.array_equal(to_host(dots), codec.block_dots(wtail, codec.quantize_q8_0(x), k))
+    # the unsampled columns: every output finite and the production entry gives the same bits
+    y2 = qs.mul_mat_q4_0_f32(wq_dev, to_dev(x))
+    assert bool(torch.equal(y, y2))
+    assert bool(torch.isfinite(y).all())
+    del y, y2, wq_dev
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("j", [0, 1, 2])
+def test_prefill_m512_f16(j):
+    import torch
+    qs = _qs()
+    n, k = workloads.WORKLOADS[4]["shapes"][j]
+    seed = workloads.weight_seed(4, j)
+    say("prefill f16", j, n, k)
+    w16 = to_dev(workloads.weights_f16(seed, n, k))
+    x = workloads.activations(workloads.activation_seed(4, 512), 512, k)
+    y = qs.mul_mat_f16_f32(w16, to_dev(x))
+    cols = _sampled_cols(n, 50 + j)
+    ysel = to_host(y[:, torch.from_numpy(cols).cuda()])
+    ref = mul_mat.mul_mat_f16_f32(workloads.weights_f16(seed, n, k, rows=cols), x)
+    assert_close(ysel, ref, TOL_F, f"prefill f16 w{j}")
+    del y, w16
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind", ["f16", "f32"])
+@pytest.mark.parametrize("j", [0, 1])
+def test_decode_f16_f32(kind, j):
+    qs = _qs()
+    n, k = workloads.WORKLOADS[2]["shapes"][j]
+    seed = workloads.weight_seed(2, j)
+    w = workloads.weights_f16(seed, n, k) if kind == "f16" else workloads.weights_f32(seed, n, k)
+    wd = to_dev(w)
+    for m in workloads.WORKLOADS[2]["ms"]:
+        x = workloads.activations(workloads.activation_seed(2, m), m, k)
+        say("decode", kind, j, m)
+        fn = qs.mul_mat_f16_f32 if kind == "f16" else qs.mul_mat_f32
+        y = to_host(fn(wd, to_dev(x)))
+        ref = mul_mat.mul_mat_f16_f32(w, x) if kind == "f16" else mul_mat.mul_mat_f32(w, x)
+        assert_close(y, ref, TOL_F, f"{kind} w{j} M={m}")
+
+
+# ------------------------------------------------------------------ edges
+@pytest.mark.parametrize("m,n,k", [
+    (1, 1, 32), (1, 1000, 96), (3, 257, 4128), (8, 129, 2080), (9, 77, 1056),
+    (16, 300, 544), (33, 65, 3200), (100, 190, 512), (130, 33, 8192), (513, 70, 256),
+    (1, 64, 14336), (32, 64, 14336), (2, 7, 32),
+])
+def test_ragged_shapes_q4_0(m, n, k):
+    rng = np.random.default_rng(m * 1_000_003 + n * 101 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    wq = codec.quantize_q4_0(w)
+    wq_dev = to_dev(wq)
+    for v in (0, 1, 2):
+        _check_q4_product(wq_dev, wq, x, f"ragged {m}x{n}x{k}", v, (0, min(n, 40)))
+
+
+def test_misaligned_src0_uses_generic_path():
+    """src0 at a 2-byte (not 4-byte) offset: the kernels fall back to 16-bit loads."""
+    import torch
+    rng = np.random.default_rng(9)
+    n, k = 96, 1024
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((5, k)).astype(np.float32)
+    wq = codec.quantize_q4_0(w)
+    buf = torch.zeros(wq.size + 16, dtype=torch.uint8, device="cuda")
+    view = buf[2:2 + wq.size].view(n, wq.shape[1])
+    view.copy_(torch.from_numpy(wq).cuda())
+    assert view.data_ptr() % 4 == 2
+    for v in (1, 2):
+        _check_q4_product(view, wq, x, "misaligned", v, (0, 8))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (2, 33, 7), (5, 100, 1000), (16, 129, 257),
+                                   (17, 70, 300), (40, 300, 64), (130, 129, 200)])
+def test_ragged_shapes_f16_f32(m, n, k):
+    qs = _qs()
+    rng = np.random.default_rng(m * 7919 + n * 31 + k)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    wh = w.astype(np.float16)
+    say("ragged f", m, n, k)
+    y32 = to_host(qs.mul_mat_f32(to_dev(w), to_dev(x)))
+    y16 = to_host(qs.mul_mat_f16_f32(to_dev(wh), to_dev(x)))
+    assert_close(y32, mul_mat.mul_mat_f32(w, x), TOL_F, "f32")
+    assert_close(y16, mul_mat.mul_mat_f16_f32(wh, x), TOL_F, "f16")
+    for v in (1, 2):
+        y, _ = qs.debug_mul_mat(qs.MM_TYPE_F16, to_dev(wh), to_dev(x), v)
+        assert_close(to_host(y), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 variant {v}")
+
+
+def test_empty_and_zero_k():
+    import torch
+    qs = _qs()
+    say("empty / K=0")
+    out = qs.mul_mat_q4_0_f32(torch.zeros((5, 0), dtype=torch.uint8, device="cuda"),
+                              torch.zeros((3, 0), dtype=torch.float32, device="cuda"))
+    assert out.shape == (3, 5) and bool((out == 0).all())
+    out = torch.full((3, 5), 7.0, device="cuda")
+    qs.mul_mat_f32(torch.zeros((5, 0), device="cuda"), torch.zeros((3, 0), device="cuda"), out=out)
+    assert bool((out == 0).all())
+    e = qs.mul_mat_f16_f32(torch.zeros((0, 8), dtype=torch.float16, device="cuda"),
+                           torch.zeros((4, 8), device="cuda"))
+    assert e.shape == (4, 0)
+    e = qs.mul_mat_q4_0_f32(torch.zeros((6, 18), dtype=torch.uint8, device="cuda"),
+                            torch.zeros((0, 32), device="cuda"))
+    assert e.shape == (0, 6)
+
+
+def test_zero_blocks_and_extremes():
+    rng = np.random.default_rng(10)
+    n, k, m = 64, 512, 6
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    w[3] = 0.0
+    w[5, :64] = 0.0
+    w[7] *= 1e4
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[1] = 0.0
+    x[2, 32:96] = 0.0
+    x[4] *= 1e-5
+    wq = codec.quantize_q4_0(w)
+    for v in (1, 2):
+        _check_q4_product(to_dev(wq), wq, x, "zeros/extremes", v, (0, n))
+
+
+def test_deterministic_run_to_run():
+    import torch
+    qs = _qs()
+    n, k = 4096, 14336
+    wq_dev, _ = _q4_weights(3, 1, n, k)
+    for m in (1, 8, 32, 128):
+        x = to_dev(workloads.activations(workloads.activation_seed(3, m), m, k))
+        say("determinism", m)
+        a = qs.mul_mat_q4_0_f32(wq_dev, x)
+        b = qs.mul_mat_q4_0_f32(wq_dev, x)
+        assert bool(torch.equal(a, b)), m
+
+
+def test_batch_vs_alone():
+    """Row m of a batched product equals the M=1 product of that row (within
+    tolerance across kernels; the Q8_0 wdata of the row is identical)."""
+    qs = _qs()
+    n, k = 14336, 4096
+    wq_dev, wq = _q4_weights(3, 0, n, k)
+    x = workloads.activations(workloads.activation_seed(3, 64), 64, k)
+    say("batch vs alone")
+    full = to_host(qs.mul_mat_q4_0_f32(wq_dev, to_dev(x)))
+    for i in (0, 17, 63):
+        alone = to_host(qs.mul_mat_q4_0_f32(wq_dev, to_dev(x[i:i + 1])))
+        assert_close(full[i:i + 1], alone.astype(np.float64), TOL_Q4_0, f"row {i}")
+
+
+def test_workspace_errors_launch_nothing():
+    import torch
+    qs = _qs()
+    w = torch.zeros((64, 18 * 8), dtype=torch.uint8, device="cuda")
+    x = torch.zeros((4, 256), device="cuda")
+    out = torch.full((4, 64), 3.0, device="cuda")
+    need = qs.workspace_size(qs.MM_TYPE_Q4_0, 4, 64, 256)
+    ws = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    st = qs.lib.mm_mul_mat_q4_0_f32(w.data_ptr(), x.data_ptr(), out.data_ptr(), 4, 64, 256,
+                                    ws.data_ptr(), need - 1, None)
+    assert st == -4
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
+
+
+def test_init_compute_stages_equal_the_fused_call():
+    """mm_q4_0_init + mm_q4_0_compute gives the same bits as mm_mul_mat_q4_0_f32, and one
+    init serves several weight matrices of the same shape (split-K tickets included)."""
+    import torch
+    qs = _qs()
+    for (n, k, m) in ((4096, 4096, 1), (64, 14336, 1), (64, 14336, 32), (4096, 14336, 16)):
+        rng = np.random.default_rng(n + k + m)
+        x = to_dev(rng.standard_normal((m, k)).astype(np.float32))
+        say("init/compute", n, k, m)
+        ws = qs.q4_0_init(x, n)
+        for rep in range(3):
+            w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+            wq = codec.quantize_q4_0(w)
+            wq_dev = to_dev(wq)
+            y_stage = qs.q4_0_compute(wq_dev, ws, m, k)
+            y_fused = qs.mul_mat_q4_0_f32(wq_dev, x)
+            assert bool(torch.equal(y_stage, y_fused)), (n, k, m, rep)
+            assert_close(to_host(y_stage), mul_mat.mul_mat_q4_0_f32_dequant(wq, to_host(x)),
+                         TOL_Q4_0, "staged")
