@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Throughput of the Q4_0 MUL_MAT at Llama-7B decode shapes on one MI355X.
+
+One step = the weight products of one decoded token of a Llama-7B-shaped
+model: 32 layers x 7 products at M = 1 (q, k, v, o: 4096x4096; ffn gate,
+up: 11008x4096; ffn down: 4096x11008), each a full mm_mul_mat_q4_0_f32
+call (INIT: quantize the activation row to Q8_0; COMPUTE: the Q4_0 x Q8_0
+product).  The 224 weight matrices are distinct device buffers (3.64 GB of
+Q4_0), so every step streams the whole model from HBM, as decode does (the
+token reads every weight once: smallbard "Generer a plusieurs", opening
+section).  Inputs are resident in HBM before timing starts.
+
+Output: one JSON line on stdout.  `value` is whole-step algorithmic HBM
+traffic / step time (GB/s); `roofline` reports the COMPUTE kernel alone
+(HIP events around graph replays of its launches); `cpu_baseline` times the
+CPU oracle on a bounded sample of the same work.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Q4_0 mul_mat HBM GB/s (M≤16) and TOPS (M≥32), % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+Q4_BYTES_PER_VALUE = 18 / 32   # Q4_0 block: 18 bytes per 32 values
+Q8_BYTES_PER_VALUE = 34 / 32   # Q8_0 block: 34 bytes per 32 values
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q4_narrow_decode.json")
+NARROW_SRC = os.path.join(ROOT, "quantized_skinny_gemm_amd", "csrc", "q4_narrow.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------- accounting
+def q4_step_bytes(m: int, n: int, k: int) -> float:
+    """Algorithmic bytes of one mm_mul_mat_q4_0_f32: Q4_0 weights read once, src1 read,
+    Q8_0 wdata written then read once, dst written."""
+    return Q4_BYTES_PER_VALUE * n * k + 4.0 * m * k + 2.0 * Q8_BYTES_PER_VALUE * m * k + 4.0 * m * n
+
+
+def q4_compute_bytes(m: int, n: int, k: int) -> float:
+    """Algorithmic bytes of the COMPUTE kernel alone: weights, wdata read, dst written."""
+    return Q4_BYTES_PER_VALUE * n * k + Q8_BYTES_PER_VALUE * m * k + 4.0 * m * n
+
+
+def f32_weight_intensity(m: int) -> float:
+    """Operations per byte of f32 weights read for an M-row product: 2*M*N*K / (4*N*K)."""
+    return 2.0 * m / 4.0
+
+
+def product_ops(m: int, n: int, k: int) -> float:
+    return 2.0 * m * n * k
+
+
+# ------------------------------------------------------------ workload
+LAYER_SLOTS = [0, 0, 0, 0, 1, 1, 2]     # q k v o gate up down -> distinct shape index
+
+
+def _shapes():
+    import workloads
+    return [workloads.LLAMA7B_LAYER[0], workloads.LLAMA7B_LAYER[4], workloads.LLAMA7B_LAYER[6]]
+
+
+def setup_gpu(layers: int):
+    import numpy as np
+    import torch
+
+    import quantized_skinny_gemm_amd as qs
+    import workloads
+
+    dev = torch.device("cuda:0")
+    shapes = _shapes()
+    q4_dev = []
+    for j, (n, k) in enumerate(shapes):
+        w = workloads.weights_f32(workloads.weight_seed(1, j), n, k)
+        q4_dev.append(qs.quantize_q4_0(torch.from_numpy(w).to(dev)))
+    # one allocation holding every layer's copy of every slot
+    sizes = [q4_dev[s].numel() for s in LAYER_SLOTS]
+    per_layer = sum(sizes)
+    pool = torch.empty(per_layer * layers, dtype=torch.uint8, device=dev)
+    weights = []
+    off = 0
+    for _ in range(layers):
+        row = []
+        for s, sz in zip(LAYER_SLOTS, sizes):
+            v = pool[off:off + sz].view(q4_dev[s].shape)
+            v.copy_(q4_dev[s])
+            row.append(v)
+            off += sz
+        weights.append(row)
+    xs = {}
+    for n, k in shapes:
+        if k not in xs:
+            xs[k] = torch.from_numpy(workloads.activations(workloads.activation_seed(1, 1), 1, k)).to(dev)
+    dsts = [torch.empty((1, shapes[s][0]), dtype=torch.float32, device=dev) for s in LAYER_SLOTS]
+    ws_bytes = max(qs.workspace_size(qs.MM_TYPE_Q4_0, 1, n, k) for n, k in shapes)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    return dict(qs=qs, torch=torch, np=np, shapes=shapes, weights=weights, xs=xs, dsts=dsts,
+                ws=ws, ws_bytes=ws_bytes, pool_bytes=pool.numel(), pool=pool)
+
+
+def make_step(st, stream_handle):
+    """The list of (fn, args) for one step; every call goes through the C ABI."""
+    lib = st["qs"].lib
+    calls = []
+    for row in st["weights"]:
+        for slot, w in enumerate(row):
+            n, k = st["shapes"][LAYER_SLOTS[slot]]
+            calls.append((lib.mm_mul_mat_q4_0_f32,
+                          (w.data_ptr(), st["xs"][k].data_ptr(), st["dsts"][slot].data_ptr(),
+                           1, n, k, st["ws"].data_ptr(), st["ws_bytes"], stream_handle)))
+    return calls
+
+
+def run_calls(calls):
+    for fn, args in calls:
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"library call failed with status {rc}")
+
+
+def measure_compute_kernel(st, reps: int):
+    """Average duration of the COMPUTE kernel per launch shape, from HIP events
+    recorded on the launch stream around graph replays of back-to-back launches."""
+    torch, qs = st["torch"], st["qs"]
+    lib = qs.lib
+    s = torch.cuda.Stream()
+    res = []
+    for j, (n, k) in enumerate(st["shapes"]):
+        ws_b = qs.workspace_size(qs.MM_TYPE_Q4_0, 1, n, k)
+        ws = torch.empty(ws_b, dtype=torch.uint8, device="cuda")
+        bufs = [row[slot] for row in st["weights"] for slot in range(7) if LAYER_SLOTS[slot] == j]
+        out = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(s):
+            rc = lib.mm_q4_0_init(st["xs"][k].data_ptr(), ws.data_ptr(), 1, n, k, ws_b, s.cuda_stream)
+            assert rc == 0
+            calls = [(lib.mm_q4_0_compute, (b.data_ptr(), out.data_ptr(), 1, n, k, ws.data_ptr(),
+                                            ws_b, s.cuda_stream)) for b in bufs]
+            run_calls(calls)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            run_calls(calls)
+        with torch.cuda.stream(s):
+            g.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+        s.synchronize()
+        avg_us = e0.elapsed_time(e1) * 1e3 / (reps * len(bufs))
+        res.append(dict(n=n, k=k, launches_per_step=len(bufs), avg_us=avg_us,
+                        bytes=q4_compute_bytes(1, n, k)))
+        del g
+    return res
+
+
+def traffic_from_profile(per_launch_bytes):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None when
+    absent or taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+        with open(NARROW_SRC, "rb") as fh:
+            src_hash = hashlib.sha256(fh.read()).hexdigest()
+        if t.get("kernel_source_sha256") != src_hash:
+            return None
+        return float(t["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+# ------------------------------------------------------------ cpu leg
+def cpu_baseline(budget_s: float = 10.0):
+    """The CPU oracle (as it stands) on one layer's 7 products, repeated for
+    about `budget_s` seconds of work; weights quantized by the oracle itself."""
+    import workloads
+    from oracle import codec, mul_mat
+
+    shapes = _shapes()
+    wq = [codec.quantize_q4_0(workloads.weights_f32(workloads.weight_seed(1, j), n, k))
+          for j, (n, k) in enumerate(shapes)]
+    xs = {k: workloads.activations(workloads.activation_seed(1, 1), 1, k) for _, k in shapes}
+    layer_bytes = sum(q4_step_bytes(1, *shapes[s]) for s in LAYER_SLOTS)
+    done = 0
+    c0 = os.times()
+    t0 = time.perf_counter()
+    while True:
+        for s in LAYER_SLOTS:
+            n, k = shapes[s]
+            mul_mat.mul_mat_q4_0_f32(wq[s], xs[k])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    c1 = os.times()
+    cpu = (c1.user - c0.user) + (c1.system - c0.system)
+    return {"value": layer_bytes * done / wall / 1e9, "unit": "GB/s",
+            "cores": max(1, round(cpu / wall)), "kind": "oracle",
+            "sample": f"{done} x one Llama-7B layer at M=1 (7 Q4_0 products incl. Q8_0 "
+                      f"quantize of src1), {wall:.1f} s wall, host: {os.cpu_count()} cpus"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    st = setup_gpu(args.layers)
+    torch = st["torch"]
+    shapes = st["shapes"]
+    log(f"weights resident: {st['pool_bytes'] / 1e9:.3f} GB Q4_0 in {args.layers} layers x 7")
+
+    s = torch.cuda.Stream()
+    calls = make_step(st, s.cuda_stream)
+    with torch.cuda.stream(s):
+        run_calls(calls)                        # first call initialises the device check
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        run_calls(calls)
+
+    with torch.cuda.stream(s):
+        for _ in range(args.warmup):
+            graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        for _ in range(args.steps):
+            graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # the same step without the graph (launch cost included), for reference
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        for _ in range(max(1, args.steps // 10)):
+            run_calls(calls)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - e0) * 1e3 / max(1, args.steps // 10)
+
+    step_bytes = args.layers * sum(q4_step_bytes(1, *shapes[sl]) for sl in LAYER_SLOTS)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"step {ms_per_step:.4f} ms (graph), {eager_ms:.4f} ms (eager); {value:.1f} GB/s")
+
+    kern = measure_compute_kernel(st, args.kernel_reps)
+    tot_bytes = sum(r["bytes"] * r["launches_per_step"] for r in kern)
+    tot_us = sum(r["avg_us"] * r["launches_per_step"] for r in kern)
+    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
+    for r in kern:
+        log(f"compute kernel {r['n']}x{r['k']}: {r['avg_us']:.3f} us/launch, "
+            f"{r['bytes'] / (r['avg_us'] * 1e-6) / 1e9:.1f} GB/s")
+    traffic = traffic_from_profile(tot_bytes / sum(r["launches_per_step"] for r in kern))
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama7b_decode_q4_0_m1",
+            "M": 1,
+            "matrices_per_step": args.layers * 7,
+            "shapes_NxK": [list(shapes[sl]) for sl in LAYER_SLOTS],
+            "layers": args.layers,
+            "weights_GB": round(st["pool_bytes"] / 1e9, 4),
+            "launch": "hip graph of 224 mm_mul_mat_q4_0_f32 calls (2 kernels each)",
+        },
+        "tokens_per_s": round(1e3 / ms_per_step, 2),
+        "eager_ms_per_step": round(eager_ms, 5),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_q4_narrow (COMPUTE stage, M=1)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "per_shape_us": {f"{r['n']}x{r['k']}": round(r["avg_us"], 4) for r in kern},
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle (about 10 s)")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
