@@ -3,15 +3,18 @@
 
 One step = the weight products of one decoded token of a Llama-7B-shaped
 model: 32 layers x 7 products at M = 1 (q, k, v, o: 4096x4096; ffn gate,
-up: 11008x4096; ffn down: 4096x11008), each a full mm_mul_mat_q4_0_f32
-call (INIT: quantize the activation row to Q8_0; COMPUTE: the Q4_0 x Q8_0
-product).  The 224 weight matrices are distinct device buffers (3.64 GB of
+up: 11008x4096; ffn down: 4096x11008), each the full product (INIT:
+quantize the activation row to Q8_0; COMPUTE: the Q4_0 x Q8_0 product).
+The products that share an input -- q, k, v and gate, up -- are issued as
+one mm_mul_mat_q4_0_f32_group call each, the others as mm_mul_mat_q4_0_f32:
+4 launches per layer.  The same step issued as one call per matrix is
+timed too and reported beside it.  The 224 weight matrices are distinct device buffers (3.64 GB of
 Q4_0), so every step streams the whole model from HBM, as decode does (the
 token reads every weight once: smallbard "Generer a plusieurs", opening
 section).  Inputs are resident in HBM before timing starts.
 
 Output: one JSON line on stdout.  `value` is whole-step algorithmic HBM
-traffic / step time (GB/s); `roofline` reports the COMPUTE kernel alone
+traffic / step time (GB/s); `roofline` reports the product kernel alone
 (HIP events around graph replays of its launches); `cpu_baseline` times the
 CPU oracle on a bounded sample of the same work.
 
@@ -47,6 +50,12 @@ def q4_step_bytes(m: int, n: int, k: int) -> float:
     """Algorithmic bytes of one mm_mul_mat_q4_0_f32: Q4_0 weights read once, src1 read,
     Q8_0 wdata written then read once, dst written."""
     return Q4_BYTES_PER_VALUE * n * k + 4.0 * m * k + 2.0 * Q8_BYTES_PER_VALUE * m * k + 4.0 * m * n
+
+
+def q4_fused_bytes(m: int, n: int, k: int) -> float:
+    """Algorithmic bytes of the product when INIT is fused into it: the Q8_0 wdata
+    stays in on-chip memory, so only weights, src1 and dst touch HBM."""
+    return Q4_BYTES_PER_VALUE * n * k + 4.0 * m * k + 4.0 * m * n
 
 
 def q4_compute_bytes(m: int, n: int, k: int) -> float:
@@ -111,61 +120,94 @@ def setup_gpu(layers: int):
                 ws=ws, ws_bytes=ws_bytes, pool_bytes=pool.numel(), pool=pool)
 
 
-def make_step(st, stream_handle):
-    """The list of (fn, args) for one step; every call goes through the C ABI."""
+def _group_args(ws_list, outs, ns):
+    import ctypes
+    count = len(ws_list)
+    src = (ctypes.c_void_p * count)(*[w.data_ptr() for w in ws_list])
+    dst = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
+    narr = (ctypes.c_int64 * count)(*ns)
+    return src, dst, narr
+
+
+def make_calls(st, stream_handle, grouped: bool):
+    """Per layer, the list of (kind, fn, args, bytes) of one decode token's products.
+    grouped: q, k, v in one grouped call and gate, up in another (they share src1);
+    otherwise one mm_mul_mat_q4_0_f32 per matrix.  Every call goes through the C ABI."""
     lib = st["qs"].lib
-    calls = []
+    ws, wsb = st["ws"].data_ptr(), st["ws_bytes"]
+    layers = []
     for row in st["weights"]:
-        for slot, w in enumerate(row):
-            n, k = st["shapes"][LAYER_SLOTS[slot]]
-            calls.append((lib.mm_mul_mat_q4_0_f32,
-                          (w.data_ptr(), st["xs"][k].data_ptr(), st["dsts"][slot].data_ptr(),
-                           1, n, k, st["ws"].data_ptr(), st["ws_bytes"], stream_handle)))
-    return calls
+        calls = []
+        if grouped:
+            for kind, slots in (("qkv", [0, 1, 2]), ("o", [3]), ("gate_up", [4, 5]), ("down", [6])):
+                n_k = [st["shapes"][LAYER_SLOTS[sl]] for sl in slots]
+                k = n_k[0][1]
+                # src1 is read once per launch
+                nbytes = sum(q4_fused_bytes(1, n, k) for n, _ in n_k) - 4.0 * k * (len(slots) - 1)
+                if len(slots) == 1:
+                    sl = slots[0]
+                    args = (row[sl].data_ptr(), st["xs"][k].data_ptr(), st["dsts"][sl].data_ptr(),
+                            1, n_k[0][0], k, ws, wsb, stream_handle)
+                    calls.append((kind, lib.mm_mul_mat_q4_0_f32, args, nbytes))
+                else:
+                    src, dst, narr = _group_args([row[sl] for sl in slots],
+                                                 [st["dsts"][sl] for sl in slots], [n for n, _ in n_k])
+                    st.setdefault("_keep", []).append((src, dst, narr))
+                    args = (len(slots), src, dst, narr, st["xs"][k].data_ptr(), 1, k, ws, wsb,
+                            stream_handle)
+                    calls.append((kind, lib.mm_mul_mat_q4_0_f32_group, args, nbytes))
+        else:
+            for sl, w in enumerate(row):
+                n, k = st["shapes"][LAYER_SLOTS[sl]]
+                args = (w.data_ptr(), st["xs"][k].data_ptr(), st["dsts"][sl].data_ptr(), 1, n, k,
+                        ws, wsb, stream_handle)
+                calls.append((f"{n}x{k}", lib.mm_mul_mat_q4_0_f32, args, q4_fused_bytes(1, n, k)))
+        layers.append(calls)
+    return layers
 
 
 def run_calls(calls):
-    for fn, args in calls:
-        rc = fn(*args)
+    for c in calls:
+        rc = c[1](*c[2])
         if rc != 0:
             raise RuntimeError(f"library call failed with status {rc}")
 
 
-def measure_compute_kernel(st, reps: int):
-    """Average duration of the COMPUTE kernel per launch shape, from HIP events
-    recorded on the launch stream around graph replays of back-to-back launches."""
-    torch, qs = st["torch"], st["qs"]
-    lib = qs.lib
-    s = torch.cuda.Stream()
-    res = []
-    for j, (n, k) in enumerate(st["shapes"]):
-        ws_b = qs.workspace_size(qs.MM_TYPE_Q4_0, 1, n, k)
-        ws = torch.empty(ws_b, dtype=torch.uint8, device="cuda")
-        bufs = [row[slot] for row in st["weights"] for slot in range(7) if LAYER_SLOTS[slot] == j]
-        out = torch.empty((1, n), dtype=torch.float32, device="cuda")
-        with torch.cuda.stream(s):
-            rc = lib.mm_q4_0_init(st["xs"][k].data_ptr(), ws.data_ptr(), 1, n, k, ws_b, s.cuda_stream)
-            assert rc == 0
-            calls = [(lib.mm_q4_0_compute, (b.data_ptr(), out.data_ptr(), 1, n, k, ws.data_ptr(),
-                                            ws_b, s.cuda_stream)) for b in bufs]
-            run_calls(calls)
-        s.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            run_calls(calls)
-        with torch.cuda.stream(s):
+def time_graph(torch, s, calls, reps):
+    """Graph of `calls` on stream s; average ms per replay from HIP events on s."""
+    with torch.cuda.stream(s):
+        run_calls(calls)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run_calls(calls)
+    with torch.cuda.stream(s):
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
             g.replay()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(s)
-            for _ in range(reps):
-                g.replay()
-            e1.record(s)
-        s.synchronize()
-        avg_us = e0.elapsed_time(e1) * 1e3 / (reps * len(bufs))
-        res.append(dict(n=n, k=k, launches_per_step=len(bufs), avg_us=avg_us,
-                        bytes=q4_compute_bytes(1, n, k)))
-        del g
+        e1.record(s)
+    s.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_kernels(st, layers, reps: int, s):
+    """Average duration per launch of each call kind (every M=1 call here is
+    one kernel: INIT fused), from HIP events on the launch stream s (the one
+    the calls are bound to) around graph replays of that kind's launches over
+    all layers."""
+    torch = st["torch"]
+    kinds = {}
+    for calls in layers:
+        for c in calls:
+            kinds.setdefault(c[0], []).append(c)
+    res = []
+    for kind, calls in kinds.items():
+        ms = time_graph(torch, s, calls, reps)
+        res.append(dict(kind=kind, launches_per_step=len(calls), avg_us=ms * 1e3 / len(calls),
+                        bytes=calls[0][3]))
     return res
 
 
@@ -238,13 +280,15 @@ def main():
     log(f"weights resident: {st['pool_bytes'] / 1e9:.3f} GB Q4_0 in {args.layers} layers x 7")
 
     s = torch.cuda.Stream()
-    calls = make_step(st, s.cuda_stream)
+    grouped = make_calls(st, s.cuda_stream, grouped=True)
+    single = make_calls(st, s.cuda_stream, grouped=False)
+    step_calls = [c for layer in grouped for c in layer]
     with torch.cuda.stream(s):
-        run_calls(calls)                        # first call initialises the device check
+        run_calls(step_calls)                   # first call initialises the device check
     s.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s):
-        run_calls(calls)
+        run_calls(step_calls)
 
     with torch.cuda.stream(s):
         for _ in range(args.warmup):
@@ -258,25 +302,24 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # the same step without the graph (launch cost included), for reference
-    torch.cuda.synchronize()
-    e0 = time.perf_counter()
-    with torch.cuda.stream(s):
-        for _ in range(max(1, args.steps // 10)):
-            run_calls(calls)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - e0) * 1e3 / max(1, args.steps // 10)
+    # the same products as one call per matrix (7 launches per layer)
+    single_ms = time_graph(torch, s, [c for layer in single for c in layer], max(1, args.steps // 4))
 
     step_bytes = args.layers * sum(q4_step_bytes(1, *shapes[sl]) for sl in LAYER_SLOTS)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"step {ms_per_step:.4f} ms (graph), {eager_ms:.4f} ms (eager); {value:.1f} GB/s")
+    log(f"step {ms_per_step:.4f} ms grouped ({len(step_calls)} launches), {single_ms:.4f} ms "
+        f"one call per matrix; {value:.1f} GB/s")
 
-    kern = measure_compute_kernel(st, args.kernel_reps)
+    kern = measure_kernels(st, grouped, args.kernel_reps, s)
+    kern_single = measure_kernels(st, single, args.kernel_reps, s)
+    for r in kern_single:
+        log(f"one call per matrix, kernel {r['kind']}: {r['avg_us']:.3f} us/launch, "
+            f"{r['bytes'] / (r['avg_us'] * 1e-6) / 1e9:.1f} GB/s")
     tot_bytes = sum(r["bytes"] * r["launches_per_step"] for r in kern)
     tot_us = sum(r["avg_us"] * r["launches_per_step"] for r in kern)
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
     for r in kern:
-        log(f"compute kernel {r['n']}x{r['k']}: {r['avg_us']:.3f} us/launch, "
+        log(f"kernel {r['kind']}: {r['avg_us']:.3f} us/launch, "
             f"{r['bytes'] / (r['avg_us'] * 1e-6) / 1e9:.1f} GB/s")
     traffic = traffic_from_profile(tot_bytes / sum(r["launches_per_step"] for r in kern))
 
@@ -300,19 +343,21 @@ def main():
             "shapes_NxK": [list(shapes[sl]) for sl in LAYER_SLOTS],
             "layers": args.layers,
             "weights_GB": round(st["pool_bytes"] / 1e9, 4),
-            "launch": "hip graph of 224 mm_mul_mat_q4_0_f32 calls (2 kernels each)",
+            "launch": f"hip graph of {len(step_calls)} calls: per layer q,k,v grouped, o, "
+                      "gate,up grouped, down; one kernel each (INIT fused)",
         },
         "tokens_per_s": round(1e3 / ms_per_step, 2),
-        "eager_ms_per_step": round(eager_ms, 5),
+        "one_call_per_matrix_ms_per_step": round(single_ms, 5),
+        "one_call_per_matrix_GBs": round(step_bytes / (single_ms * 1e-3) / 1e9, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_q4_narrow (COMPUTE stage, M=1)",
+            "kernel": "k_q4_narrow (INIT fused), M=1, all launches of the step",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "per_shape_us": {f"{r['n']}x{r['k']}": round(r["avg_us"], 4) for r in kern},
+            "per_kind_us": {r["kind"]: round(r["avg_us"], 4) for r in kern},
         },
     }
     if not args.no_cpu_baseline:

@@ -122,6 +122,21 @@ int mm_q4_0_compute(const void* src0, float* dst, int64_t M, int64_t N, int64_t 
                     const void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mm_mul_mat_q4_0_f32_group -- several Q4_0 products that share src1, in as
+ * few launches as possible: dsts[i][M][Ns[i]] = Q8_0(src1) . src0s[i]^T for
+ * i < count (1 <= count <= 8), e.g. the q, k and v projections of one
+ * activation, or the ffn gate and up projections.  src0s, dsts and Ns are
+ * HOST arrays of count entries; every src0s[i] and dsts[i] follows the rules
+ * of mm_mul_mat_q4_0_f32 (shared M, K, src1); the dsts must not overlap
+ * each other or any src0.  Results equal count separate mm_mul_mat_q4_0_f32
+ * calls.  ws: mm_mul_mat_q4_0_group_workspace_size(count, Ns, M, K) bytes.
+ */
+int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const* dsts,
+                              const int64_t* Ns, const float* src1, int64_t M, int64_t K,
+                              void* ws, size_t ws_bytes, void* stream);
+size_t mm_mul_mat_q4_0_group_workspace_size(int count, const int64_t* Ns, int64_t M, int64_t K);
+
+/*
  * mm_mul_mat_f16_f32 -- dst[M][N] = src1[M][K] . f32(src0[N][K])^T, fp32 accumulation.
  *   src0: IEEE binary16 [N][K], 2-byte aligned.  src1: f32 [M][K], 4-byte
  *   aligned.  dst: f32, 4-byte aligned.  Any K >= 0.  For M <= 16 src1 is
@@ -154,11 +169,13 @@ const char* mm_status_string(int status);
 
 /*
  * mm_dispatch -- the kernel choice mm_mul_mat_* makes at this shape (pure
- * host function).  Writes up to 4 ints to out (may be NULL):
+ * host function).  Writes 5 ints to out (may be NULL):
  *   out[0] variant: 1 = narrow-M kernel, 2 = wide-M (MFMA) kernel
  *   out[1] split-K factor (1 = none)
  *   out[2] rows of src1 per pass (narrow) or output tile rows (wide)
  *   out[3] output tile columns (wide) or src0 rows per wave (narrow)
+ *   out[4] kernels one call launches on the stream (for Q4_0 at small M
+ *          the INIT stage is fused into the product kernel: 1)
  * Returns MM_OK or MM_ERR_SHAPE / MM_ERR_ARG.
  */
 int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);

@@ -23,7 +23,8 @@ __all__ = [
     "LIB_PATH", "lib", "MM_TYPE_F32", "MM_TYPE_F16", "MM_TYPE_Q4_0", "MM_TYPE_Q8_0",
     "MMError", "quantize_q4_0", "quantize_q8_0", "mul_mat_q4_0_f32", "mul_mat_f16_f32",
     "mul_mat_f32", "workspace_size", "debug_workspace_size", "row_bytes", "dispatch",
-    "debug_mul_mat", "status_string", "q4_0_init", "q4_0_compute",
+    "debug_mul_mat", "status_string", "q4_0_init", "q4_0_compute", "mul_mat_q4_0_f32_group",
+    "group_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsgemm.so")
@@ -46,6 +47,9 @@ for _name, _args, _res in [
     ("mm_mul_mat_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     ("mm_q4_0_init", [_vp, _vp, _i64, _i64, _i64, _sz, _vp], _int),
     ("mm_q4_0_compute", [_vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    ("mm_mul_mat_q4_0_f32_group", [_int, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                   ctypes.POINTER(_i64), _vp, _i64, _i64, _vp, _sz, _vp], _int),
+    ("mm_mul_mat_q4_0_group_workspace_size", [_int, ctypes.POINTER(_i64), _i64, _i64], _sz),
     ("mm_mul_mat_workspace_size", [_int, _i64, _i64, _i64], _sz),
     ("mm_debug_workspace_size", [_int, _i64, _i64, _i64, _int], _sz),
     ("mm_row_bytes", [_int, _i64], _i64),
@@ -101,8 +105,8 @@ def debug_workspace_size(mm_type: int, m: int, n: int, k: int, variant: int) -> 
 
 
 def dispatch(mm_type: int, m: int, n: int, k: int):
-    """(variant, split, rows, cols): the kernel mm_mul_mat_* picks at this shape."""
-    out = (_int * 4)()
+    """(variant, split, rows, cols, launches): the kernel mm_mul_mat_* picks at this shape."""
+    out = (_int * 5)()
     _check(lib.mm_dispatch(int(mm_type), int(m), int(n), int(k), out), "mm_dispatch")
     return tuple(out)
 
@@ -159,6 +163,33 @@ def mul_mat_q4_0_f32(w: torch.Tensor, x: torch.Tensor, out=None, ws=None) -> tor
     if w.shape[1] != row_bytes(MM_TYPE_Q4_0, x.shape[1]):
         raise ValueError("w row bytes do not match K")
     return _mul_mat(lib.mm_mul_mat_q4_0_f32, MM_TYPE_Q4_0, w, x, out, ws, "mm_mul_mat_q4_0_f32")
+
+
+def group_workspace_size(ns, m: int, k: int) -> int:
+    arr = (_i64 * len(ns))(*ns)
+    return int(lib.mm_mul_mat_q4_0_group_workspace_size(len(ns), arr, int(m), int(k)))
+
+
+def mul_mat_q4_0_f32_group(ws_list, x: torch.Tensor, outs=None, ws=None):
+    """[Q8_0(x) . Q4_0(w)^T for w in ws_list] as one grouped call (shared x); returns the outputs."""
+    x = _dev(x, "x", torch.float32)
+    m, k = x.shape
+    ws_list = [_dev(w, f"w[{i}]", torch.uint8) for i, w in enumerate(ws_list)]
+    for w in ws_list:
+        if w.shape[1] != row_bytes(MM_TYPE_Q4_0, k):
+            raise ValueError("w row bytes do not match K")
+    ns = [w.shape[0] for w in ws_list]
+    if outs is None:
+        outs = [torch.empty((m, n), dtype=torch.float32, device=x.device) for n in ns]
+    count = len(ws_list)
+    src = (_vp * count)(*[w.data_ptr() for w in ws_list])
+    dst = (_vp * count)(*[o.data_ptr() for o in outs])
+    narr = (_i64 * count)(*ns)
+    ws = _workspace(group_workspace_size(ns, m, k), x.device, ws)
+    nbytes = 0 if ws is None else ws.numel()
+    _check(lib.mm_mul_mat_q4_0_f32_group(count, src, dst, narr, _ptr(x), m, k, _ptr(ws), nbytes,
+                                         _stream(x)), "mm_mul_mat_q4_0_f32_group")
+    return outs
 
 
 def mul_mat_f16_f32(w: torch.Tensor, x: torch.Tensor, out=None, ws=None) -> torch.Tensor:

@@ -45,32 +45,46 @@ Q4Args q4_args(const Plan& p, const void* src0, float* dst, int32_t* dots, int64
   a.ab = (const int32_t*)(base + p.off_ab);
   a.dst = dst;
   a.part = p.split > 1 ? (float*)(base + p.off_part) : nullptr;
-  a.tick = p.split > 1 ? (uint32_t*)(base + p.off_tick) : nullptr;
   a.M = (int)M; a.N = (int)N; a.K = (int)K;
   a.dots = dots; a.n0 = (int)n0; a.n1 = (int)n1;
   return a;
 }
 
-// INIT: src1 -> Q8_0 wdata in the workspace (and zeroed split-K tickets).
+// INIT: src1 -> Q8_0 wdata in the workspace.
 int q4_init(const Plan& p, const float* src1, int64_t M, int64_t K, void* ws, hipStream_t s) {
   uint8_t* base = (uint8_t*)ws;
-  const int64_t nticks = p.split > 1 ? p.tiles_m * p.tiles_n : 0;
   return hip_status(launch_quantize_q8_0(src1, M, K, nullptr, (int8_t*)(base + p.off_aq),
-                                         (float*)(base + p.off_ad), (int32_t*)(base + p.off_ab),
-                                         nticks ? (uint32_t*)(base + p.off_tick) : nullptr,
-                                         nticks, s));
+                                         (float*)(base + p.off_ad), (int32_t*)(base + p.off_ab), s));
 }
 
-// COMPUTE: src0 x wdata -> dst.
-int q4_compute(const Plan& p, const Q4Args& a, hipStream_t s) {
-  return hip_status(p.kind == KK_Q4_NARROW ? launch_q4_narrow(p, a, s) : launch_q4_wide(p, a, s));
+Q4Mats single_mat(const void* src0, float* dst, int64_t N) {
+  Q4Mats m;
+  for (int i = 0; i < kMaxGroup; ++i) { m.w[i] = nullptr; m.dst[i] = nullptr; }
+  for (int i = 0; i <= kMaxGroup; ++i) m.row0[i] = (int)N;
+  m.w[0] = (const uint8_t*)src0;
+  m.dst[0] = dst;
+  m.row0[0] = 0;
+  m.count = 1;
+  return m;
+}
+
+// The product kernel (x != NULL: INIT fused), then the split-K reduction.
+int q4_product(const Plan& p, const Q4Args& a, const float* x, hipStream_t s) {
+  hipError_t e = p.kind == KK_Q4_NARROW
+                     ? launch_q4_narrow(p, a, single_mat(a.w, a.dst, a.N), x, s)
+                     : launch_q4_wide(p, a, s);
+  if (e == hipSuccess && p.split > 1)
+    e = launch_splitk_reduce(a.part, a.dst, (int64_t)a.M * a.N, p.split, s);
+  return hip_status(e);
 }
 
 int run_q4_0(const Plan& p, const void* src0, const float* src1, float* dst, int32_t* dots,
              int64_t M, int64_t N, int64_t K, int64_t n0, int64_t n1, void* ws, hipStream_t s) {
+  const Q4Args a = q4_args(p, src0, dst, dots, M, N, K, n0, n1, ws);
+  if (p.kind == KK_Q4_NARROW && p.fuse) return q4_product(p, a, src1, s);
   const int st = q4_init(p, src1, M, K, ws, s);
   if (st != MM_OK) return st;
-  return q4_compute(p, q4_args(p, src0, dst, dots, M, N, K, n0, n1, ws), s);
+  return q4_product(p, a, nullptr, s);
 }
 
 int mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* dots,
@@ -106,8 +120,7 @@ int quantize(int out_type, const float* x, void* y, int64_t nrows, int64_t k, vo
   if (st != MM_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (out_type == MM_TYPE_Q4_0) return hip_status(launch_quantize_q4_0(x, nrows, k, (uint8_t*)y, s));
-  return hip_status(launch_quantize_q8_0(x, nrows, k, (uint8_t*)y, nullptr, nullptr, nullptr,
-                                         nullptr, 0, s));
+  return hip_status(launch_quantize_q8_0(x, nrows, k, (uint8_t*)y, nullptr, nullptr, nullptr, s));
 }
 
 }  // namespace
@@ -162,7 +175,125 @@ int mm_q4_0_compute(const void* src0, float* dst, int64_t M, int64_t N, int64_t 
   if (st != MM_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (p.kind == KK_ZERO) return hip_status(launch_zero(dst, M * N, s));
-  return q4_compute(p, q4_args(p, src0, dst, nullptr, M, N, K, 0, 0, (void*)ws), s);
+  return q4_product(p, q4_args(p, src0, dst, nullptr, M, N, K, 0, 0, (void*)ws), nullptr, s);
+}
+
+namespace {
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Plan of a grouped product: narrow -> one launch over the concatenated rows
+// (no split); wide -> one plan per matrix, sharing the wdata at the front of
+// the workspace.  Returns the workspace size through *ws.
+int group_plan(int count, const int64_t* Ns, int64_t M, int64_t K, Plan* whole, int64_t* ntot,
+               size_t* ws) {
+  if (count < 1 || count > kMaxGroup) return MM_ERR_ARG;
+  if (!Ns) return MM_ERR_NULL;
+  int64_t tot = 0;
+  for (int i = 0; i < count; ++i) {
+    if (Ns[i] < 0) return MM_ERR_SHAPE;
+    tot += Ns[i];
+  }
+  if (tot > 0x7fffffff) return MM_ERR_SHAPE;
+  *ntot = tot;
+  int st = make_plan(MM_TYPE_Q4_0, M, tot, K, 0, whole, /*allow_split=*/false);
+  if (st != MM_OK) return st;
+  size_t need = whole->ws_bytes;
+  if (whole->kind == KK_Q4_WIDE) {
+    for (int i = 0; i < count; ++i) {
+      Plan pi;
+      st = make_plan(MM_TYPE_Q4_0, M, Ns[i], K, 0, &pi);
+      if (st != MM_OK) return st;
+      if (pi.ws_bytes > need) need = pi.ws_bytes;
+    }
+  }
+  *ws = need;
+  return MM_OK;
+}
+
+}  // namespace
+
+size_t mm_mul_mat_q4_0_group_workspace_size(int count, const int64_t* Ns, int64_t M, int64_t K) {
+  Plan p;
+  int64_t tot;
+  size_t ws = 0;
+  if (group_plan(count, Ns, M, K, &p, &tot, &ws) != MM_OK) return 0;
+  return ws;
+}
+
+int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const* dsts,
+                              const int64_t* Ns, const float* src1, int64_t M, int64_t K,
+                              void* ws, size_t ws_bytes, void* stream) {
+  Plan whole;
+  int64_t ntot = 0;
+  size_t need = 0;
+  int st = group_plan(count, Ns, M, K, &whole, &ntot, &need);
+  if (st != MM_OK) return st;
+  if (!src0s || !dsts) return MM_ERR_NULL;
+  if (M == 0 || ntot == 0) return MM_OK;
+  // each product on its own, then the group as a whole
+  const int64_t rbytes = row_bytes(MM_TYPE_Q4_0, K);
+  for (int i = 0; i < count; ++i) {
+    if (Ns[i] == 0) continue;
+    Plan pi = whole;
+    pi.ws_bytes = need;
+    st = validate_mul_mat(MM_TYPE_Q4_0, src0s[i], src1, dsts[i], M, Ns[i], K, ws, ws_bytes, pi);
+    if (st != MM_OK) return st;
+    for (int j = 0; j < count; ++j) {
+      if (j == i || Ns[j] == 0) continue;
+      if (ranges_overlap(dsts[i], (size_t)M * Ns[i] * 4, dsts[j], (size_t)M * Ns[j] * 4) ||
+          (K > 0 && ranges_overlap(dsts[i], (size_t)M * Ns[i] * 4, src0s[j], (size_t)Ns[j] * rbytes)))
+        return MM_ERR_ALIAS;
+    }
+  }
+  st = check_device();
+  if (st != MM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (K == 0) {
+    for (int i = 0; i < count; ++i) {
+      if (Ns[i] == 0) continue;
+      st = hip_status(launch_zero(dsts[i], M * Ns[i], s));
+      if (st != MM_OK) return st;
+    }
+    return MM_OK;
+  }
+  if (whole.kind == KK_Q4_NARROW) {
+    Q4Mats mats;
+    int row = 0, c = 0;
+    for (int i = 0; i < kMaxGroup; ++i) { mats.w[i] = nullptr; mats.dst[i] = nullptr; }
+    for (int i = 0; i < count; ++i) {
+      if (Ns[i] == 0) continue;
+      mats.w[c] = (const uint8_t*)src0s[i];
+      mats.dst[c] = dsts[i];
+      mats.row0[c] = row;
+      row += (int)Ns[i];
+      ++c;
+    }
+    for (int i = c; i <= kMaxGroup; ++i) mats.row0[i] = row;
+    mats.count = c;
+    const Q4Args a = q4_args(whole, mats.w[0], mats.dst[0], nullptr, M, ntot, K, 0, 0, ws);
+    if (!whole.fuse) {
+      st = q4_init(whole, src1, M, K, ws, s);
+      if (st != MM_OK) return st;
+    }
+    return hip_status(launch_q4_narrow(whole, a, mats, whole.fuse ? src1 : nullptr, s));
+  }
+  // wide: one INIT, then one product per matrix (same wdata layout at the
+  // front of every per-matrix plan)
+  st = q4_init(whole, src1, M, K, ws, s);
+  if (st != MM_OK) return st;
+  for (int i = 0; i < count; ++i) {
+    if (Ns[i] == 0) continue;
+    Plan pi;
+    make_plan(MM_TYPE_Q4_0, M, Ns[i], K, 0, &pi);
+    st = q4_product(pi, q4_args(pi, src0s[i], dsts[i], nullptr, M, Ns[i], K, 0, 0, ws), nullptr, s);
+    if (st != MM_OK) return st;
+  }
+  return MM_OK;
 }
 
 size_t mm_mul_mat_workspace_size(int type, int64_t M, int64_t N, int64_t K) {
@@ -188,6 +319,8 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
     out[1] = p.split;
     out[2] = p.variant == 2 ? p.bm : p.mt;
     out[3] = p.variant == 2 ? p.bn : p.rpw;
+    const int init = (p.type == MM_TYPE_Q4_0 && !(p.kind == KK_Q4_NARROW && p.fuse)) ? 1 : 0;
+    out[4] = init + 1 + (p.split > 1 ? 1 : 0);
   }
   return MM_OK;
 }

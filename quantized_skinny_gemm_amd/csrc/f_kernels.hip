@@ -234,7 +234,26 @@ __global__ void k_zero(float* __restrict__ p, int64_t n) {
     p[i] = 0.0f;
 }
 
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part,
+                                                      float* __restrict__ dst, int64_t n,
+                                                      int split) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float s = 0.0f;
+    for (int z = 0; z < split; ++z) s += part[(int64_t)z * n + i];
+    dst[i] = s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_splitk_reduce(const float* part, float* dst, int64_t n, int split,
+                                hipStream_t s) {
+  int64_t grid = (n + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  if (grid < 1) return hipSuccess;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)grid), dim3(256), 0, s, part, dst, n, split);
+  return hipGetLastError();
+}
 
 hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* x, float* dst,
                            int M, int N, int K, hipStream_t s) {

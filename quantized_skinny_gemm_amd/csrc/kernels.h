@@ -11,11 +11,9 @@ namespace qsg {
 // Q8_0 activation quantisation.  Writes the canonical 34-byte blocks to
 // `canon` (may be NULL) and/or the library's internal wdata layout
 // (codes int8 [rows][k], scales f32 [rows][k/32], bias -8*sum(q) int32
-// [rows][k/32]; all NULL to skip).  Also zeroes `zero_words` 32-bit words at
-// `zero` (split-K tickets) in the same launch.
+// [rows][k/32]; all NULL to skip).
 hipError_t launch_quantize_q8_0(const float* x, int64_t nrows, int64_t k, uint8_t* canon,
-                                int8_t* wq, float* wd, int32_t* wb, uint32_t* zero,
-                                int64_t zero_words, hipStream_t s);
+                                int8_t* wq, float* wd, int32_t* wb, hipStream_t s);
 
 hipError_t launch_quantize_q4_0(const float* x, int64_t nrows, int64_t k, uint8_t* y,
                                 hipStream_t s);
@@ -27,13 +25,28 @@ struct Q4Args {
   const int32_t* ab;     // wdata -8*sum(q)
   float* dst;
   float* part;           // split-K partials [split][M][N]
-  uint32_t* tick;        // split-K tickets, one per output tile
   int M, N, K;
   int32_t* dots;         // debug block dots (NULL in production)
   int n0, n1;
 };
 
-hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, hipStream_t s);
+// Weight matrices that share src1, concatenated along N for the narrow
+// kernel: global row r of the group belongs to matrix i with
+// row0[i] <= r < row0[i+1] and is row r - row0[i] of w[i]; its outputs go to
+// column r - row0[i] of dst[i] ([M][N_i]).
+constexpr int kMaxGroup = 8;
+struct Q4Mats {
+  const uint8_t* w[kMaxGroup];
+  float* dst[kMaxGroup];
+  int row0[kMaxGroup + 1];
+  int count;
+};
+
+// x != NULL selects the fused kernel: src1 (f32) is quantized to Q8_0 in LDS
+// by every workgroup (p.fuse must be set); x == NULL reads the wdata in a.
+// a.N is the total row count of mats; a.w / a.dst are unused here.
+hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, const float* x,
+                            hipStream_t s);
 hipError_t launch_q4_wide(const Plan& p, const Q4Args& a, hipStream_t s);
 
 hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* x, float* dst,
@@ -41,5 +54,7 @@ hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* 
 hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, float* dst,
                            int M, int N, int K, hipStream_t s);
 hipError_t launch_zero(float* dst, int64_t n, hipStream_t s);
+// dst[i] = sum over z = 0..split-1, in that order, of part[z * n + i].
+hipError_t launch_splitk_reduce(const float* part, float* dst, int64_t n, int split, hipStream_t s);
 
 }  // namespace qsg

@@ -40,7 +40,7 @@ int64_t row_bytes(int type, int64_t K) {
   }
 }
 
-int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p) {
+int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, bool allow_split) {
   *p = Plan();
   p->type = type;
   if (type != MM_TYPE_F32 && type != MM_TYPE_F16 && type != MM_TYPE_Q4_0) return MM_ERR_ARG;
@@ -62,21 +62,36 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p) {
       p->variant = 1;
       p->mt = narrow_mt(M, kNarrowQ4MaxM);
       p->rpw = p->mt <= 2 ? 2 : 4;
+      p->waves = p->mt <= 2 ? 8 : 4;
       p->tiles_m = ceil_div(M, p->mt);
-      p->tiles_n = ceil_div(N, 4 * p->rpw);
+      p->tiles_n = ceil_div(N, p->waves * p->rpw);
       // K units of the narrow kernel are block pairs (blocks when K/32 is odd).
       const int64_t units = (nb % 2 == 0) ? nb / 2 : nb;
-      const int64_t wgs = p->tiles_m * p->tiles_n;
+      // Split K when there are fewer than 4 waves per CU.
+      const int64_t waves = p->tiles_m * p->tiles_n * p->waves;
       int64_t split = 1;
-      if (wgs < 2 * kCUs) {
+      if (allow_split && waves < 4 * kCUs) {
         const int64_t max_split = units / 64;        // keep every lane busy
-        split = ceil_div(2 * kCUs, wgs);
+        split = ceil_div(4 * kCUs, waves);
         if (split > max_split) split = max_split;
         if (split > 16) split = 16;
         if (split < 1) split = 1;
       }
       p->kchunk = ceil_div(units, split);
       p->split = (int)ceil_div(units, p->kchunk);
+      // At most kNarrowMaxGrid workgroups along N, each walking an equal
+      // number of row groups (the activation slice is staged once per
+      // workgroup, so fewer, longer-lived workgroups re-read it less).
+      {
+        const int64_t per = ceil_div(p->tiles_n, kNarrowMaxGrid);
+        p->grid_n = ceil_div(p->tiles_n, per);
+      }
+      // Fuse the INIT stage (src1 -> Q8_0 in LDS, 40 bytes per block and row)
+      // when the pass is small: every workgroup re-quantizes its src1 slice,
+      // which costs about M / (0.56 * rows per wave) of the weight traffic in
+      // L2 reads, and saves a launch and the wdata round trip.
+      const int64_t kblocks = (nb % 2 == 0) ? 2 * p->kchunk : p->kchunk;
+      p->fuse = p->mt <= kFuseMaxM && (int64_t)p->mt * kblocks * 40 <= kNarrowMaxLds;
     } else {
       p->kind = KK_Q4_WIDE;
       p->variant = 2;
@@ -95,7 +110,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p) {
       const int64_t tiles = p->tiles_m * p->tiles_n;
       const int64_t stages = ceil_div(nb, kWideKB);
       int64_t split = 1;
-      if (tiles < kCUs) {
+      if (allow_split && tiles < kCUs) {
         split = ceil_div(kCUs, tiles);
         const int64_t max_split = stages / 2;          // >= 2 stages per split
         if (split > max_split) split = max_split;
@@ -107,7 +122,6 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p) {
     }
     if (p->split > 1) {
       p->off_part = off; off = align_up(off + (size_t)p->split * (size_t)M * (size_t)N * 4, 256);
-      p->off_tick = off; off = align_up(off + (size_t)(p->tiles_m * p->tiles_n) * 4, 256);
     }
     p->ws_bytes = off;
     return MM_OK;

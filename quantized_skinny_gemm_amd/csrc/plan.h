@@ -24,6 +24,9 @@ constexpr int kWideKB = 4;         // Q4_0 blocks per LDS stage in the wide kern
 constexpr int kF16WideKS = 32;     // k elements per LDS stage in the f16 wide kernel
 constexpr int kNarrowQ4MaxM = 8;   // largest M the Q4_0 narrow kernel takes in one pass
 constexpr int kNarrowFMaxM = 16;   // largest M the f16/f32 narrow kernel takes in one pass
+constexpr int kFuseMaxM = 2;       // narrow Q4_0 passes of at most this many rows fuse INIT
+constexpr int kNarrowMaxLds = 65536; // LDS bytes the narrow kernel may stage activations in
+constexpr int kNarrowMaxGrid = 512;  // narrow workgroups along N (2 per CU)
 
 enum KernelKind {
   KK_NONE = 0,      // nothing to do (M == 0 or N == 0)
@@ -41,20 +44,26 @@ struct Plan {
   // narrow kernels
   int mt = 1;               // src1 rows per pass (compile-time tile)
   int rpw = 1;              // src0 rows per wave
+  int waves = 4;            // waves per workgroup
   // wide kernels
   int bm = 0, bn = 0, waves_m = 0, waves_n = 0;
   // grid
   int64_t tiles_m = 1;      // wide: output tile rows; narrow: passes over M
-  int64_t tiles_n = 1;      // output tile columns (narrow: groups of 4*rpw src0 rows)
+  int64_t tiles_n = 1;      // output tile columns (narrow: row groups of waves*rpw src0 rows)
+  int64_t grid_n = 1;       // narrow: workgroups along N (each walks tiles_n / grid_n row groups)
   int split = 1;            // split-K factor
+  bool fuse = false;        // narrow Q4_0: quantize src1 inside the product kernel
   int64_t kchunk = 0;       // K units per split (Q4_0: blocks; f16: elements)
   // workspace layout (bytes)
-  size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0, off_tick = 0;
+  size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0;
   size_t ws_bytes = 0;
 };
 
 // Builds the plan; returns 0 (MM_OK) or a negative mm_status.
-int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p);
+// allow_split = false keeps K whole (used when several matrices share one
+// launch: their outputs are written directly, never as split partials).
+int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p,
+              bool allow_split = true);
 
 // Which operands a call takes: the whole product, or one of the two stages
 // of the quantized product (INIT: src1 -> wdata; COMPUTE: src0 x wdata -> dst).

@@ -6,23 +6,29 @@
 // At decode shapes the product is bound by reading the weights (arXiv
 // 2407.07304, section 2.2: the next-token phase is GEMV-like and memory
 // bound; DeepSpeed-Inference notes, III.A: small batches are limited by the
-// bandwidth of reading the weights).  smallbard "Generer a plusieurs" shows
-// a narrow kernel that re-reads each weight per pack of 8 rows; here each
-// weight byte is read exactly once for all M rows of the pass:
+// bandwidth of reading the weights, and by the fixed cost of every kernel
+// launch).  smallbard "Generer a plusieurs" shows a narrow kernel that
+// re-reads each weight per pack of 8 rows; here each weight byte is read
+// exactly once for all M rows of the pass:
 //
 //   * a wave owns R consecutive weight rows; lane l walks the row's 36-byte
 //     block pairs l, l+64, ... (a pair is 4-byte aligned when K/32 is even,
-//     so it loads as dwordx4 + dwordx4 + dword);
+//     so it loads as dwordx4 + dwordx4 + dword), and the next pair's loads
+//     are issued before the current pair is computed;
 //   * nibbles are unpacked in registers; each block costs 8 v_dot4 per
 //     activation row, seeded with -8 * sum(q8) so that the unsigned nibbles
 //     give the signed block dot;
-//   * the fp32 accumulators are reduced over the 64 lanes with a fixed
-//     butterfly (DeepSpeed-Inference notes, III.C: reduce each output's
-//     partials in registers within one wave);
+//   * the fp32 accumulators are reduced over the 64 lanes with DPP row
+//     operations in a fixed order (DeepSpeed-Inference notes, III.C: reduce
+//     each output's partials in registers within one wave);
+//   * the activations of the workgroup's K slice are staged in LDS; for
+//     small M the INIT stage is fused in: every workgroup quantizes the src1
+//     rows (and K range) it needs into LDS with the same Q8_0 routine as the
+//     stand-alone quantizer, so one launch does the whole product;
 //   * when the grid would not fill the device, K is split across workgroups
-//     and the last workgroup of each tile adds the partial sums in a fixed
-//     order (smallbard, "La courbe, une premiere fois": cut the common
-//     dimension into slices and add the partial sums afterwards).
+//     and a second kernel adds the partial sums in a fixed order (smallbard,
+//     "La courbe, une premiere fois": cut the common dimension into slices
+//     and add the partial sums afterwards).
 #include "device.h"
 #include "kernels.h"
 
@@ -30,13 +36,21 @@ namespace qsg {
 
 namespace {
 
+// Where a kernel reads the Q8_0 activation codes, scales and -8*sum(q).
+struct ActView {
+  const int8_t* q;      // codes of row 0, block boff
+  const float* d;       // scale of row 0, block boff
+  const int32_t* bias;  // -8 * sum(q) of row 0, block boff
+  int64_t qpitch;       // bytes between rows of codes
+  int64_t dpitch;       // entries between rows of scales / bias
+  int boff;             // first block held
+  int rows;             // valid rows (>= 1)
+};
+
 template <int MT, int R, bool kDump>
-__device__ __forceinline__ void block_mac(const uint32_t (&q)[R][4], const float (&dw)[R],
-                                          int b, int nb, int K, const int8_t* __restrict__ aq,
-                                          const float* __restrict__ ad,
-                                          const int32_t* __restrict__ ab, int m0, int M,
-                                          float (&acc)[R][MT], int nw, int32_t* __restrict__ dots,
-                                          int n0d, int n1d) {
+__device__ __forceinline__ void block_mac(const uint32_t (&q)[R][4], const float (&dw)[R], int b,
+                                          const ActView& av, float (&acc)[R][MT], int nw, int m0,
+                                          int nb, const Q4Args& a) {
   uint32_t lo[R][4], hi[R][4];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -46,13 +60,14 @@ __device__ __forceinline__ void block_mac(const uint32_t (&q)[R][4], const float
       hi[r][j] = (q[r][j] >> 4) & 0x0F0F0F0Fu;   // elements 16+4j .. 16+4j+3
     }
   }
+  const int bl = b - av.boff;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int mm = (m0 + m < M) ? m0 + m : M - 1;
-    const v4i* ap = reinterpret_cast<const v4i*>(aq + (int64_t)mm * K + (int64_t)b * 32);
+    const int mm = m < av.rows ? m : av.rows - 1;
+    const v4i* ap = reinterpret_cast<const v4i*>(av.q + mm * av.qpitch + (int64_t)bl * 32);
     const v4i a0 = ap[0], a1 = ap[1];
-    const float da = ad[(int64_t)mm * nb + b];
-    const int bias = ab[(int64_t)mm * nb + b];
+    const float da = av.d[mm * av.dpitch + bl];
+    const int bias = av.bias[mm * av.dpitch + bl];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       int s = bias;
@@ -67,142 +82,448 @@ __device__ __forceinline__ void block_mac(const uint32_t (&q)[R][4], const float
       acc[r][m] = fmaf((float)s, dw[r] * da, acc[r][m]);
       if (kDump) {
         const int n = nw + r;
-        if (m0 + m < M && n >= n0d && n < n1d)
-          dots[((int64_t)(m0 + m) * (n1d - n0d) + (n - n0d)) * nb + b] = s;
+        if (m0 + m < a.M && n >= a.n0 && n < a.n1)
+          a.dots[((int64_t)(m0 + m) * (a.n1 - a.n0) + (n - a.n0)) * nb + b] = s;
       }
     }
   }
 }
 
+// Loads one K unit (a 36-byte block pair, or one 18-byte block as 16-bit
+// words) of each of the wave's rows.
+template <int R, bool kPairs>
+__device__ __forceinline__ void load_unit(uint32_t (&wv)[R][9], const uint8_t* const (&rowp)[R],
+                                          int64_t u) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (kPairs) {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(rowp[r] + 36 * u);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) wv[r][i] = p[i];
+    } else {
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(rowp[r] + 18 * u);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) wv[r][i] = p[i];
+    }
+  }
+}
+
 template <int MT, int R, bool kPairs, bool kDump>
-__global__ __launch_bounds__(256) void k_q4_narrow(Q4Args a, int64_t kchunk, int split) {
+__device__ __forceinline__ void unit_mac(const uint32_t (&wv)[R][9], int64_t u, const ActView& av,
+                                         float (&acc)[R][MT], int nw, int m0, int nb,
+                                         const Q4Args& a) {
+  if (kPairs) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t q[R][4];
+      float dw[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (half == 0) {
+          dw[r] = f16_bits_to_f32(wv[r][0]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) q[r][j] = __builtin_amdgcn_alignbit(wv[r][j + 1], wv[r][j], 16);
+        } else {
+          dw[r] = f16_bits_to_f32(wv[r][4] >> 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) q[r][j] = wv[r][5 + j];
+        }
+      }
+      block_mac<MT, R, kDump>(q, dw, (int)(2 * u + half), av, acc, nw, m0, nb, a);
+    }
+  } else {
+    uint32_t q[R][4];
+    float dw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      dw[r] = f16_bits_to_f32(wv[r][0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[r][j] = wv[r][1 + 2 * j] | (wv[r][2 + 2 * j] << 16);
+    }
+    block_mac<MT, R, kDump>(q, dw, (int)u, av, acc, nw, m0, nb, a);
+  }
+}
+
+// Staging of the activation slice into LDS, in batches of kBatch rounds of
+// NT threads.  load_*: issue the global loads of one batch (unconditional,
+// on clamped addresses); store_*: consume them into LDS.
+struct Slice {
+  int total, kbmax, nbs, rows, m0, b0, K, nb;
+};
+
+// Splits a staging block index into (row m < MT, block bl < kbmax) without a
+// division (MT is small).
+template <int MT>
+__device__ __forceinline__ void split_blk(int blk, int kbmax, int& m, int& bl) {
+  m = 0;
+#pragma unroll
+  for (int j = 1; j < MT; ++j) m += blk >= j * kbmax ? 1 : 0;
+  bl = blk - m * kbmax;
+}
+
+// Quantize staging: two lanes per block (items i = 2*block + half), each
+// holding 16 values.
+template <int NT, int kBatch, int MT>
+__device__ __forceinline__ void quant_load(const Slice& sl, const float* __restrict__ x, int it0,
+                                           int rounds, float (&v)[kBatch][16],
+                                           bool (&ok)[kBatch]) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int i = (it0 + j) * NT + (int)threadIdx.x;
+    const int blk = i >> 1, h = i & 1;
+    int m, bl;
+    split_blk<MT>(blk, sl.kbmax, m, bl);
+    ok[j] = it0 + j < rounds && i < sl.total && bl < sl.nbs && m < sl.rows;
+    const int64_t off = ok[j] ? (int64_t)(sl.m0 + m) * sl.K + (int64_t)(sl.b0 + bl) * 32 + 16 * h
+                              : (int64_t)sl.m0 * sl.K + (int64_t)sl.b0 * 32 + 16 * h;
+    const float4* p = reinterpret_cast<const float4*>(x + off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = p[q];
+      v[j][4 * q] = f.x; v[j][4 * q + 1] = f.y; v[j][4 * q + 2] = f.z; v[j][4 * q + 3] = f.w;
+    }
+  }
+}
+
+template <int NT, int kBatch, int MT>
+__device__ __forceinline__ void quant_store(const Slice& sl, int it0, int rounds,
+                                            float (&v)[kBatch][16], const bool (&ok)[kBatch],
+                                            int8_t* sq, float* sd, int32_t* sb) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    if (it0 + j < rounds) {                          // uniform over the workgroup
+      const int i = (it0 + j) * NT + (int)threadIdx.x;
+      const int blk = i >> 1, h = i & 1;
+      int m, bl;
+      split_blk<MT>(blk, sl.kbmax, m, bl);
+      if (!ok[j]) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[j][e] = 0.0f;
+      }
+      uint32_t packed[4], dbits;
+      int sum;
+      q8_0_pair(v[j], packed, dbits, sum);
+      if (ok[j]) {
+        *reinterpret_cast<uint4*>(sq + (int64_t)m * sl.kbmax * 32 + bl * 32 + 16 * h) =
+            make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        if (h == 0) {
+          sd[m * sl.kbmax + bl] = f16_bits_to_f32(dbits);
+          sb[m * sl.kbmax + bl] = -8 * sum;
+        }
+      }
+    }
+  }
+}
+
+template <int NT, int kBatch, int MT>
+__device__ __forceinline__ void copy_load(const Slice& sl, const Q4Args& a, int it0, int rounds,
+                                          v4i (&c)[kBatch], float (&d)[kBatch], int (&bi)[kBatch],
+                                          bool (&ok)[kBatch]) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int i = (it0 + j) * NT + (int)threadIdx.x;
+    int m, bl;
+    split_blk<MT>(i >> 1, sl.kbmax, m, bl);
+    const int cc = 2 * bl + (i & 1);
+    ok[j] = it0 + j < rounds && i < sl.total && bl < sl.nbs && m < sl.rows;
+    const int64_t row = ok[j] ? sl.m0 + m : sl.m0;
+    const int64_t blk = ok[j] ? sl.b0 + bl : sl.b0;
+    const int half = ok[j] ? (cc & 1) : 0;
+    c[j] = *reinterpret_cast<const v4i*>(a.aq + row * sl.K + blk * 32 + half * 16);
+    d[j] = a.ad[row * sl.nb + blk];
+    bi[j] = a.ab[row * sl.nb + blk];
+  }
+}
+
+template <int NT, int kBatch, int MT>
+__device__ __forceinline__ void copy_store(const Slice& sl, int it0, const v4i (&c)[kBatch],
+                                           const float (&d)[kBatch], const int (&bi)[kBatch],
+                                           const bool (&ok)[kBatch], int8_t* sq, float* sd,
+                                           int32_t* sb) {
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int i = (it0 + j) * NT + (int)threadIdx.x;
+    int m, bl;
+    split_blk<MT>(i >> 1, sl.kbmax, m, bl);
+    const int cc = 2 * bl + (i & 1);
+    if (ok[j]) {
+      *reinterpret_cast<v4i*>(sq + (int64_t)m * sl.kbmax * 32 + bl * 32 + (cc & 1) * 16) = c[j];
+      if ((cc & 1) == 0) {
+        sd[m * sl.kbmax + bl] = d[j];
+        sb[m * sl.kbmax + bl] = bi[j];
+      }
+    }
+  }
+}
+
+// Where the activations come from.  kActGlobal: the Q8_0 wdata in global
+// memory, read at use.  kActCopy: the wdata K-slice copied into LDS first.
+// kActQuant: src1 (f32) quantized into LDS by the workgroup itself (INIT
+// fused).  In both LDS forms the slice's loads are issued before the first
+// weight loads: vmcnt retires in order, so consuming the activations never
+// waits on weights still streaming in from HBM, and the barrier is LDS-only.
+enum { kActGlobal = 0, kActCopy = 1, kActQuant = 2 };
+
+__device__ __forceinline__ int mat_of(const Q4Mats& mats, int n) {
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxGroup; ++j)
+    if (j < mats.count && n >= mats.row0[j]) i = j;
+  return i;
+}
+
+// Row pointers of the wave's R rows in row group g (rows past the end are
+// clamped to the last row; their results are never stored).
+template <int R, int RPG>
+__device__ __forceinline__ void rows_of(const Q4Mats& mats, int g, int wave, int N, int64_t rb,
+                                        const uint8_t* (&rp)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int n = g * RPG + wave * R + r;
+    n = n < N ? n : N - 1;
+    const int i = mat_of(mats, n);
+    rp[r] = mats.w[i] + (int64_t)(n - mats.row0[i]) * rb;
+  }
+}
+
+// kBatch: activation-slice loads in flight per thread (sized to the slice).
+// Small-M variants with short K slices ask for 6 waves per SIMD (at most 80
+// VGPRs; the second launch-bounds argument is waves per execution unit
+// here), so that all workgroups are resident at once; longer K slices
+// (larger kBatch) hold more staging registers.
+//
+// Work layout: rows are taken in groups of WAVES * R (R per wave); a grid of
+// at most a few workgroups per CU walks the groups g = blockIdx.x,
+// blockIdx.x + gridDim.x, ... after staging the activations once, so the
+// activation slice is read (and, fused, quantized) once per workgroup rather
+// than once per row group.  Each wave runs a flat sequence of (group, K unit)
+// steps and loads the next step's weights before computing the current one.
+template <int MT, int R, int WAVES, bool kPairs, bool kDump, int kAct, int kBatch>
+__global__ __launch_bounds__(64 * WAVES, MT > 2 ? 1 : kAct == kActQuant ? (kBatch <= 1 ? 6 : 5) : (kBatch <= 4 ? 6 : 1))
+void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kchunk, int split) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int RPG = WAVES * R;                     // rows per group
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // uniform within the wave: row and matrix lookups run on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int M = a.M, N = a.N, K = a.K;
   const int nb = K / 32;
   const int64_t rb = (int64_t)nb * 18;
   const int m0 = blockIdx.y * MT;
   const int z = blockIdx.z;
-  const int nw = (blockIdx.x * 4 + wave) * R;
+  const int ngroups = (N + RPG - 1) / RPG;
+  constexpr int kBPU = kPairs ? 2 : 1;               // blocks per K unit
+  const int64_t units = kPairs ? nb / 2 : nb;
+  const int64_t u0 = (int64_t)z * kchunk;
+  const int64_t u1 = (u0 + kchunk < units) ? u0 + kchunk : units;
+  const int SU = (int)((u1 - u0 + 63) / 64);         // steps per row group
+  int g = blockIdx.x;
+  if (g >= ngroups || SU <= 0) return;               // uniform over the workgroup
+  const int kbmax = (int)(kchunk * kBPU);            // LDS capacity in blocks per row
+  const int b0 = (int)(u0 * kBPU);
+  const int nbs = (int)((u1 * kBPU < nb ? u1 * kBPU : nb) - b0);
 
-  const uint8_t* rowp[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int n = (nw + r < N) ? nw + r : N - 1;
-    rowp[r] = a.w + (int64_t)n * rb;
+  ActView av;
+  av.rows = (M - m0 < MT) ? M - m0 : MT;
+  int8_t* sq = smem;
+  float* sd = reinterpret_cast<float*>(smem + (int64_t)MT * kbmax * 32);
+  int32_t* sb = reinterpret_cast<int32_t*>(sd + MT * kbmax);
+
+  const uint8_t* rp[R];
+  rows_of<R, RPG>(mats, g, wave, N, rb, rp);
+  uint32_t wv[R][9];
+  // Loads below are unconditional, on clamped (always valid) addresses, with
+  // the values masked afterwards: straight-line code lets the compiler wait
+  // for exactly the loads a value needs instead of for every load in flight.
+  const int64_t ufirst = u0 + lane < u1 ? u0 + lane : u0;
+  Slice sl;
+  sl.kbmax = kbmax; sl.nbs = nbs; sl.rows = av.rows; sl.m0 = m0; sl.b0 = b0; sl.K = K; sl.nb = nb;
+  if (kAct == kActQuant) {
+    sl.total = MT * kbmax * 2;                       // 2 lanes per block
+    const int rounds = (sl.total + NT - 1) / NT;
+    {
+      float v[kBatch][16];
+      bool ok[kBatch];
+      quant_load<NT, kBatch, MT>(sl, x, 0, rounds, v, ok);
+      load_unit<R, kPairs>(wv, rp, ufirst);          // after the slice's loads
+      quant_store<NT, kBatch, MT>(sl, 0, rounds, v, ok, sq, sd, sb);
+    }
+    for (int it0 = kBatch; it0 < rounds; it0 += kBatch) {
+      float v[kBatch][16];
+      bool ok[kBatch];
+      quant_load<NT, kBatch, MT>(sl, x, it0, rounds, v, ok);
+      quant_store<NT, kBatch, MT>(sl, it0, rounds, v, ok, sq, sd, sb);
+    }
+    lds_barrier();
+  } else if (kAct == kActCopy) {
+    // 16-byte code chunks; the thread holding a block's first chunk also
+    // stores its scale and bias.
+    sl.total = MT * kbmax * 2;
+    const int rounds = (sl.total + NT - 1) / NT;
+    {
+      v4i c[kBatch];
+      float d[kBatch];
+      int bi[kBatch];
+      bool ok[kBatch];
+      copy_load<NT, kBatch, MT>(sl, a, 0, rounds, c, d, bi, ok);
+      load_unit<R, kPairs>(wv, rp, ufirst);          // after the slice's loads
+      copy_store<NT, kBatch, MT>(sl, 0, c, d, bi, ok, sq, sd, sb);
+    }
+    for (int it0 = kBatch; it0 < rounds; it0 += kBatch) {
+      v4i c[kBatch];
+      float d[kBatch];
+      int bi[kBatch];
+      bool ok[kBatch];
+      copy_load<NT, kBatch, MT>(sl, a, it0, rounds, c, d, bi, ok);
+      copy_store<NT, kBatch, MT>(sl, it0, c, d, bi, ok, sq, sd, sb);
+    }
+    lds_barrier();
+  } else {
+    load_unit<R, kPairs>(wv, rp, ufirst);
   }
+
+  if (kAct == kActGlobal) {
+    av.q = a.aq + (int64_t)m0 * K;
+    av.d = a.ad + (int64_t)m0 * nb;
+    av.bias = a.ab + (int64_t)m0 * nb;
+    av.qpitch = K; av.dpitch = nb; av.boff = 0;
+  } else {
+    av.q = sq; av.d = sd; av.bias = sb;
+    av.qpitch = (int64_t)kbmax * 32; av.dpitch = kbmax; av.boff = b0;
+  }
+
   float acc[R][MT];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
-  const int64_t units = kPairs ? nb / 2 : nb;
-  const int64_t u0 = (int64_t)z * kchunk;
-  const int64_t u1 = (u0 + kchunk < units) ? u0 + kchunk : units;
-
-  for (int64_t u = u0 + lane; u < u1; u += 64) {
-    if (kPairs) {
-      uint32_t wv[R][9];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(rowp[r] + 36 * u);
-#pragma unroll
-        for (int i = 0; i < 9; ++i) wv[r][i] = p[i];
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t q[R][4];
-        float dw[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (half == 0) {
-            dw[r] = f16_bits_to_f32(wv[r][0]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) q[r][j] = __builtin_amdgcn_alignbit(wv[r][j + 1], wv[r][j], 16);
-          } else {
-            dw[r] = f16_bits_to_f32(wv[r][4] >> 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) q[r][j] = wv[r][5 + j];
-          }
-        }
-        block_mac<MT, R, kDump>(q, dw, (int)(2 * u + half), nb, K, a.aq, a.ad, a.ab, m0, M, acc,
-                                nw, a.dots, a.n0, a.n1);
-      }
+  int i = 0;                                         // K step within the group
+  for (;;) {
+    // the next step: (gn, in)
+    int in = i + 1, gn = g;
+    if (in == SU) { in = 0; gn = g + (int)gridDim.x; }
+    const bool more = gn < ngroups;
+    const uint8_t* rpn[R];
+    if (gn != g) {
+      rows_of<R, RPG>(mats, more ? gn : g, wave, N, rb, rpn);
     } else {
-      uint32_t q[R][4];
-      float dw[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(rowp[r] + 18 * u);
-        uint32_t hw[9];
-#pragma unroll
-        for (int i = 0; i < 9; ++i) hw[i] = p[i];
-        dw[r] = f16_bits_to_f32(hw[0]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) q[r][j] = hw[1 + 2 * j] | (hw[2 + 2 * j] << 16);
-      }
-      block_mac<MT, R, kDump>(q, dw, (int)u, nb, K, a.aq, a.ad, a.ab, m0, M, acc, nw, a.dots,
-                              a.n0, a.n1);
+      for (int r = 0; r < R; ++r) rpn[r] = rp[r];
     }
-  }
+    uint32_t cur[R][9];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < 9; ++j) cur[r][j] = wv[r][j];
+    // prefetch the next step (past the last one it reloads a valid unit)
+    int64_t un = u0 + lane + 64 * (int64_t)in;
+    un = un < u1 ? un : u0;
+    load_unit<R, kPairs>(wv, rpn, un);
 
-  // Reduce each accumulator over the wave; lane r*MT+m stores output (m, nw+r).
-  float mine = 0.0f;
+    const int64_t u = u0 + lane + 64 * (int64_t)i;
+    const int nw = g * RPG + wave * R;
+    if (u < u1) unit_mac<MT, R, kPairs, kDump>(cur, u, av, acc, nw, m0, nb, a);
+
+    if (i == SU - 1) {
+      // Reduce each accumulator over the wave; lane r*MT+m stores (m, row nw+r).
+      float mine = 0.0f;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float v = wave_sum(acc[r][m]);
-      if (lane == r * MT + m) mine = v;
+        for (int m = 0; m < MT; ++m) {
+          const float v = wave_sum_dpp(acc[r][m]);
+          if (lane == r * MT + m) mine = v;
+          acc[r][m] = 0.0f;
+        }
+      const int r = lane / MT, m = lane % MT;
+      const int n = nw + r;
+      if (lane < R * MT && m0 + m < M && n < N) {
+        if (split == 1) {
+          const int mi = mat_of(mats, n);
+          const int ni = mats.row0[mi + 1] - mats.row0[mi];
+          mats.dst[mi][(int64_t)(m0 + m) * ni + (n - mats.row0[mi])] = mine;
+        } else {
+          a.part[((int64_t)z * M + m0 + m) * N + n] = mine;
+        }
+      }
     }
-  const int r = lane / MT, m = lane % MT;
-  const bool owner = lane < R * MT && m0 + m < M && nw + r < N;
-  if (split == 1) {
-    if (owner) a.dst[(int64_t)(m0 + m) * N + nw + r] = mine;
-    return;
+    if (!more && in == 0) break;
+    g = gn;
+    i = in;
+#pragma unroll
+    for (int r = 0; r < R; ++r) rp[r] = rpn[r];
   }
-  if (owner) a.part[((int64_t)z * M + m0 + m) * N + nw + r] = mine;
-  const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-  if (splitk_arrive(a.tick + tile, split))
-    splitk_reduce_tile(a.part, a.dst, M, N, m0, MT, blockIdx.x * 4 * R, 4 * R, split);
 }
 
-template <int MT, int R>
-hipError_t launch_mt(const Plan& p, const Q4Args& a, bool pairs, hipStream_t s) {
-  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.split);
-  const dim3 block(256);
+template <int MT, int R, int WAVES, bool kPairs, bool kDump, int kBatch>
+void launch_5(const dim3& grid, size_t lds, int act, const Q4Args& a, const Q4Mats& mats,
+              const float* x, int64_t kchunk, int split, hipStream_t s) {
+  const dim3 block(64 * WAVES);
+  if constexpr (kBatch <= 2) {
+    if (act == kActQuant) {
+      hipLaunchKernelGGL((k_q4_narrow<MT, R, WAVES, kPairs, kDump, kActQuant, kBatch>), grid, block, lds, s, a, mats, x, kchunk, split);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_q4_narrow<MT, R, WAVES, kPairs, kDump, kActCopy, kBatch>), grid, block, lds, s, a, mats, x, kchunk, split);
+}
+
+template <int MT, int R, int WAVES, bool kPairs, bool kDump>
+void launch_4(const dim3& grid, size_t lds, int act, int rounds, const Q4Args& a,
+              const Q4Mats& mats, const float* x, int64_t kchunk, int split, hipStream_t s) {
+  if (act == kActGlobal) {
+    hipLaunchKernelGGL((k_q4_narrow<MT, R, WAVES, kPairs, kDump, kActGlobal, 1>), grid, dim3(64 * WAVES), 0, s, a, mats, x, kchunk, split);
+    return;
+  }
+  // quantize items hold 16 floats each: at most 2 in flight per thread
+  if (rounds <= 1) launch_5<MT, R, WAVES, kPairs, kDump, 1>(grid, lds, act, a, mats, x, kchunk, split, s);
+  else if (rounds <= 2 || act == kActQuant) launch_5<MT, R, WAVES, kPairs, kDump, 2>(grid, lds, act, a, mats, x, kchunk, split, s);
+  else if (rounds <= 4) launch_5<MT, R, WAVES, kPairs, kDump, 4>(grid, lds, act, a, mats, x, kchunk, split, s);
+  else launch_5<MT, R, WAVES, kPairs, kDump, 8>(grid, lds, act, a, mats, x, kchunk, split, s);
+}
+
+template <int MT, int R, int WAVES>
+hipError_t launch_mt(const Plan& p, const Q4Args& a, const Q4Mats& mats, const float* x, bool pairs,
+                     hipStream_t s) {
+  const dim3 grid((unsigned)p.grid_n, (unsigned)p.tiles_m, (unsigned)p.split);
+  const int bpu = pairs ? 2 : 1;
+  const size_t lds = (size_t)MT * (size_t)(p.kchunk * bpu) * 40;
+  const int act = x ? kActQuant : (lds <= (size_t)kNarrowMaxLds ? kActCopy : kActGlobal);
+  // staging rounds per thread: 2 lane items per block (quantize or copy)
+  const int64_t items = (int64_t)MT * p.kchunk * bpu * 2;
+  const int rounds = (int)((items + 64 * WAVES - 1) / (64 * WAVES));
   const bool dump = a.dots != nullptr;
   if (pairs) {
-    if (dump) hipLaunchKernelGGL((k_q4_narrow<MT, R, true, true>), grid, block, 0, s, a, p.kchunk, p.split);
-    else hipLaunchKernelGGL((k_q4_narrow<MT, R, true, false>), grid, block, 0, s, a, p.kchunk, p.split);
+    if (dump) launch_4<MT, R, WAVES, true, true>(grid, lds, act, rounds, a, mats, x, p.kchunk, p.split, s);
+    else launch_4<MT, R, WAVES, true, false>(grid, lds, act, rounds, a, mats, x, p.kchunk, p.split, s);
   } else {
-    if (dump) hipLaunchKernelGGL((k_q4_narrow<MT, R, false, true>), grid, block, 0, s, a, p.kchunk, p.split);
-    else hipLaunchKernelGGL((k_q4_narrow<MT, R, false, false>), grid, block, 0, s, a, p.kchunk, p.split);
+    if (dump) launch_4<MT, R, WAVES, false, true>(grid, lds, act, rounds, a, mats, x, p.kchunk, p.split, s);
+    else launch_4<MT, R, WAVES, false, false>(grid, lds, act, rounds, a, mats, x, p.kchunk, p.split, s);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, hipStream_t s) {
+hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, const float* x,
+                            hipStream_t s) {
   const int nb = a.K / 32;
-  const bool pairs = (nb % 2 == 0) && ((uintptr_t)a.w % 4 == 0);
-  // The plan counts K units as pairs exactly when K/32 is even; the generic
-  // path (single blocks) is only taken with an odd K/32 or a 2-byte-aligned
-  // src0, in which case the plan's units are blocks or the split is 1.
+  bool aligned = true;
+  for (int i = 0; i < mats.count; ++i) aligned = aligned && ((uintptr_t)mats.w[i] % 4 == 0);
+  const bool pairs = (nb % 2 == 0) && aligned;
+  // The plan counts K units as pairs exactly when K/32 is even; with a
+  // 2-byte-aligned src0 the kernel walks single blocks instead, so the chunk
+  // (in units) doubles and the split count is unchanged.
   Plan q = p;
-  if (!pairs && nb % 2 == 0) {
-    // units become blocks: rescale the chunk (split count unchanged)
-    q.kchunk = p.kchunk * 2;
-  }
-  switch (p.mt) {
-    case 1: return launch_mt<1, 2>(q, a, pairs, s);
-    case 2: return launch_mt<2, 2>(q, a, pairs, s);
-    case 4: return launch_mt<4, 4>(q, a, pairs, s);
-    case 8: return launch_mt<8, 4>(q, a, pairs, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (!pairs && nb % 2 == 0) q.kchunk = p.kchunk * 2;
+  // rows per wave and waves per workgroup must match make_plan()
+  if (p.mt == 1 && p.rpw == 2 && p.waves == 8) return launch_mt<1, 2, 8>(q, a, mats, x, pairs, s);
+  if (p.mt == 2 && p.rpw == 2 && p.waves == 8) return launch_mt<2, 2, 8>(q, a, mats, x, pairs, s);
+  if (p.mt == 4 && p.rpw == 4 && p.waves == 4) return launch_mt<4, 4, 4>(q, a, mats, x, pairs, s);
+  if (p.mt == 8 && p.rpw == 4 && p.waves == 4) return launch_mt<8, 4, 4>(q, a, mats, x, pairs, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qsg

@@ -17,9 +17,9 @@
 //   * each wave runs WM x WN MFMAs per block and applies the fp32 scale
 //     epilogue acc += f32(S_b) * (d_a * d_w);
 // and, when the tiles cannot fill the device, K is split across workgroups
-// whose partial tiles the last arriving workgroup adds in fixed order
-// (smallbard "Generer a plusieurs", "La courbe, une premiere fois";
-// DeepSpeed-Inference notes, III.C SBI-GeMM tiling).
+// whose partial tiles a second kernel adds in fixed order (smallbard
+// "Generer a plusieurs", "La courbe, une premiere fois"; DeepSpeed-Inference
+// notes, III.C SBI-GeMM: a second kernel reduces across the input-dim tiles).
 #include "device.h"
 #include "kernels.h"
 
@@ -220,8 +220,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
         if (m < M && n < N) out[(int64_t)m * N + n] = acc[i][j][r];
       }
     }
-  if (split > 1 && splitk_arrive(a.tick + tt, split))
-    splitk_reduce_tile(a.part, a.dst, M, N, m0, BM, n0, BN, split);
 }
 
 template <int BM, int BN, int WMS, int WNS>

@@ -5,9 +5,9 @@
 // COMPUTE); Arm China NUMA article, MulMat operator section (src1 is
 // quantized into wdata, then dst = src0 * wdata).
 //
-// Layout of the work: one 8-lane group per 32-value block, each lane owning
-// four consecutive values (one 16-byte load).  The block's absmax is reduced
-// across the 8 lanes with xor shuffles.  Codes follow the fp32 op sequence:
+// Layout of the work: Q8_0 uses a pair of lanes per 32-value block (16
+// values, four 16-byte loads each); Q4_0 an 8-lane group per block (four
+// values each).  The block's absmax is reduced across the lanes of the group.  Codes follow the fp32 op sequence:
 // one correctly rounded reciprocal per block, one fp32 product per value,
 // (Q4_0) one fp32 add of 8.5 -- with FP contraction disabled so that no
 // multiply-add is fused -- then floor/clamp (Q4_0) or round half away from
@@ -33,47 +33,36 @@ __device__ __forceinline__ void store_u16(uint8_t* p, uint32_t v) {
 
 __global__ __launch_bounds__(kThreads) void k_quantize_q8_0(
     const float* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ canon,
-    int8_t* __restrict__ wq, float* __restrict__ wd, int32_t* __restrict__ wb,
-    uint32_t* __restrict__ zero, int64_t zero_words) {
-#pragma clang fp contract(off)
+    int8_t* __restrict__ wq, float* __restrict__ wd, int32_t* __restrict__ wb) {
+  // two lanes per block, 16 values (64 bytes) each
   const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (int64_t i = gtid; i < zero_words; i += (int64_t)gridDim.x * kThreads) zero[i] = 0u;
-
-  const int64_t blk = gtid >> 3;
-  const int g = threadIdx.x & 7;
+  const int64_t blk = gtid >> 1;
+  const int h = threadIdx.x & 1;
   const bool active = blk < nblocks;
-  float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-  if (active) load4(x + blk * 32 + g * 4, v0, v1, v2, v3);
-
-  float amax = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
-
-  const float d = amax / 127.0f;                    // correctly rounded fp32 division
-  const float id = d != 0.0f ? 1.0f / d : 0.0f;     // one correctly rounded reciprocal
-  const int q0 = (int)roundf(v0 * id);              // round half away from zero
-  const int q1 = (int)roundf(v1 * id);
-  const int q2 = (int)roundf(v2 * id);
-  const int q3 = (int)roundf(v3 * id);
-  const uint32_t packed = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
-                          ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
-  int sum = q0 + q1 + q2 + q3;
-  sum += __shfl_xor(sum, 1, 8);
-  sum += __shfl_xor(sum, 2, 8);
-  sum += __shfl_xor(sum, 4, 8);
+  float v[16];
+  const float4* p = reinterpret_cast<const float4*>(x + (active ? blk : 0) * 32 + 16 * h);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 f = p[i];
+    v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+  }
+  uint32_t packed[4], dbits;
+  int sum;
+  q8_0_pair(v, packed, dbits, sum);
   if (!active) return;
 
-  const uint32_t dbits = f32_to_f16_bits(d);
   if (canon) {
     uint8_t* b = canon + blk * 34;
-    if (g == 0) store_u16(b, dbits);
-    store_u16(b + 2 + 4 * g, packed & 0xffffu);
-    store_u16(b + 4 + 4 * g, packed >> 16);
+    if (h == 0) store_u16(b, dbits);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      store_u16(b + 2 + 16 * h + 4 * j, packed[j] & 0xffffu);
+      store_u16(b + 4 + 16 * h + 4 * j, packed[j] >> 16);
+    }
   }
   if (wq) {
-    reinterpret_cast<uint32_t*>(wq + blk * 32)[g] = packed;
-    if (g == 0) {
+    *reinterpret_cast<uint4*>(wq + blk * 32 + 16 * h) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    if (h == 0) {
       wd[blk] = f16_bits_to_f32(dbits);
       wb[blk] = -8 * sum;
     }
@@ -127,25 +116,24 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q4_0(const float* __restr
   store_u16(b + 4 + 4 * g, bytes >> 16);
 }
 
-int64_t grid_for(int64_t nblocks) { return (nblocks * 8 + kThreads - 1) / kThreads; }
+int64_t grid_for(int64_t nblocks, int lanes) { return (nblocks * lanes + kThreads - 1) / kThreads; }
 
 }  // namespace
 
 hipError_t launch_quantize_q8_0(const float* x, int64_t nrows, int64_t k, uint8_t* canon,
-                                int8_t* wq, float* wd, int32_t* wb, uint32_t* zero,
-                                int64_t zero_words, hipStream_t s) {
+                                int8_t* wq, float* wd, int32_t* wb, hipStream_t s) {
   const int64_t nblocks = nrows * (k / 32);
-  int64_t grid = grid_for(nblocks);
-  if (grid < 1) grid = 1;
+  const int64_t grid = grid_for(nblocks, 2);
+  if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL(k_quantize_q8_0, dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks,
-                     canon, wq, wd, wb, zero, zero_words);
+                     canon, wq, wd, wb);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_q4_0(const float* x, int64_t nrows, int64_t k, uint8_t* y,
                                 hipStream_t s) {
   const int64_t nblocks = nrows * (k / 32);
-  const int64_t grid = grid_for(nblocks);
+  const int64_t grid = grid_for(nblocks, 8);
   if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL(k_quantize_q4_0, dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, y);
   return hipGetLastError();

@@ -128,7 +128,9 @@ def test_debug_entry_argument_checks():
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 64, 100, 128, 512])
 def test_dispatch_threshold_and_workspace(m):
-    variant, split, rows, cols = qs.dispatch(Q4, m, 4096, 4096)
+    variant, split, rows, cols, launches = qs.dispatch(Q4, m, 4096, 4096)
+    # INIT is fused into the narrow kernel for M <= 2; a split adds the reduce kernel
+    assert launches == (0 if m <= 2 else 1) + 1 + (1 if split > 1 else 0)
     assert variant == (1 if m <= 8 else 2)
     assert split >= 1
     ws = qs.workspace_size(Q4, m, 4096, 4096)
@@ -144,7 +146,7 @@ def test_dispatch_threshold_and_workspace(m):
 
 def test_split_k_when_grid_is_small():
     # the tiny workload (N = 256) and a narrow N at the wide kernel must split K
-    v, split, _, _ = qs.dispatch(Q4, 32, 64, 14336)
+    v, split, _, _, _ = qs.dispatch(Q4, 32, 64, 14336)
     assert v == 2 and split > 1
     assert qs.workspace_size(Q4, 32, 64, 14336) >= split * 32 * 64 * 4
     # large grids do not split
@@ -155,3 +157,24 @@ def test_split_k_when_grid_is_small():
 def test_workspace_size_of_invalid_shapes_is_zero():
     assert qs.workspace_size(Q4, 1, 16, 48) == 0
     assert qs.workspace_size(7, 1, 16, 64) == 0
+
+
+def test_group_argument_checks():
+    n = (ctypes.c_int64 * 2)(64, 64)
+    src = (ctypes.c_void_p * 2)(FAKE, FAKE + 2**20)
+    dst = (ctypes.c_void_p * 2)(FAKE + 2**31, FAKE + 2**31 + 4 * 64)
+    g = qs.lib.mm_mul_mat_q4_0_f32_group
+    assert g(0, src, dst, n, FAKE + 2**30, 1, 64, None, 0, None) == ARG
+    assert g(9, src, dst, n, FAKE + 2**30, 1, 64, None, 0, None) == ARG
+    assert g(2, None, dst, n, FAKE + 2**30, 1, 64, None, 0, None) == NULL
+    assert g(2, src, dst, None, FAKE + 2**30, 1, 64, None, 0, None) == NULL
+    ws = qs.group_workspace_size([64, 64], 1, 64)
+    assert ws > 0
+    assert g(2, src, dst, n, FAKE + 2**30, 1, 64, FAKE + 2**32, ws - 1, None) == WS
+    # overlapping outputs
+    dst2 = (ctypes.c_void_p * 2)(FAKE + 2**31, FAKE + 2**31 + 4)
+    assert g(2, src, dst2, n, FAKE + 2**30, 1, 64, FAKE + 2**32, ws, None) == ALIAS
+    # an output overlapping another member's weights
+    dst3 = (ctypes.c_void_p * 2)(FAKE + 2**31, FAKE + 2**20 + 8)
+    assert g(2, src, dst3, n, FAKE + 2**30, 1, 64, FAKE + 2**32, ws, None) == ALIAS
+    assert qs.group_workspace_size([64, -1], 1, 64) == 0

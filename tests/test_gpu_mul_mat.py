@@ -306,3 +306,30 @@ def test_init_compute_stages_equal_the_fused_call():
             assert bool(torch.equal(y_stage, y_fused)), (n, k, m, rep)
             assert_close(to_host(y_stage), mul_mat.mul_mat_q4_0_f32_dequant(wq, to_host(x)),
                          TOL_Q4_0, "staged")
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 16, 40])
+def test_grouped_products(m):
+    """Several products sharing src1 in one grouped call equal the separate calls."""
+    import torch
+    qs = _qs()
+    k = 4096
+    rng = np.random.default_rng(70 + m)
+    ns = [4096, 1000, 0, 4096, 37]
+    ws, wqs = [], []
+    for n in ns:
+        w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+        wq = codec.quantize_q4_0(w)
+        wqs.append(wq)
+        ws.append(to_dev(wq) if n else torch.zeros((0, k // 32 * 18), dtype=torch.uint8, device="cuda"))
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    say("grouped", m, ns)
+    outs = qs.mul_mat_q4_0_f32_group(ws, to_dev(x))
+    for n, wq, w, out in zip(ns, wqs, ws, outs):
+        assert out.shape == (m, n)
+        if n == 0:
+            continue
+        single = qs.mul_mat_q4_0_f32(w, to_dev(x))
+        if n >= 4096:                       # same plan (no split): the same bits
+            assert bool(torch.equal(out, single))
+        assert_close(to_host(out), mul_mat.mul_mat_q4_0_f32_dequant(wq, x), TOL_Q4_0, f"group n={n}")
