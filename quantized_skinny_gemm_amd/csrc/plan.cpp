@@ -82,10 +82,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       // At most kNarrowMaxGrid workgroups along N, each walking an equal
       // number of row groups (the activation slice is staged once per
       // workgroup, so fewer, longer-lived workgroups re-read it less).
-      {
-        const int64_t per = ceil_div(p->tiles_n, kNarrowMaxGrid);
-        p->grid_n = ceil_div(p->tiles_n, per);
-      }
+      p->grid_n = p->tiles_n < kNarrowMaxGrid ? p->tiles_n : kNarrowMaxGrid;
       // Fuse the INIT stage (src1 -> Q8_0 in LDS, 40 bytes per block and row)
       // when the pass is small: every workgroup re-quantizes its src1 slice,
       // which costs about M / (0.56 * rows per wave) of the weight traffic in

@@ -47,10 +47,13 @@ struct ActView {
   int rows;             // valid rows (>= 1)
 };
 
-template <int MT, int R, bool kDump>
+// kMask: lanes with !valid hold a clamped (valid) unit whose contribution
+// is dropped; they still compute, so every loaded register is consumed on
+// every path.
+template <int MT, int R, bool kDump, bool kMask>
 __device__ __forceinline__ void block_mac(const uint32_t (&q)[R][4], const float (&dw)[R], int b,
-                                          const ActView& av, float (&acc)[R][MT], int nw, int m0,
-                                          int nb, const Q4Args& a) {
+                                          bool valid, const ActView& av, float (&acc)[R][MT],
+                                          int nw, int m0, int nb, const Q4Args& a) {
   uint32_t lo[R][4], hi[R][4];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -79,10 +82,12 @@ __device__ __forceinline__ void block_mac(const uint32_t (&q)[R][4], const float
       s = __builtin_amdgcn_sdot4((int)hi[r][1], a1.y, s, false);
       s = __builtin_amdgcn_sdot4((int)hi[r][2], a1.z, s, false);
       s = __builtin_amdgcn_sdot4((int)hi[r][3], a1.w, s, false);
-      acc[r][m] = fmaf((float)s, dw[r] * da, acc[r][m]);
+      const float sc = dw[r] * da;
+      // s * 0 is a zero, so a dropped lane leaves its sum unchanged
+      acc[r][m] = fmaf((float)s, kMask ? (valid ? sc : 0.0f) : sc, acc[r][m]);
       if (kDump) {
         const int n = nw + r;
-        if (m0 + m < a.M && n >= a.n0 && n < a.n1)
+        if ((!kMask || valid) && m0 + m < a.M && n >= a.n0 && n < a.n1)
           a.dots[((int64_t)(m0 + m) * (a.n1 - a.n0) + (n - a.n0)) * nb + b] = s;
       }
     }
@@ -96,22 +101,26 @@ __device__ __forceinline__ void load_unit(uint32_t (&wv)[R][9], const uint8_t* c
                                           int64_t u) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    // weights live in global memory: say so, so the loads are global_load
+    // (a flat load would also count against the LDS wait counter)
     if (kPairs) {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(rowp[r] + 36 * u);
+      const __attribute__((address_space(1))) uint32_t* p =
+          (const __attribute__((address_space(1))) uint32_t*)(rowp[r] + 36 * u);
 #pragma unroll
       for (int i = 0; i < 9; ++i) wv[r][i] = p[i];
     } else {
-      const uint16_t* p = reinterpret_cast<const uint16_t*>(rowp[r] + 18 * u);
+      const __attribute__((address_space(1))) uint16_t* p =
+          (const __attribute__((address_space(1))) uint16_t*)(rowp[r] + 18 * u);
 #pragma unroll
       for (int i = 0; i < 9; ++i) wv[r][i] = p[i];
     }
   }
 }
 
-template <int MT, int R, bool kPairs, bool kDump>
-__device__ __forceinline__ void unit_mac(const uint32_t (&wv)[R][9], int64_t u, const ActView& av,
-                                         float (&acc)[R][MT], int nw, int m0, int nb,
-                                         const Q4Args& a) {
+template <int MT, int R, bool kPairs, bool kDump, bool kMask>
+__device__ __forceinline__ void unit_mac(const uint32_t (&wv)[R][9], int64_t u, bool valid,
+                                         const ActView& av, float (&acc)[R][MT], int nw, int m0,
+                                         int nb, const Q4Args& a) {
   if (kPairs) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -129,7 +138,7 @@ __device__ __forceinline__ void unit_mac(const uint32_t (&wv)[R][9], int64_t u, 
           for (int j = 0; j < 4; ++j) q[r][j] = wv[r][5 + j];
         }
       }
-      block_mac<MT, R, kDump>(q, dw, (int)(2 * u + half), av, acc, nw, m0, nb, a);
+      block_mac<MT, R, kDump, kMask>(q, dw, (int)(2 * u + half), valid, av, acc, nw, m0, nb, a);
     }
   } else {
     uint32_t q[R][4];
@@ -140,7 +149,7 @@ __device__ __forceinline__ void unit_mac(const uint32_t (&wv)[R][9], int64_t u, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) q[r][j] = wv[r][1 + 2 * j] | (wv[r][2 + 2 * j] << 16);
     }
-    block_mac<MT, R, kDump>(q, dw, (int)u, av, acc, nw, m0, nb, a);
+    block_mac<MT, R, kDump, kMask>(q, dw, (int)u, valid, av, acc, nw, m0, nb, a);
   }
 }
 
@@ -189,27 +198,28 @@ template <int NT, int kBatch, int MT>
 __device__ __forceinline__ void quant_store(const Slice& sl, int it0, int rounds,
                                             float (&v)[kBatch][16], const bool (&ok)[kBatch],
                                             int8_t* sq, float* sd, int32_t* sb) {
+  // Every round of the batch is computed, also past the last one (on zeros,
+  // nothing stored): a loaded register left unread on some path would make
+  // the compiler wait for the loads in flight wherever it is next written.
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) {
-    if (it0 + j < rounds) {                          // uniform over the workgroup
-      const int i = (it0 + j) * NT + (int)threadIdx.x;
-      const int blk = i >> 1, h = i & 1;
-      int m, bl;
-      split_blk<MT>(blk, sl.kbmax, m, bl);
-      if (!ok[j]) {
+    const int i = (it0 + j) * NT + (int)threadIdx.x;
+    const int blk = i >> 1, h = i & 1;
+    int m, bl;
+    split_blk<MT>(blk, sl.kbmax, m, bl);
+    if (!ok[j]) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v[j][e] = 0.0f;
-      }
-      uint32_t packed[4], dbits;
-      int sum;
-      q8_0_pair(v[j], packed, dbits, sum);
-      if (ok[j]) {
-        *reinterpret_cast<uint4*>(sq + (int64_t)m * sl.kbmax * 32 + bl * 32 + 16 * h) =
-            make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        if (h == 0) {
-          sd[m * sl.kbmax + bl] = f16_bits_to_f32(dbits);
-          sb[m * sl.kbmax + bl] = -8 * sum;
-        }
+      for (int e = 0; e < 16; ++e) v[j][e] = 0.0f;
+    }
+    uint32_t packed[4], dbits;
+    int sum;
+    q8_0_pair(v[j], packed, dbits, sum);
+    if (ok[j]) {
+      *reinterpret_cast<uint4*>(sq + (int64_t)m * sl.kbmax * 32 + bl * 32 + 16 * h) =
+          make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      if (h == 0) {
+        sd[m * sl.kbmax + bl] = f16_bits_to_f32(dbits);
+        sb[m * sl.kbmax + bl] = -8 * sum;
       }
     }
   }
@@ -299,7 +309,7 @@ __device__ __forceinline__ void rows_of(const Q4Mats& mats, int g, int wave, int
 // than once per row group.  Each wave runs a flat sequence of (group, K unit)
 // steps and loads the next step's weights before computing the current one.
 template <int MT, int R, int WAVES, bool kPairs, bool kDump, int kAct, int kBatch>
-__global__ __launch_bounds__(64 * WAVES, MT > 2 ? 1 : kAct == kActQuant ? (kBatch <= 1 ? 6 : 5) : (kBatch <= 4 ? 6 : 1))
+__global__ __launch_bounds__(64 * WAVES, MT > 2 ? 1 : kAct == kActQuant ? (kBatch <= 1 ? 4 : 4) : (kBatch <= 4 ? 6 : 1))
 void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kchunk, int split) {
   constexpr int NT = 64 * WAVES;
   constexpr int RPG = WAVES * R;                     // rows per group
@@ -399,9 +409,13 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
+  // One step of the wave's (group, K unit) sequence: issue the loads of the
+  // next step into `nxt`, then compute the current step from `cur`.  The
+  // loop below alternates two register buffers, so a step's loads stay in
+  // flight while the previous step is computed (no register copy waits for
+  // them).  Returns false after the wave's last step.
   int i = 0;                                         // K step within the group
-  for (;;) {
-    // the next step: (gn, in)
+  auto step = [&](const uint32_t (&cur)[R][9], uint32_t (&nxt)[R][9]) -> bool {
     int in = i + 1, gn = g;
     if (in == SU) { in = 0; gn = g + (int)gridDim.x; }
     const bool more = gn < ngroups;
@@ -412,19 +426,23 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
 #pragma unroll
       for (int r = 0; r < R; ++r) rpn[r] = rp[r];
     }
-    uint32_t cur[R][9];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int j = 0; j < 9; ++j) cur[r][j] = wv[r][j];
-    // prefetch the next step (past the last one it reloads a valid unit)
+    // past the wave's last step this reloads a valid unit
     int64_t un = u0 + lane + 64 * (int64_t)in;
     un = un < u1 ? un : u0;
-    load_unit<R, kPairs>(wv, rpn, un);
+    load_unit<R, kPairs>(nxt, rpn, un);
+    // keep the scheduler from hoisting the current step's first uses (which
+    // wait for its loads) above the next step's loads
+    __builtin_amdgcn_sched_barrier(0);
 
+    // the current step's unit, clamped as its loads were
     const int64_t u = u0 + lane + 64 * (int64_t)i;
+    const bool valid = u < u1;
+    const int64_t uc = valid ? u : u0;
     const int nw = g * RPG + wave * R;
-    if (u < u1) unit_mac<MT, R, kPairs, kDump>(cur, u, av, acc, nw, m0, nb, a);
+    if (u0 + 64 * (int64_t)(i + 1) <= u1)              // every lane valid (uniform)
+      unit_mac<MT, R, kPairs, kDump, false>(cur, uc, true, av, acc, nw, m0, nb, a);
+    else
+      unit_mac<MT, R, kPairs, kDump, true>(cur, uc, valid, av, acc, nw, m0, nb, a);
 
     if (i == SU - 1) {
       // Reduce each accumulator over the wave; lane r*MT+m stores (m, row nw+r).
@@ -439,21 +457,155 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
         }
       const int r = lane / MT, m = lane % MT;
       const int n = nw + r;
-      if (lane < R * MT && m0 + m < M && n < N) {
-        if (split == 1) {
-          const int mi = mat_of(mats, n);
-          const int ni = mats.row0[mi + 1] - mats.row0[mi];
-          mats.dst[mi][(int64_t)(m0 + m) * ni + (n - mats.row0[mi])] = mine;
-        } else {
-          a.part[((int64_t)z * M + m0 + m) * N + n] = mine;
+      if (split == 1) {
+        // Output row of each of the R rows: the matrix lookups use the
+        // wave-uniform row index (scalar loads of the kernel arguments), and
+        // each lane then picks its own row's pointer.  A lane-indexed lookup
+        // would read the argument block with vector loads, whose wait would
+        // also wait for the weight loads already in flight.
+        float* out = nullptr;
+        int ldo = 0;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          const int nr = nw + rr < N ? nw + rr : N - 1;
+          const int mi = mat_of(mats, nr);
+          float* pr = mats.dst[mi] + (nr - mats.row0[mi]);
+          const int nir = mats.row0[mi + 1] - mats.row0[mi];
+          if (r == rr) { out = pr; ldo = nir; }
         }
+        if (lane < R * MT && m0 + m < M && n < N) out[(int64_t)(m0 + m) * ldo] = mine;
+      } else if (lane < R * MT && m0 + m < M && n < N) {
+        a.part[((int64_t)z * M + m0 + m) * N + n] = mine;
       }
     }
-    if (!more && in == 0) break;
+    if (!more && in == 0) return false;
     g = gn;
     i = in;
 #pragma unroll
     for (int r = 0; r < R; ++r) rp[r] = rpn[r];
+    return true;
+  };
+  uint32_t wv2[R][9];
+  for (;;) {
+    if (!step(wv, wv2)) break;
+    if (!step(wv2, wv)) break;
+  }
+}
+
+// Fused small-M kernel (MT <= 2 rows of src1, K/32 even, 4-byte aligned
+// weights, no K split): the common decode case, kept as lean as possible.
+// Each workgroup quantizes src1 into LDS once, then walks row groups
+// g = blockIdx.x, blockIdx.x + gridDim.x, ...; wave w of the group owns rows
+// 16g + 2w and 16g + 2w + 1, and lane l the K units (block pairs) l, l + 64,
+// ...  The steps (group, K unit range) of a wave form one flat sequence
+// whose next step's weights are loaded before the current one is computed.
+template <int MT, int NR>
+__global__ __launch_bounds__(512)
+void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
+  constexpr int R = 2, WAVES = 8, NT = 64 * WAVES, RPG = WAVES * R;
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nb = K / 32;
+  const int units = nb / 2;
+  const int64_t rb = (int64_t)nb * 18;
+  const int SU = (units + 63) / 64;                  // steps per row group
+  const int m0 = blockIdx.y * MT;
+  const int rows = M - m0 < MT ? M - m0 : MT;
+  const int ngroups = (N + RPG - 1) / RPG;
+  const int G = (int)gridDim.x;
+  const int mygroups = (int)blockIdx.x < ngroups ? (ngroups - 1 - (int)blockIdx.x) / G + 1 : 0;
+  const int S = mygroups * SU;
+  if (S == 0) return;                                // uniform over the workgroup
+  int8_t* sq = smem;
+  float* sd = reinterpret_cast<float*>(smem + (int64_t)MT * nb * 32);
+  int32_t* sb = reinterpret_cast<int32_t*>(sd + MT * nb);
+
+  // weight row pointer of the wave's row r at step s (rows past N clamped)
+  auto rowptr = [&](int g, int r) -> const uint8_t* {
+    int n = g * RPG + wave * R + r;
+    n = n < N ? n : N - 1;
+    const int i = mat_of(mats, n);
+    return mats.w[i] + (int64_t)(n - mats.row0[i]) * rb;
+  };
+
+  // activation loads first (vmcnt retires in order), then the first weights
+  Slice sl;
+  sl.kbmax = nb; sl.nbs = nb; sl.rows = rows; sl.m0 = m0; sl.b0 = 0; sl.K = K; sl.nb = nb;
+  sl.total = MT * nb * 2;
+  const int rounds = (sl.total + NT - 1) / NT;
+  float v[NR][16];
+  bool ok[NR];
+  quant_load<NT, NR, MT>(sl, x, 0, rounds, v, ok);
+  int g = blockIdx.x, i = 0;                         // current step: group g, K step i
+  uint32_t wv[R][9];
+  {
+    const uint8_t* rp[R] = {rowptr(g, 0), rowptr(g, 1)};
+    const int u = lane < units ? lane : 0;
+    load_unit<R, true>(wv, rp, u);
+  }
+  quant_store<NT, NR, MT>(sl, 0, rounds, v, ok, sq, sd, sb);
+  for (int it0 = NR; it0 < rounds; it0 += NR) {
+    quant_load<NT, NR, MT>(sl, x, it0, rounds, v, ok);
+    quant_store<NT, NR, MT>(sl, it0, rounds, v, ok, sq, sd, sb);
+  }
+  lds_barrier();
+
+  ActView av;
+  av.q = sq; av.d = sd; av.bias = sb;
+  av.qpitch = (int64_t)nb * 32; av.dpitch = nb; av.boff = 0; av.rows = rows;
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+  for (int s = 0; s < S; ++s) {
+    // next step (the last step reloads itself: valid, and never computed)
+    int in = i + 1, gn = g;
+    if (in == SU) { in = 0; gn = g + G; }
+    if (s + 1 == S) { in = i; gn = g; }
+    uint32_t cur[R][9];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < 9; ++j) cur[r][j] = wv[r][j];
+    {
+      const uint8_t* rp[R] = {rowptr(gn, 0), rowptr(gn, 1)};
+      int un = lane + 64 * in;
+      un = un < units ? un : 0;
+      load_unit<R, true>(wv, rp, un);
+    }
+    const int u = lane + 64 * i;
+    const int nw = g * RPG + wave * R;
+    if (u < units) unit_mac<MT, R, true, false, false>(cur, u, true, av, acc, nw, m0, nb, Q4Args{});
+    if (i == SU - 1) {
+      float mine = 0.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const float t = wave_sum_dpp(acc[r][m]);
+          if (lane == r * MT + m) mine = t;
+          acc[r][m] = 0.0f;
+        }
+      // output pointers of the two rows (wave-uniform lookups)
+      float* out[R];
+      int ldo[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int nr = nw + r < N ? nw + r : N - 1;
+        const int mi = mat_of(mats, nr);
+        out[r] = mats.dst[mi] + (nr - mats.row0[mi]);
+        ldo[r] = mats.row0[mi + 1] - mats.row0[mi];
+      }
+      const int r = lane / MT, m = lane % MT;
+      float* o = r == 0 ? out[0] : out[1];
+      const int ld = r == 0 ? ldo[0] : ldo[1];
+      if (lane < R * MT && m < rows && nw + r < N) o[(int64_t)(m0 + m) * ld] = mine;
+    }
+    g = gn;
+    i = in;
   }
 }
 
@@ -518,6 +670,19 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
   // (in units) doubles and the split count is unchanged.
   Plan q = p;
   if (!pairs && nb % 2 == 0) q.kchunk = p.kchunk * 2;
+  if (x && pairs && p.split == 1 && a.dots == nullptr && p.mt <= 2 && p.rpw == 2 && p.waves == 8) {
+    const dim3 grid((unsigned)p.grid_n, (unsigned)p.tiles_m, 1u);
+    const size_t lds = (size_t)p.mt * nb * 40;
+    const int rounds = (int)(((int64_t)p.mt * nb * 2 + 511) / 512);
+    if (p.mt == 1) {
+      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<1, 1>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+      else hipLaunchKernelGGL((k_q4_fused<1, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+    } else {
+      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<2, 1>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+      else hipLaunchKernelGGL((k_q4_fused<2, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+    }
+    return hipGetLastError();
+  }
   // rows per wave and waves per workgroup must match make_plan()
   if (p.mt == 1 && p.rpw == 2 && p.waves == 8) return launch_mt<1, 2, 8>(q, a, mats, x, pairs, s);
   if (p.mt == 2 && p.rpw == 2 && p.waves == 8) return launch_mt<2, 2, 8>(q, a, mats, x, pairs, s);
