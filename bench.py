@@ -19,6 +19,12 @@ traffic / step time (GB/s); `roofline` reports the product kernel alone
 CPU oracle on a bounded sample of the same work.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--only-step] [--copy-calibration BYTES]
+
+--only-step skips the one-call-per-matrix comparison (profiling runs use it,
+so that every product launch belongs to the grouped step's mix);
+--copy-calibration runs a plain device copy of BYTES ten times and exits
+(the reference reading for the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -37,7 +43,7 @@ METRIC = "Q4_0 mul_mat HBM GB/s (M≤16) and TOPS (M≥32), % of MI355X roofline
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 Q4_BYTES_PER_VALUE = 18 / 32   # Q4_0 block: 18 bytes per 32 values
 Q8_BYTES_PER_VALUE = 34 / 32   # Q8_0 block: 34 bytes per 32 values
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q4_narrow_decode.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q4_fused_llama7b_decode.json")
 NARROW_SRC = os.path.join(ROOT, "quantized_skinny_gemm_amd", "csrc", "q4_narrow.hip")
 
 
@@ -211,9 +217,10 @@ def measure_kernels(st, layers, reps: int, s):
     return res
 
 
-def traffic_from_profile(per_launch_bytes):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None when
-    absent or taken on a different version of the kernel source."""
+def traffic_from_profile():
+    """HBM bytes per launch of the product kernel (the step's launch mix) from the
+    committed rocprofv3 PMC summary, or None when absent or taken on a different
+    version of the kernel source."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
@@ -224,6 +231,20 @@ def traffic_from_profile(per_launch_bytes):
         return float(t["bytes_per_launch"])
     except (OSError, ValueError, KeyError):
         return None
+
+
+def copy_calibration(nbytes: int):
+    """A plain device-to-device copy of nbytes, ten times: under rocprofv3 --pmc
+    its FETCH_SIZE / WRITE_SIZE give the counters' reading for known traffic."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": a.numel() * 4, "copies": 10}), flush=True)
 
 
 # ------------------------------------------------------------ cpu leg
@@ -266,6 +287,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--only-step", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -273,6 +296,10 @@ def main():
         print(f"bench.py measures one GPU: this library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
 
     st = setup_gpu(args.layers)
     torch = st["torch"]
@@ -303,25 +330,30 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     # the same products as one call per matrix (7 launches per layer)
-    single_ms = time_graph(torch, s, [c for layer in single for c in layer], max(1, args.steps // 4))
+    single_ms = None
+    if not args.only_step:
+        single_ms = time_graph(torch, s, [c for layer in single for c in layer],
+                               max(1, args.steps // 4))
 
     step_bytes = args.layers * sum(q4_step_bytes(1, *shapes[sl]) for sl in LAYER_SLOTS)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"step {ms_per_step:.4f} ms grouped ({len(step_calls)} launches), {single_ms:.4f} ms "
-        f"one call per matrix; {value:.1f} GB/s")
+    log(f"step {ms_per_step:.4f} ms grouped ({len(step_calls)} launches); {value:.1f} GB/s")
+    if single_ms is not None:
+        log(f"step {single_ms:.4f} ms as one call per matrix ({len(step_calls) * 7 // 4} launches)")
 
     kern = measure_kernels(st, grouped, args.kernel_reps, s)
-    kern_single = measure_kernels(st, single, args.kernel_reps, s)
-    for r in kern_single:
-        log(f"one call per matrix, kernel {r['kind']}: {r['avg_us']:.3f} us/launch, "
-            f"{r['bytes'] / (r['avg_us'] * 1e-6) / 1e9:.1f} GB/s")
+    if not args.only_step:
+        for r in measure_kernels(st, single, args.kernel_reps, s):
+            log(f"one call per matrix, kernel {r['kind']}: {r['avg_us']:.3f} us/launch, "
+                f"{r['bytes'] / (r['avg_us'] * 1e-6) / 1e9:.1f} GB/s")
     tot_bytes = sum(r["bytes"] * r["launches_per_step"] for r in kern)
     tot_us = sum(r["avg_us"] * r["launches_per_step"] for r in kern)
+    launches = sum(r["launches_per_step"] for r in kern)
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
     for r in kern:
         log(f"kernel {r['kind']}: {r['avg_us']:.3f} us/launch, "
             f"{r['bytes'] / (r['avg_us'] * 1e-6) / 1e9:.1f} GB/s")
-    traffic = traffic_from_profile(tot_bytes / sum(r["launches_per_step"] for r in kern))
+    traffic = traffic_from_profile()
 
     out = {
         "metric": METRIC,
@@ -347,11 +379,14 @@ def main():
                       "gate,up grouped, down; one kernel each (INIT fused)",
         },
         "tokens_per_s": round(1e3 / ms_per_step, 2),
-        "one_call_per_matrix_ms_per_step": round(single_ms, 5),
-        "one_call_per_matrix_GBs": round(step_bytes / (single_ms * 1e-3) / 1e9, 2),
+        "one_call_per_matrix_ms_per_step": None if single_ms is None else round(single_ms, 5),
+        "one_call_per_matrix_GBs": None if single_ms is None else
+            round(step_bytes / (single_ms * 1e-3) / 1e9, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_q4_narrow (INIT fused), M=1, all launches of the step",
+            "kernel": "k_q4_fused (INIT fused), M=1, all launches of the step",
+            "avg_launch_us": round(tot_us / launches, 4),
+            "algorithmic_bytes_per_launch": round(tot_bytes / launches, 1),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
