@@ -19,7 +19,7 @@ traffic / step time (GB/s); `roofline` reports the product kernel alone
 CPU oracle on a bounded sample of the same work.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only-step] [--copy-calibration BYTES]
+                    [--only-step] [--copy-calibration BYTES] [--sweep [JSON]]
 
 --only-step skips the one-call-per-matrix comparison (profiling runs use it,
 so that every product launch belongs to the grouped step's mix);
@@ -247,6 +247,97 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_bytes": a.numel() * 4, "copies": 10}), flush=True)
 
 
+# ------------------------------------------------------------ config sweep
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (T op/s)
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA, published
+MALL_DEFEAT_BYTES = 600e6      # distinct weight copies per timing loop (last-level cache)
+
+
+def sweep_rows():
+    """(workload, type, M, N, K) of every product in the five workloads."""
+    import workloads
+    rows = []
+    for w, spec in workloads.WORKLOADS.items():
+        for t in spec["types"]:
+            for n, k in spec["shapes"]:
+                for m in spec["ms"]:
+                    rows.append((w, t, m, n, k))
+    return rows
+
+
+def algo_bytes(t: str, m: int, n: int, k: int, fused: bool) -> float:
+    if t == "q4_0":
+        return q4_fused_bytes(m, n, k) if fused else q4_step_bytes(m, n, k)
+    wb = 2 if t == "f16" else 4
+    return wb * n * k + 4.0 * m * k + 4.0 * m * n
+
+
+def run_sweep(reps: int, out_path: str | None):
+    """Times every product of the five workloads (one call per product, HIP
+    graph of calls over distinct weight copies, HIP events on the launch
+    stream) and reports GB/s, TOPS and the fraction of the bounding roofline."""
+    import ctypes
+    import torch
+    import quantized_skinny_gemm_amd as qs
+
+    dev = torch.device("cuda:0")
+    s = torch.cuda.Stream()
+    gen = torch.Generator(device=dev)
+    results = []
+    for (w, t, m, n, k) in sweep_rows():
+        mm_type = {"q4_0": qs.MM_TYPE_Q4_0, "f16": qs.MM_TYPE_F16, "f32": qs.MM_TYPE_F32}[t]
+        gen.manual_seed(1000 * w + n + k)
+        wf = torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02
+        if t == "q4_0":
+            base = qs.quantize_q4_0(wf)
+        elif t == "f16":
+            base = wf.to(torch.float16)
+        else:
+            base = wf
+        del wf
+        nbytes = base.numel() * base.element_size()
+        copies = max(1, min(64, int(-(-MALL_DEFEAT_BYTES // nbytes))))
+        if nbytes * copies > 6e9:
+            copies = max(1, int(6e9 // nbytes))
+        ws_list = [base] + [base.clone() for _ in range(copies - 1)]
+        x = torch.randn((m, k), generator=gen, device=dev, dtype=torch.float32)
+        dst = torch.empty((m, n), dtype=torch.float32, device=dev)
+        wsb = qs.workspace_size(mm_type, m, n, k)
+        wsp = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        fn = {"q4_0": qs.lib.mm_mul_mat_q4_0_f32, "f16": qs.lib.mm_mul_mat_f16_f32,
+              "f32": qs.lib.mm_mul_mat_f32}[t]
+        calls = [(t, fn, (wc.data_ptr(), x.data_ptr(), dst.data_ptr(), m, n, k, wsp.data_ptr(),
+                          wsb, s.cuda_stream), 0.0) for wc in ws_list]
+        ms = time_graph(torch, s, calls, reps)
+        us = ms * 1e3 / len(calls)
+        d = (ctypes.c_int * 5)()
+        qs.lib.mm_dispatch(mm_type, m, n, k, d)
+        variant, split, launches = d[0], d[1], d[4]
+        fused = t == "q4_0" and variant == 1 and launches == 1
+        nb = algo_bytes(t, m, n, k, fused)
+        gbs = nb / (us * 1e-6) / 1e9
+        tops = product_ops(m, n, k) / (us * 1e-6) / 1e12
+        if t == "q4_0" and m >= 32:
+            bound, frac = "int8 MFMA", tops / INT8_PEAK_TOPS
+        elif t == "f16" and m >= 32:
+            bound, frac = "fp16 MFMA", tops / FP16_PEAK_TFLOPS
+        else:
+            bound, frac = "hbm", gbs / HBM_PEAK_GBS
+        r = dict(workload=w, type=t, M=m, N=n, K=k, us=round(us, 3), GBs=round(gbs, 1),
+                 TOPS=round(tops, 2), bound=bound, frac=round(frac, 4),
+                 kernel="narrow" if variant == 1 else "wide", split=split, launches=launches,
+                 copies=copies)
+        results.append(r)
+        log(f"w{w} {t:5s} M={m:4d} {n:6d}x{k:<6d} {us:9.3f} us {gbs:8.1f} GB/s {tops:8.2f} TOPS "
+            f"{bound:9s} {100 * frac:5.1f}%  ({r['kernel']}, split {split}, {launches} launch)")
+        del ws_list, base, x, dst, wsp
+        torch.cuda.empty_cache()
+    if out_path:
+        with open(out_path, "w") as fh:
+            json.dump(results, fh, indent=1)
+    return results
+
+
 # ------------------------------------------------------------ cpu leg
 def cpu_baseline(budget_s: float = 10.0):
     """The CPU oracle (as it stands) on one layer's 7 products, repeated for
@@ -289,6 +380,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--only-step", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--sweep", metavar="JSON", nargs="?", const="",
+                    help="time every product of the five workloads instead (table on "
+                         "stderr, optional JSON file)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -299,6 +393,9 @@ def main():
 
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
+        return
+    if args.sweep is not None:
+        run_sweep(max(2, args.kernel_reps // 4), args.sweep or None)
         return
 
     st = setup_gpu(args.layers)
