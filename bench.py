@@ -325,7 +325,8 @@ def run_sweep(reps: int, out_path: str | None):
             bound, frac = "hbm", gbs / HBM_PEAK_GBS
         r = dict(workload=w, type=t, M=m, N=n, K=k, us=round(us, 3), GBs=round(gbs, 1),
                  TOPS=round(tops, 2), bound=bound, frac=round(frac, 4),
-                 kernel="narrow" if variant == 1 else "wide", split=split, launches=launches,
+                 kernel={1: "narrow", 2: "wide", 3: "skinny mfma"}.get(variant, str(variant)),
+                 split=split, launches=launches,
                  copies=copies)
         results.append(r)
         log(f"w{w} {t:5s} M={m:4d} {n:6d}x{k:<6d} {us:9.3f} us {gbs:8.1f} GB/s {tops:8.2f} TOPS "

@@ -70,9 +70,9 @@ Q4Mats single_mat(const void* src0, float* dst, int64_t N) {
 
 // The product kernel (x != NULL: INIT fused), then the split-K reduction.
 int q4_product(const Plan& p, const Q4Args& a, const float* x, hipStream_t s) {
-  hipError_t e = p.kind == KK_Q4_NARROW
-                     ? launch_q4_narrow(p, a, single_mat(a.w, a.dst, a.N), x, s)
-                     : launch_q4_wide(p, a, s);
+  hipError_t e = p.kind == KK_Q4_NARROW ? launch_q4_narrow(p, a, single_mat(a.w, a.dst, a.N), x, s)
+                 : p.kind == KK_Q4_MMA  ? launch_q4_mma(p, a, s)
+                                        : launch_q4_wide(p, a, s);
   if (e == hipSuccess && p.split > 1)
     e = launch_splitk_reduce(a.part, a.dst, (int64_t)a.M * a.N, p.split, s);
   return hip_status(e);
@@ -102,6 +102,7 @@ int mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* 
   switch (p.kind) {
     case KK_ZERO: return hip_status(launch_zero(dst, M * N, s));
     case KK_Q4_NARROW:
+    case KK_Q4_MMA:
     case KK_Q4_WIDE: return run_q4_0(p, src0, src1, dst, dots, M, N, K, n0, n1, ws, s);
     case KK_F_NARROW:
       return hip_status(launch_f_narrow(p, type, src0, src1, dst, (int)M, (int)N, (int)K, s));
@@ -203,7 +204,7 @@ int group_plan(int count, const int64_t* Ns, int64_t M, int64_t K, Plan* whole, 
   int st = make_plan(MM_TYPE_Q4_0, M, tot, K, 0, whole, /*allow_split=*/false);
   if (st != MM_OK) return st;
   size_t need = whole->ws_bytes;
-  if (whole->kind == KK_Q4_WIDE) {
+  if (whole->kind == KK_Q4_WIDE || whole->kind == KK_Q4_MMA) {
     for (int i = 0; i < count; ++i) {
       Plan pi;
       st = make_plan(MM_TYPE_Q4_0, M, Ns[i], K, 0, &pi);
@@ -282,8 +283,8 @@ int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const*
     }
     return hip_status(launch_q4_narrow(whole, a, mats, whole.fuse ? src1 : nullptr, s));
   }
-  // wide: one INIT, then one product per matrix (same wdata layout at the
-  // front of every per-matrix plan)
+  // wide and skinny MFMA: one INIT, then one product per matrix (same wdata
+  // layout at the front of every per-matrix plan)
   st = q4_init(whole, src1, M, K, ws, s);
   if (st != MM_OK) return st;
   for (int i = 0; i < count; ++i) {
@@ -318,7 +319,7 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
     out[0] = p.variant;
     out[1] = p.split;
     out[2] = p.variant == 2 ? p.bm : p.mt;
-    out[3] = p.variant == 2 ? p.bn : p.rpw;
+    out[3] = p.variant == 2 ? p.bn : p.variant == 3 ? p.waves : p.rpw;
     const int init = (p.type == MM_TYPE_Q4_0 && !(p.kind == KK_Q4_NARROW && p.fuse)) ? 1 : 0;
     out[4] = init + 1 + (p.split > 1 ? 1 : 0);
   }
@@ -328,7 +329,7 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
 int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* dots,
                      int64_t M, int64_t N, int64_t K, int64_t n0, int64_t n1, int variant,
                      void* ws, size_t ws_bytes, void* stream) {
-  if (variant < 0 || variant > 2) return MM_ERR_ARG;
+  if (variant < 0 || variant > 3) return MM_ERR_ARG;
   if (n0 < 0 || n1 < n0 || n1 > N) return MM_ERR_SHAPE;
   if (type != MM_TYPE_Q4_0 || n1 == n0) dots = nullptr;
   else if (!dots) return MM_ERR_NULL;

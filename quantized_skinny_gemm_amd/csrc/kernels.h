@@ -48,6 +48,9 @@ struct Q4Mats {
 hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, const float* x,
                             hipStream_t s);
 hipError_t launch_q4_wide(const Plan& p, const Q4Args& a, hipStream_t s);
+// Skinny MFMA kernel: reads the wdata in a (INIT must have run), writes a.dst
+// or, when p.split > 1, the partials in a.part.
+hipError_t launch_q4_mma(const Plan& p, const Q4Args& a, hipStream_t s);
 
 hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* x, float* dst,
                            int M, int N, int K, hipStream_t s);

@@ -44,7 +44,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   *p = Plan();
   p->type = type;
   if (type != MM_TYPE_F32 && type != MM_TYPE_F16 && type != MM_TYPE_Q4_0) return MM_ERR_ARG;
-  if (variant < 0 || variant > 2) return MM_ERR_ARG;
+  if (variant < 0 || variant > 3 || (variant == 3 && type != MM_TYPE_Q4_0)) return MM_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MM_ERR_SHAPE;
   if (type == MM_TYPE_Q4_0 && (K % kQK)) return MM_ERR_SHAPE;
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
@@ -52,12 +52,36 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
 
   if (type == MM_TYPE_Q4_0) {
     const int64_t nb = K / kQK;
-    const bool narrow = variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM);
+    // M <= 2: the fused narrow kernel; up to kMmaMaxM: the skinny MFMA
+    // kernel; beyond: the tiled wide kernel.
+    const bool mma = variant == 3 || (variant == 0 && M > kFuseMaxM && M <= kMmaMaxM);
+    const bool narrow = !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
     size_t off = 0;
     p->off_aq = off; off = align_up(off + (size_t)M * (size_t)K, 256);
     p->off_ad = off; off = align_up(off + (size_t)M * (size_t)nb * 4, 256);
     p->off_ab = off; off = align_up(off + (size_t)M * (size_t)nb * 4, 256);
-    if (narrow) {
+    if (mma) {
+      p->kind = KK_Q4_MMA;
+      p->variant = 3;
+      p->mt = M <= 8 ? 8 : M <= 16 ? 16 : 32;
+      p->waves = kMmaWaves;
+      p->tiles_m = ceil_div(M, p->mt);
+      p->tiles_n = ceil_div(N, 32);
+      // Split K across workgroups while the 32-row tiles do not give every
+      // CU a workgroup; at least one 32-block chunk per split.
+      const int64_t wgs = p->tiles_m * p->tiles_n;
+      int64_t split = 1;
+      if (allow_split && wgs < kCUs) {
+        split = ceil_div(kCUs, wgs);
+        const int64_t max_split = nb / 32 > 1 ? nb / 32 : 1;
+        if (split > max_split) split = max_split;
+        if (split > 16) split = 16;
+      }
+      int64_t kc = ceil_div(nb, split);
+      kc = ceil_div(kc, 8) * 8;                        // chunk starts stay 16-byte aligned
+      p->kchunk = kc;
+      p->split = (int)ceil_div(nb, kc);
+    } else if (narrow) {
       p->kind = KK_Q4_NARROW;
       p->variant = 1;
       p->mt = narrow_mt(M, kNarrowQ4MaxM);

@@ -27,6 +27,8 @@ constexpr int kNarrowFMaxM = 16;   // largest M the f16/f32 narrow kernel takes 
 constexpr int kFuseMaxM = 2;       // narrow Q4_0 passes of at most this many rows fuse INIT
 constexpr int kNarrowMaxLds = 65536; // LDS bytes the narrow kernel may stage activations in
 constexpr int kNarrowMaxGrid = 512;  // narrow workgroups along N (2 per CU)
+constexpr int kMmaMaxM = 32;       // largest M the skinny MFMA kernel takes by default
+constexpr int kMmaWaves = 8;       // waves per skinny MFMA workgroup (they split K)
 
 enum KernelKind {
   KK_NONE = 0,      // nothing to do (M == 0 or N == 0)
@@ -35,12 +37,13 @@ enum KernelKind {
   KK_Q4_WIDE = 3,
   KK_F_NARROW = 4,  // f16 or f32 src0
   KK_F16_WIDE = 5,
+  KK_Q4_MMA = 6,    // skinny Q4_0 on int8 MFMA (32 weight rows per workgroup)
 };
 
 struct Plan {
   int type = 0;
   int kind = KK_NONE;
-  int variant = 0;          // 1 narrow, 2 wide
+  int variant = 0;          // 1 narrow, 2 wide, 3 skinny MFMA (Q4_0)
   // narrow kernels
   int mt = 1;               // src1 rows per pass (compile-time tile)
   int rpw = 1;              // src0 rows per wave
@@ -53,7 +56,7 @@ struct Plan {
   int64_t grid_n = 1;       // narrow: workgroups along N (each walks tiles_n / grid_n row groups)
   int split = 1;            // split-K factor
   bool fuse = false;        // narrow Q4_0: quantize src1 inside the product kernel
-  int64_t kchunk = 0;       // K units per split (Q4_0: blocks; f16: elements)
+  int64_t kchunk = 0;       // K per split (Q4 narrow: units; wide / skinny: blocks; f16: elements)
   // workspace layout (bytes)
   size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0;
   size_t ws_bytes = 0;

@@ -120,24 +120,31 @@ def test_aliasing():
 
 def test_debug_entry_argument_checks():
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 7, None, 0, None) == ARG
+    # the skinny MFMA variant is for Q4_0 only
+    assert qs.lib.mm_debug_mul_mat(F16, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 3, None, 0, None) == ARG
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 5, 3, 0, None, 0, None) == SHAPE
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 65, 0, None, 0, None) == SHAPE
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 8, 0, None, 0, None) == NULL
     assert qs.lib.mm_debug_mul_mat(9, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 0, None, 0, None) == ARG
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 64, 100, 128, 512])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64, 100, 128, 512])
 def test_dispatch_threshold_and_workspace(m):
     variant, split, rows, cols, launches = qs.dispatch(Q4, m, 4096, 4096)
-    # INIT is fused into the narrow kernel for M <= 2; a split adds the reduce kernel
+    # M <= 2: narrow kernel with INIT fused (one launch); up to 32 src1 rows:
+    # the skinny MFMA kernel; beyond: the wide kernel.  Both of the latter
+    # run INIT first, and a split adds the reduce kernel.
+    want = 1 if m <= 2 else 3 if m <= 32 else 2
+    assert variant == want
     assert launches == (0 if m <= 2 else 1) + 1 + (1 if split > 1 else 0)
-    assert variant == (1 if m <= 8 else 2)
     assert split >= 1
     ws = qs.workspace_size(Q4, m, 4096, 4096)
     # at least the wdata: codes + scale + bias per block
     assert ws >= m * 4096 + 2 * 4 * m * 128
     if variant == 1:
         assert rows >= m or rows == 8
+    if variant == 3:
+        assert rows in (8, 16, 32) and rows >= min(m, 32) and cols == 8
     f16 = qs.dispatch(F16, m, 4096, 4096)
     assert f16[0] == (1 if m <= 16 else 2)
     assert qs.workspace_size(F16, m, 4096, 4096) == 0
@@ -145,13 +152,31 @@ def test_dispatch_threshold_and_workspace(m):
 
 
 def test_split_k_when_grid_is_small():
-    # the tiny workload (N = 256) and a narrow N at the wide kernel must split K
+    # a narrow N at the skinny MFMA kernel must split K (and its workspace
+    # holds the partials)
     v, split, _, _, _ = qs.dispatch(Q4, 32, 64, 14336)
-    assert v == 2 and split > 1
+    assert v == 3 and split > 1
     assert qs.workspace_size(Q4, 32, 64, 14336) >= split * 32 * 64 * 4
+    # the wide kernel too
+    v, split, _, _, _ = qs.dispatch(Q4, 64, 64, 14336)
+    assert v == 2 and split > 1
     # large grids do not split
     assert qs.dispatch(Q4, 512, 14336, 4096)[1] == 1
     assert qs.dispatch(Q4, 1, 11008, 4096)[1] == 1
+    assert qs.dispatch(Q4, 16, 14336, 4096)[1] == 1
+
+
+def test_skinny_mfma_split_keeps_whole_chunks():
+    # K is split across workgroups only while the 32-row tiles leave CUs
+    # idle, with at least one 32-block chunk per split and 8-block aligned
+    # split boundaries
+    for m, n, k in ((32, 14336, 4096), (32, 4096, 14336), (8, 64, 32), (16, 64, 14336)):
+        v, split, rows, _, _ = qs.dispatch(Q4, m, n, k)
+        assert v == 3
+        nb = k // 32
+        assert split == 1 or nb // split >= 24
+        if n >= 8192:
+            assert split == 1
 
 
 def test_workspace_size_of_invalid_shapes_is_zero():
