@@ -325,7 +325,8 @@ def run_sweep(reps: int, out_path: str | None):
             bound, frac = "hbm", gbs / HBM_PEAK_GBS
         r = dict(workload=w, type=t, M=m, N=n, K=k, us=round(us, 3), GBs=round(gbs, 1),
                  TOPS=round(tops, 2), bound=bound, frac=round(frac, 4),
-                 kernel={1: "narrow", 2: "wide", 3: "skinny mfma"}.get(variant, str(variant)),
+                 kernel=({1: "narrow", 2: "wide i8", 3: "skinny mfma", 4: "wide fp16"} if t == "q4_0"
+                         else {1: "narrow", 2: "wide fp16"}).get(variant, str(variant)),
                  split=split, launches=launches,
                  copies=copies)
         results.append(r)

@@ -171,7 +171,8 @@ const char* mm_status_string(int status);
  * mm_dispatch -- the kernel choice mm_mul_mat_* makes at this shape (pure
  * host function).  Writes 5 ints to out (may be NULL):
  *   out[0] variant: 1 = narrow-M kernel, 2 = wide-M (MFMA) kernel,
- *          3 = skinny MFMA kernel (Q4_0, a few src1 rows)
+ *          3 = skinny MFMA kernel (Q4_0, a few src1 rows),
+ *          4 = wide-M fp16-MFMA kernel (Q4_0, batches of tens of rows)
  *   out[1] split-K factor (1 = none)
  *   out[2] rows of src1 per pass (narrow, skinny) or output tile rows (wide)
  *   out[3] output tile columns (wide), src0 rows per wave (narrow) or
@@ -185,7 +186,7 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);
 /*
  * mm_debug_mul_mat -- test entry: the same product as mm_mul_mat_<type>,
  * with the kernel forced (variant 0 = as dispatched, 1 = narrow, 2 = wide,
- * 3 = skinny MFMA; 3 is for Q4_0 only)
+ * 3 = skinny MFMA, 4 = wide fp16 MFMA; 3 and 4 are for Q4_0 only)
  * and, for Q4_0, the int32 block dots S_b[m][n][b] of output columns
  * n0 <= n < n1 also written to `dots` ([M][n1-n0][K/32] int32, may be NULL)
  * by the production kernel itself.  Workspace: mm_debug_workspace_size().

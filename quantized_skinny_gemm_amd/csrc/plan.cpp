@@ -44,7 +44,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   *p = Plan();
   p->type = type;
   if (type != MM_TYPE_F32 && type != MM_TYPE_F16 && type != MM_TYPE_Q4_0) return MM_ERR_ARG;
-  if (variant < 0 || variant > 3 || (variant == 3 && type != MM_TYPE_Q4_0)) return MM_ERR_ARG;
+  if (variant < 0 || variant > 4 || (variant >= 3 && type != MM_TYPE_Q4_0)) return MM_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MM_ERR_SHAPE;
   if (type == MM_TYPE_Q4_0 && (K % kQK)) return MM_ERR_SHAPE;
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
@@ -56,6 +56,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     // kernel; beyond: the tiled wide kernel.
     const bool mma = variant == 3 || (variant == 0 && M > kFuseMaxM && M <= kMmaMaxM);
     const bool narrow = !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
+    const bool wide16 = variant == 4 || (variant == 0 && M > kMmaMaxM && M <= kWide16MaxM);
     size_t off = 0;
     p->off_aq = off; off = align_up(off + (size_t)M * (size_t)K, 256);
     p->off_ad = off; off = align_up(off + (size_t)M * (size_t)nb * 4, 256);
@@ -113,6 +114,27 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       // L2 reads, and saves a launch and the wdata round trip.
       const int64_t kblocks = (nb % 2 == 0) ? 2 * p->kchunk : p->kchunk;
       p->fuse = p->mt <= kFuseMaxM && (int64_t)p->mt * kblocks * 40 <= kNarrowMaxLds;
+    } else if (wide16) {
+      p->kind = KK_Q4_WIDE16;
+      p->variant = 4;
+      // its MFMA operands are binary16: INIT also writes the codes in that form
+      p->off_ah = off; off = align_up(off + (size_t)M * (size_t)K * 2, 256);
+      if (M <= 32) { p->bm = 32; p->bn = 64; p->waves_m = 1; p->waves_n = 2; }
+      else { p->bm = 64; p->bn = 64; p->waves_m = 2; p->waves_n = 2; }
+      p->tiles_m = ceil_div(M, p->bm);
+      p->tiles_n = ceil_div(N, p->bn);
+      const int64_t tiles = p->tiles_m * p->tiles_n;
+      const int64_t stages = ceil_div(nb, kWide16KB);
+      int64_t split = 1;
+      if (allow_split && tiles < kCUs) {
+        split = ceil_div(kCUs, tiles);
+        const int64_t max_split = stages / 2;          // >= 2 stages per split
+        if (split > max_split) split = max_split;
+        if (split > 16) split = 16;
+        if (split < 1) split = 1;
+      }
+      p->kchunk = ceil_div(stages, split) * kWide16KB;   // blocks per split
+      p->split = (int)ceil_div(nb, p->kchunk);
     } else {
       p->kind = KK_Q4_WIDE;
       p->variant = 2;
@@ -129,7 +151,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
         break;
       }
       const int64_t tiles = p->tiles_m * p->tiles_n;
-      const int64_t stages = ceil_div(nb, kWideKB);
+      const int64_t stages = ceil_div(nb, kWideI8KB);
       int64_t split = 1;
       if (allow_split && tiles < kCUs) {
         split = ceil_div(kCUs, tiles);
@@ -138,7 +160,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
         if (split > 16) split = 16;
         if (split < 1) split = 1;
       }
-      p->kchunk = ceil_div(stages, split) * kWideKB;   // blocks per split
+      p->kchunk = ceil_div(stages, split) * kWideI8KB;   // blocks per split
       p->split = (int)ceil_div(nb, p->kchunk);
     }
     if (p->split > 1) {

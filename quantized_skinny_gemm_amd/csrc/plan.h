@@ -20,7 +20,9 @@ constexpr int kQK = 32;            // values per Q4_0 / Q8_0 block
 constexpr int kQ4Bytes = 18;       // bytes per Q4_0 block
 constexpr int kQ8Bytes = 34;       // bytes per Q8_0 block
 constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kWideKB = 4;         // Q4_0 blocks per LDS stage in the wide kernel
+constexpr int kWideI8KB = 4;       // Q4_0 blocks per LDS stage, int8 wide kernel
+constexpr int kWide16KB = 8;       // Q4_0 blocks per LDS stage, fp16 wide kernel
+constexpr int kWide16MaxM = 128;   // largest M the fp16 wide kernel takes by default
 constexpr int kF16WideKS = 32;     // k elements per LDS stage in the f16 wide kernel
 constexpr int kNarrowQ4MaxM = 8;   // largest M the Q4_0 narrow kernel takes in one pass
 constexpr int kNarrowFMaxM = 16;   // largest M the f16/f32 narrow kernel takes in one pass
@@ -38,12 +40,13 @@ enum KernelKind {
   KK_F_NARROW = 4,  // f16 or f32 src0
   KK_F16_WIDE = 5,
   KK_Q4_MMA = 6,    // skinny Q4_0 on int8 MFMA (32 weight rows per workgroup)
+  KK_Q4_WIDE16 = 7, // wide Q4_0 on fp16 MFMA with exact block dots
 };
 
 struct Plan {
   int type = 0;
   int kind = KK_NONE;
-  int variant = 0;          // 1 narrow, 2 wide, 3 skinny MFMA (Q4_0)
+  int variant = 0;          // 1 narrow, 2 wide (int8), 3 skinny MFMA, 4 wide (fp16); Q4_0
   // narrow kernels
   int mt = 1;               // src1 rows per pass (compile-time tile)
   int rpw = 1;              // src0 rows per wave
@@ -59,6 +62,7 @@ struct Plan {
   int64_t kchunk = 0;       // K per split (Q4 narrow: units; wide / skinny: blocks; f16: elements)
   // workspace layout (bytes)
   size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0;
+  size_t off_ah = 0;        // wide kernel: Q8_0 codes as binary16 [M][K] (0: not written)
   size_t ws_bytes = 0;
 };
 

@@ -1,4 +1,4 @@
-// Wide-M Q4_0 x Q8_0 product for gfx950 on int8 MFMA.
+// Wide-M Q4_0 x Q8_0 product for gfx950 on int8 MFMA (the larger batches).
 //
 // Past the narrow kernel's threshold the product is a dense contraction (the
 // first-token / prefill regime, arXiv 2407.07304 section 2.2), so it runs on
@@ -27,7 +27,7 @@ namespace qsg {
 
 namespace {
 
-constexpr int KB = kWideKB;          // blocks per stage
+constexpr int KB = kWideI8KB;        // blocks per stage
 constexpr int PITCH = KB * 32 + 8;   // bytes per LDS row of codes (pad against bank conflicts)
 
 __device__ __forceinline__ uint32_t nib_lo_signed(uint32_t q) {
@@ -240,7 +240,7 @@ hipError_t launch_cfg(const Plan& p, const Q4Args& a, bool pairs, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_q4_wide(const Plan& p, const Q4Args& a, hipStream_t s) {
+hipError_t launch_q4_wide_i8(const Plan& p, const Q4Args& a, hipStream_t s) {
   const bool pairs = ((a.K / 32) % 2 == 0) && ((uintptr_t)a.w % 4 == 0);
   if (p.bm == 32 && p.bn == 64) return launch_cfg<32, 64, 1, 2>(p, a, pairs, s);
   if (p.bm == 64 && p.bn == 64) return launch_cfg<64, 64, 2, 2>(p, a, pairs, s);

@@ -120,8 +120,10 @@ def test_aliasing():
 
 def test_debug_entry_argument_checks():
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 7, None, 0, None) == ARG
-    # the skinny MFMA variant is for Q4_0 only
+    # the skinny and fp16 wide variants are for Q4_0 only
     assert qs.lib.mm_debug_mul_mat(F16, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 3, None, 0, None) == ARG
+    assert qs.lib.mm_debug_mul_mat(F16, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 4, None, 0, None) == ARG
+    assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 5, None, 0, None) == ARG
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 5, 3, 0, None, 0, None) == SHAPE
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 65, 0, None, 0, None) == SHAPE
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 8, 0, None, 0, None) == NULL
@@ -134,7 +136,7 @@ def test_dispatch_threshold_and_workspace(m):
     # M <= 2: narrow kernel with INIT fused (one launch); up to 32 src1 rows:
     # the skinny MFMA kernel; beyond: the wide kernel.  Both of the latter
     # run INIT first, and a split adds the reduce kernel.
-    want = 1 if m <= 2 else 3 if m <= 32 else 2
+    want = 1 if m <= 2 else 3 if m <= 32 else 4 if m <= 128 else 2
     assert variant == want
     assert launches == (0 if m <= 2 else 1) + 1 + (1 if split > 1 else 0)
     assert split >= 1
@@ -157,8 +159,10 @@ def test_split_k_when_grid_is_small():
     v, split, _, _, _ = qs.dispatch(Q4, 32, 64, 14336)
     assert v == 3 and split > 1
     assert qs.workspace_size(Q4, 32, 64, 14336) >= split * 32 * 64 * 4
-    # the wide kernel too
+    # the wide kernels too
     v, split, _, _, _ = qs.dispatch(Q4, 64, 64, 14336)
+    assert v == 4 and split > 1
+    v, split, _, _, _ = qs.dispatch(Q4, 256, 64, 14336)
     assert v == 2 and split > 1
     # large grids do not split
     assert qs.dispatch(Q4, 512, 14336, 4096)[1] == 1
