@@ -326,7 +326,7 @@ def run_sweep(reps: int, out_path: str | None):
         r = dict(workload=w, type=t, M=m, N=n, K=k, us=round(us, 3), GBs=round(gbs, 1),
                  TOPS=round(tops, 2), bound=bound, frac=round(frac, 4),
                  kernel=({1: "narrow", 2: "wide i8", 3: "skinny mfma", 4: "wide fp16"} if t == "q4_0"
-                         else {1: "narrow", 2: "wide fp16"}).get(variant, str(variant)),
+                         else {1: "narrow", 2: "wide fp16", 3: "skinny mfma"}).get(variant, str(variant)),
                  split=split, launches=launches,
                  copies=copies)
         results.append(r)

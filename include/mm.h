@@ -139,19 +139,26 @@ size_t mm_mul_mat_q4_0_group_workspace_size(int count, const int64_t* Ns, int64_
 /*
  * mm_mul_mat_f16_f32 -- dst[M][N] = src1[M][K] . f32(src0[N][K])^T, fp32 accumulation.
  *   src0: IEEE binary16 [N][K], 2-byte aligned.  src1: f32 [M][K], 4-byte
- *   aligned.  dst: f32, 4-byte aligned.  Any K >= 0.  For M <= 16 src1 is
- *   used in f32; for larger M it is rounded to binary16 for the f16 MFMA
- *   (relative effect about 1e-4, inside the 1e-3 bound of this kind).
- *   ws: mm_mul_mat_workspace_size(MM_TYPE_F16, ...) bytes (may be 0).
+ *   aligned.  dst: f32, 4-byte aligned.  Any K >= 0.  M = 1: src1 is used
+ *   in f32.  2 <= M <= 16 (src0 16-byte aligned and K a multiple of 8, else
+ *   as M = 1): src1 enters the f16 MFMA as two binary16 terms hi + lo whose
+ *   sum carries about 22 significant bits of each value (relative effect
+ *   about 1e-6).  M > 16: src1 is rounded to binary16 for the f16 MFMA
+ *   (relative effect about 1e-4).  Both inside the 1e-3 bound of this kind.
+ *   ws: mm_mul_mat_workspace_size(MM_TYPE_F16, ...) bytes (0 when that is
+ *   0); at 2 <= M <= 16 it holds split-K partial sums.
  */
 int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst,
                        int64_t M, int64_t N, int64_t K,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
- * mm_mul_mat_f32 -- dst[M][N] = src1[M][K] . src0[N][K]^T, all f32, fp32 FMA.
+ * mm_mul_mat_f32 -- dst[M][N] = src1[M][K] . src0[N][K]^T, all f32 products,
+ *   fp32 accumulation (vector FMA at M = 1; from M = 2 the fp32 MFMA when
+ *   src0 is 16-byte aligned and K a multiple of 4).
  *   All pointers 4-byte aligned.  Any K >= 0.
- *   ws: mm_mul_mat_workspace_size(MM_TYPE_F32, ...) bytes (may be 0).
+ *   ws: mm_mul_mat_workspace_size(MM_TYPE_F32, ...) bytes (0 when that is
+ *   0); from M = 2 it holds split-K partial sums.
  */
 int mm_mul_mat_f32(const float* src0, const float* src1, float* dst,
                    int64_t M, int64_t N, int64_t K,
@@ -170,8 +177,8 @@ const char* mm_status_string(int status);
 /*
  * mm_dispatch -- the kernel choice mm_mul_mat_* makes at this shape (pure
  * host function).  Writes 5 ints to out (may be NULL):
- *   out[0] variant: 1 = narrow-M kernel, 2 = wide-M (MFMA) kernel,
- *          3 = skinny MFMA kernel (Q4_0, a few src1 rows),
+ *   out[0] variant: 1 = narrow-M kernel, 2 = wide-M (MFMA) kernel (Q4_0,
+ *          F16), 3 = skinny MFMA kernel (a few src1 rows; F32 from 2),
  *          4 = wide-M fp16-MFMA kernel (Q4_0, batches of tens of rows)
  *   out[1] split-K factor (1 = none)
  *   out[2] rows of src1 per pass (narrow, skinny) or output tile rows (wide)
@@ -185,8 +192,9 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);
 
 /*
  * mm_debug_mul_mat -- test entry: the same product as mm_mul_mat_<type>,
- * with the kernel forced (variant 0 = as dispatched, 1 = narrow, 2 = wide,
- * 3 = skinny MFMA, 4 = wide fp16 MFMA; 3 and 4 are for Q4_0 only)
+ * with the kernel forced (variant 0 = as dispatched, 1 = narrow, 2 = wide
+ * (Q4_0 and F16 only), 3 = skinny MFMA, 4 = wide fp16 MFMA (Q4_0 only);
+ * MM_ERR_ARG for a variant the type does not have)
  * and, for Q4_0, the int32 block dots S_b[m][n][b] of output columns
  * n0 <= n < n1 also written to `dots` ([M][n1-n0][K/32] int32, may be NULL)
  * by the production kernel itself.  Workspace: mm_debug_workspace_size().

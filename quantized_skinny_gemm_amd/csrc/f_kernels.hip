@@ -6,6 +6,17 @@
 // 64-lane butterfly reduction.  Rows of src1 beyond 16 are handled by further
 // passes (grid.y).
 //
+// Skinny MFMA kernel (F16 at 2 <= M <= 16, F32 at M >= 2; rows 16-byte
+// aligned): passes of 16 src1 rows on the 16 x 16 matrix cores.  Each wave
+// owns 16 weight rows of a K slice and loads their 16-byte pieces straight
+// into MFMA operand order (no unpacking, no per-block epilogue: the weights
+// are the B operand as stored); the workgroup's src1 slice is staged in LDS
+// once and read by its 8 waves.  F16 uses v_mfma_f32_16x16x32_f16 with src1
+// split into two binary16 terms hi + lo (their sum carries about 22 bits of
+// the f32 value; each f16 x f16 product is exact in fp32), F32 uses
+// v_mfma_f32_16x16x4_f32 on the values as they are.  K slices beyond one
+// go to split-K partials added by the fixed-order reduce kernel.
+//
 // Wide f16 kernel (M > 16): a dense contraction on v_mfma_f32_32x32x16_f16
 // with src1 rounded to binary16 while staging into LDS and fp32 accumulation.
 // bf16 is avoided: the pages note that at small sizes converting operands to
@@ -130,6 +141,123 @@ hipError_t launch_f_typed(const Plan& p, const WT* w, const float* x, float* dst
     case 8: return launch_f_mt<WT, 8, 2>(p, w, x, dst, M, N, K, vec, s);
     case 16: return launch_f_mt<WT, 16, 2>(p, w, x, dst, M, N, K, vec, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+// ------------------------------------------------------------ skinny MFMA (F16, F32)
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <bool kF16>
+struct FmCfg {
+  static constexpr int kSub = kF16 ? kFmSubF16 : kFmSubF32;   // k per sub-slice: 16 steps
+  static constexpr int kStep = kSub / 16;                       // k per step (32 or 16)
+  static constexpr int kPitch = kSub + (kF16 ? 8 : 4);          // LDS row pitch (elements)
+  static constexpr int kLds = kF16 ? 2 * 16 * kPitch * 2 : 16 * kPitch * 4;
+};
+
+// Lane (l16, kq) of wave w: B operand column = weight row n0 + 16 w + l16; in
+// step s of a sub-slice starting at k0 it holds k = k0 + kStep s + 8 kq ..
+// +7 (F16) or k0 + kStep s + 4 kq .. +3 (F32: one element per 16x16x4 MFMA,
+// the same k in the A operand).  Output: rows m0 + 4 kq .. +3, column n.
+template <bool kF16, bool kVecX>
+__global__ __launch_bounds__(512, 2)
+void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* __restrict__ out,
+             int M, int N, int K, int krange) {
+  typedef FmCfg<kF16> C;
+  constexpr int SUB = C::kSub, XP = C::kPitch, ST = C::kStep;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[C::kLds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int m0 = blockIdx.y * 16, z = blockIdx.z;
+  const int n = blockIdx.x * (16 * kFmWaves) + 16 * wave + l16;
+  const int nr = n < N ? n : N - 1;
+  const int kbeg = z * krange;
+  const int kend = kbeg + krange < K ? kbeg + krange : K;
+  const uint8_t* wrow = reinterpret_cast<const uint8_t*>(wv_) + (int64_t)nr * K * (kF16 ? 2 : 4);
+  float* o = out + (int64_t)z * M * N;               // the slice's partial (dst when one slice)
+  const int kl = kF16 ? 8 * kq : 4 * kq;             // this lane's k offset within a step
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  constexpr int IT = 16 * SUB / 4 / 512;              // src1 float4 items per thread
+  for (int k0 = kbeg; k0 < kend; k0 += SUB) {
+    // src1 rows m0 .. m0+15, k0 .. k0+SUB-1 first (their wait then leaves
+    // the weights in flight), clamped into range and zeroed past M and kend
+    // (kend % 4 == 0: an item is wholly in or out)
+    float4 xv[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + 512 * it;
+      const int r = i / (SUB / 4), c = i % (SUB / 4);
+      const int m = m0 + r < M ? m0 + r : M - 1, k = k0 + 4 * c < kend ? k0 + 4 * c : kbeg;
+      const float* px = x + (int64_t)m * K + k;
+      if (kVecX) {
+        xv[it] = *reinterpret_cast<const float4*>(px);
+      } else {
+        xv[it] = make_float4(px[0], px[1], px[2], px[3]);
+      }
+    }
+    // this lane's 16 weight pieces of the sub-slice (past kend: clamped,
+    // then zeroed)
+    v4i wp[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int k = k0 + ST * s + kl;
+      const int kc = k < kend ? k : 0;
+      wp[s] = *(const __attribute__((address_space(1))) v4i*)(wrow + (int64_t)kc * (kF16 ? 2 : 4));
+    }
+    __syncthreads();                                 // the last sub-slice's LDS reads are done
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + 512 * it;
+      const int r = i / (SUB / 4), c = i % (SUB / 4);
+      const bool ok = m0 + r < M && k0 + 4 * c < kend;
+      const float v[4] = {ok ? xv[it].x : 0.0f, ok ? xv[it].y : 0.0f, ok ? xv[it].z : 0.0f,
+                          ok ? xv[it].w : 0.0f};
+      if constexpr (kF16) {
+        _Float16* xh = reinterpret_cast<_Float16*>(xs);
+        _Float16* xl = xh + 16 * XP;
+        v4h hi, lo;
+        hi.x = (_Float16)v[0]; hi.y = (_Float16)v[1]; hi.z = (_Float16)v[2]; hi.w = (_Float16)v[3];
+        lo.x = (_Float16)(v[0] - (float)hi.x); lo.y = (_Float16)(v[1] - (float)hi.y);
+        lo.z = (_Float16)(v[2] - (float)hi.z); lo.w = (_Float16)(v[3] - (float)hi.w);
+        *reinterpret_cast<v4h*>(xh + r * XP + 4 * c) = hi;
+        *reinterpret_cast<v4h*>(xl + r * XP + 4 * c) = lo;
+      } else {
+        float* xf = reinterpret_cast<float*>(xs);
+        *reinterpret_cast<float4*>(xf + r * XP + 4 * c) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const bool in = k0 + ST * s + kl < kend;
+      v4i b = wp[s];
+      b.x = in ? b.x : 0; b.y = in ? b.y : 0; b.z = in ? b.z : 0; b.w = in ? b.w : 0;
+      if constexpr (kF16) {
+        const _Float16* xh = reinterpret_cast<const _Float16*>(xs);
+        const _Float16* xl = xh + 16 * XP;
+        const v8h bh = __builtin_bit_cast(v8h, b);
+        const v8h ah = *reinterpret_cast<const v8h*>(xh + l16 * XP + ST * s + kl);
+        const v8h al = *reinterpret_cast<const v8h*>(xl + l16 * XP + ST * s + kl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
+      } else {
+        const float* xf = reinterpret_cast<const float*>(xs);
+        const float4 a4 = *reinterpret_cast<const float4*>(xf + l16 * XP + ST * s + kl);
+        // whole-vector bit cast (a bit cast of one element lvalue of an
+        // ext_vector reads element 0 with this compiler)
+        const v4f bf = __builtin_bit_cast(v4f, b);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, bf[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, bf[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, bf[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, bf[3], acc, 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = m0 + 4 * kq + r;
+    if (m < M && n < N) o[(int64_t)m * N + n] = acc[r];
   }
 }
 
@@ -273,6 +401,25 @@ hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, flo
   } else {
     if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
     else hipLaunchKernelGGL((k_f16_wide<64, 64, false>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
+  }
+  return hipGetLastError();
+}
+
+bool f_mma_aligned(int type, const void* w, int K) {
+  return (uintptr_t)w % 16 == 0 && K % (type == MM_TYPE_F16 ? 8 : 4) == 0;
+}
+
+hipError_t launch_f_mma(const Plan& p, int type, const void* w, const float* x, float* out, int M,
+                        int N, int K, hipStream_t s) {
+  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.split);
+  const int kr = (int)p.kchunk;
+  const bool vx = (uintptr_t)x % 16 == 0;
+  if (type == MM_TYPE_F16) {
+    if (vx) hipLaunchKernelGGL((k_f_mma<true, true>), grid, dim3(512), 0, s, w, x, out, M, N, K, kr);
+    else hipLaunchKernelGGL((k_f_mma<true, false>), grid, dim3(512), 0, s, w, x, out, M, N, K, kr);
+  } else {
+    if (vx) hipLaunchKernelGGL((k_f_mma<false, true>), grid, dim3(512), 0, s, w, x, out, M, N, K, kr);
+    else hipLaunchKernelGGL((k_f_mma<false, false>), grid, dim3(512), 0, s, w, x, out, M, N, K, kr);
   }
   return hipGetLastError();
 }

@@ -44,7 +44,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   *p = Plan();
   p->type = type;
   if (type != MM_TYPE_F32 && type != MM_TYPE_F16 && type != MM_TYPE_Q4_0) return MM_ERR_ARG;
-  if (variant < 0 || variant > 4 || (variant >= 3 && type != MM_TYPE_Q4_0)) return MM_ERR_ARG;
+  if (variant < 0 || variant > 4) return MM_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MM_ERR_SHAPE;
   if (type == MM_TYPE_Q4_0 && (K % kQK)) return MM_ERR_SHAPE;
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
@@ -170,8 +170,41 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     return MM_OK;
   }
 
-  // F16 / F32
-  const bool wide = type == MM_TYPE_F16 && (variant == 2 || (variant == 0 && M > kNarrowFMaxM));
+  // F16 / F32: M = 1 the narrow kernel; F16 up to kNarrowFMaxM rows and F32
+  // from 2 rows the skinny MFMA kernel; F16 beyond the wide kernel.
+  if (variant == 4 || (variant == 2 && type != MM_TYPE_F16)) return MM_ERR_ARG;
+  const bool f16 = type == MM_TYPE_F16;
+  const bool wide = f16 && (variant == 2 || (variant == 0 && M > kNarrowFMaxM));
+  const bool fmma = !wide && (variant == 3 || (variant == 0 && M >= 2));
+  if (fmma) {
+    p->kind = KK_F_MMA;
+    p->variant = 3;
+    p->mt = 16;
+    p->waves = kFmWaves;
+    p->tiles_m = ceil_div(M, 16);
+    p->tiles_n = ceil_div(N, 16 * kFmWaves);
+    // K slices of whole sub-slices until there are about two workgroups per
+    // CU (each slice adds M * N partial sums, written and read once)
+    const int64_t sub = f16 ? kFmSubF16 : kFmSubF32;
+    const int64_t subs = ceil_div(K, sub);
+    int64_t split = 1;
+    if (allow_split) {
+      const int64_t wgs = p->tiles_m * p->tiles_n;
+      split = ceil_div(2 * kCUs, wgs);
+      if (split > subs) split = subs;
+      if (split > 16) split = 16;
+      if (split < 1) split = 1;
+    }
+    p->kchunk = ceil_div(subs, split) * sub;           // elements per slice
+    p->split = (int)ceil_div(K, p->kchunk);
+    size_t off = 0;
+    if (p->split > 1) {
+      p->off_part = off;
+      off = align_up(off + (size_t)p->split * (size_t)M * (size_t)N * 4, 256);
+    }
+    p->ws_bytes = off;
+    return MM_OK;
+  }
   if (!wide) {
     p->kind = KK_F_NARROW;
     p->variant = 1;

@@ -24,6 +24,9 @@ constexpr int kWideI8KB = 4;       // Q4_0 blocks per LDS stage, int8 wide kerne
 constexpr int kWide16KB = 8;       // Q4_0 blocks per LDS stage, fp16 wide kernel
 constexpr int kWide16MaxM = 128;   // largest M the fp16 wide kernel takes by default
 constexpr int kF16WideKS = 32;     // k elements per LDS stage in the f16 wide kernel
+constexpr int kFmSubF16 = 512;     // skinny F16 MFMA kernel: k per LDS sub-slice (16 MFMA steps)
+constexpr int kFmSubF32 = 256;     // skinny F32 MFMA kernel: k per LDS sub-slice
+constexpr int kFmWaves = 8;        // skinny F MFMA kernel: waves (16 weight rows each) per workgroup
 constexpr int kNarrowQ4MaxM = 8;   // largest M the Q4_0 narrow kernel takes in one pass
 constexpr int kNarrowFMaxM = 16;   // largest M the f16/f32 narrow kernel takes in one pass
 constexpr int kFuseMaxM = 2;       // narrow Q4_0 passes of at most this many rows fuse INIT
@@ -41,12 +44,13 @@ enum KernelKind {
   KK_F16_WIDE = 5,
   KK_Q4_MMA = 6,    // skinny Q4_0 on int8 MFMA (32 weight rows per workgroup)
   KK_Q4_WIDE16 = 7, // wide Q4_0 on fp16 MFMA with exact block dots
+  KK_F_MMA = 8,     // skinny F16 / F32 on the 16x16 MFMA (passes of 16 src1 rows)
 };
 
 struct Plan {
   int type = 0;
   int kind = KK_NONE;
-  int variant = 0;          // 1 narrow, 2 wide (int8), 3 skinny MFMA, 4 wide (fp16); Q4_0
+  int variant = 0;          // 1 narrow, 2 wide (Q4_0: int8; F16: fp16), 3 skinny MFMA, 4 wide (Q4_0, fp16)
   // narrow kernels
   int mt = 1;               // src1 rows per pass (compile-time tile)
   int rpw = 1;              // src0 rows per wave
@@ -59,7 +63,7 @@ struct Plan {
   int64_t grid_n = 1;       // narrow: workgroups along N (each walks tiles_n / grid_n row groups)
   int split = 1;            // split-K factor
   bool fuse = false;        // narrow Q4_0: quantize src1 inside the product kernel
-  int64_t kchunk = 0;       // K per split (Q4 narrow: units; wide / skinny: blocks; f16: elements)
+  int64_t kchunk = 0;       // K per split (Q4 narrow: units; Q4 wide / skinny: blocks; F: elements)
   // workspace layout (bytes)
   size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0;
   size_t off_ah = 0;        // wide kernel: Q8_0 codes as binary16 [M][K] (0: not written)

@@ -120,9 +120,13 @@ def test_aliasing():
 
 def test_debug_entry_argument_checks():
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 7, None, 0, None) == ARG
-    # the skinny and fp16 wide variants are for Q4_0 only
-    assert qs.lib.mm_debug_mul_mat(F16, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 3, None, 0, None) == ARG
+    # the fp16 wide Q4_0 variant is for Q4_0 only, the wide F kernel for F16 only
     assert qs.lib.mm_debug_mul_mat(F16, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 4, None, 0, None) == ARG
+    assert qs.lib.mm_debug_mul_mat(F32, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 4, None, 0, None) == ARG
+    assert qs.lib.mm_debug_mul_mat(F32, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 2, None, 0, None) == ARG
+    # the skinny MFMA variant exists for every type
+    for t in (F16, F32, Q4):
+        assert qs.lib.mm_debug_workspace_size(t, 4, 64, 64, 3) >= 0
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 5, None, 0, None) == ARG
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 5, 3, 0, None, 0, None) == SHAPE
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 65, 0, None, 0, None) == SHAPE
@@ -147,10 +151,19 @@ def test_dispatch_threshold_and_workspace(m):
         assert rows >= m or rows == 8
     if variant == 3:
         assert rows in (8, 16, 32) and rows >= min(m, 32) and cols == 8
-    f16 = qs.dispatch(F16, m, 4096, 4096)
-    assert f16[0] == (1 if m <= 16 else 2)
-    assert qs.workspace_size(F16, m, 4096, 4096) == 0
-    assert qs.dispatch(F32, m, 4096, 4096)[0] == 1
+    # F16: M = 1 narrow, up to 16 rows the skinny MFMA kernel (K slices
+    # through the workspace), beyond the wide kernel; F32: narrow at M = 1,
+    # skinny MFMA from 2 rows
+    for t in (F16, F32):
+        fv, fsplit, frows, fcols, flaunch = qs.dispatch(t, m, 4096, 4096)
+        fwant = 1 if m == 1 else 3 if (m <= 16 or t == F32) else 2
+        assert fv == fwant
+        if fv == 3:
+            assert frows == 16 and fcols == 8
+            assert flaunch == 1 + (1 if fsplit > 1 else 0)
+            assert qs.workspace_size(t, m, 4096, 4096) >= (fsplit * m * 4096 * 4 if fsplit > 1 else 0)
+        else:
+            assert fsplit == 1 and qs.workspace_size(t, m, 4096, 4096) == 0
 
 
 def test_split_k_when_grid_is_small():

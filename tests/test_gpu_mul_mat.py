@@ -208,9 +208,12 @@ def test_ragged_shapes_f16_f32(m, n, k):
     y16 = to_host(qs.mul_mat_f16_f32(to_dev(wh), to_dev(x)))
     assert_close(y32, mul_mat.mul_mat_f32(w, x), TOL_F, "f32")
     assert_close(y16, mul_mat.mul_mat_f16_f32(wh, x), TOL_F, "f16")
-    for v in (1, 2):
+    for v in (1, 2, 3):
         y, _ = qs.debug_mul_mat(qs.MM_TYPE_F16, to_dev(wh), to_dev(x), v)
         assert_close(to_host(y), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 variant {v}")
+    for v in (1, 3):
+        y, _ = qs.debug_mul_mat(qs.MM_TYPE_F32, to_dev(w), to_dev(x), v)
+        assert_close(to_host(y), mul_mat.mul_mat_f32(w, x), TOL_F, f"f32 variant {v}")
 
 
 def test_empty_and_zero_k():
