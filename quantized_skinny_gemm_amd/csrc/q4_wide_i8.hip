@@ -97,75 +97,111 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  for (int kb = kb0; kb < kb1; kb += KB) {
-    __syncthreads();
-    // ---- stage weights: BN rows x KB blocks, decoded
-    if (kPairs) {
-      for (int i = tid; i < BN * (KB / 2); i += NT) {
+  // Register prefetch: the next stage's global loads are issued before the
+  // current stage is computed.  Loads are unconditional, with addresses
+  // clamped into the matrices; what lies outside the tile or the K range is
+  // masked when the registers are written to LDS (codes 8 and zero scales for
+  // weights, zero codes and scales for activations).
+  constexpr int WI = kPairs ? (BN * (KB / 2) + NT - 1) / NT : (BN * KB + NT - 1) / NT;
+  constexpr int AI = (BM * KB * 2 + NT - 1) / NT;
+  constexpr int SI = (BM * KB + NT - 1) / NT;
+  uint32_t wreg[WI][9];
+  v4i areg[AI];
+  float sreg[SI];
+  auto load_stage = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < WI; ++u) {
+      const int i = tid + u * NT;
+      if (kPairs) {
+        const int r = (i / (KB / 2)) % BN, pp = i % (KB / 2);
+        const int n = n0 + r < N ? n0 + r : N - 1;
+        const int b = kb + 2 * pp < kb1 ? kb + 2 * pp : kb0;
+        const __attribute__((address_space(1))) uint32_t* p =
+            (const __attribute__((address_space(1))) uint32_t*)(a.w + (int64_t)n * rb + (int64_t)b * 18);
+#pragma unroll
+        for (int j = 0; j < 9; ++j) wreg[u][j] = p[j];
+      } else {
+        const int r = (i / KB) % BN, bb = i % KB;
+        const int n = n0 + r < N ? n0 + r : N - 1;
+        const int b = kb + bb < kb1 ? kb + bb : kb0;
+        const __attribute__((address_space(1))) uint16_t* p =
+            (const __attribute__((address_space(1))) uint16_t*)(a.w + (int64_t)n * rb + (int64_t)b * 18);
+#pragma unroll
+        for (int j = 0; j < 9; ++j) wreg[u][j] = p[j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < AI; ++u) {
+      const int i = tid + u * NT;
+      const int r = (i / (KB * 2)) % BM, c = i % (KB * 2);
+      const int m = m0 + r < M ? m0 + r : M - 1;
+      // codes of block kb + c/2, half c%2; out of range: block kb0 (valid)
+      const int64_t off = kb + c / 2 < kb1 ? (int64_t)kb * 32 + c * 16 : (int64_t)kb0 * 32 + (c & 1) * 16;
+      areg[u] = *(const __attribute__((address_space(1))) v4i*)(a.aq + (int64_t)m * K + off);
+    }
+#pragma unroll
+    for (int u = 0; u < SI; ++u) {
+      const int i = tid + u * NT;
+      const int r = i % BM, bb = (i / BM) % KB;
+      const int m = m0 + r < M ? m0 + r : M - 1;
+      const int b = kb + bb < kb1 ? kb + bb : kb0;
+      sreg[u] = *(const __attribute__((address_space(1))) float*)(a.ad + (int64_t)m * nb + b);
+    }
+  };
+  auto store_stage = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < WI; ++u) {
+      const int i = tid + u * NT;
+      if (kPairs) {
+        if (i >= BN * (KB / 2)) continue;
         const int r = i / (KB / 2), pp = i % (KB / 2);
-        const int n = n0 + r, b = kb + 2 * pp;
-        uint32_t wv[9];
-        if (n < N && b < kb1) {
-          const uint32_t* p = reinterpret_cast<const uint32_t*>(a.w + (int64_t)n * rb + (int64_t)b * 18);
-#pragma unroll
-          for (int j = 0; j < 9; ++j) wv[j] = p[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 9; ++j) wv[j] = 0x88888888u;
-          wv[0] = 0x88880000u; wv[4] = 0x00008888u;    // zero scales
-        }
+        const int b = kb + 2 * pp;
+        const bool ok0 = n0 + r < N && b < kb1, ok1 = ok0 && b + 1 < kb1;
         uint32_t q0[4], q1[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          q0[j] = __builtin_amdgcn_alignbit(wv[j + 1], wv[j], 16);
-          q1[j] = wv[5 + j];
+          q0[j] = ok0 ? __builtin_amdgcn_alignbit(wreg[u][j + 1], wreg[u][j], 16) : 0x88888888u;
+          q1[j] = ok1 ? wreg[u][5 + j] : 0x88888888u;
         }
-        const float d0 = f16_bits_to_f32(wv[0]);
-        float d1 = f16_bits_to_f32(wv[4] >> 16);
-        if (b + 1 >= kb1) {                              // odd tail: block b+1 is not ours
-          d1 = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) q1[j] = 0x88888888u;
-        }
+        const float d0 = ok0 ? f16_bits_to_f32(wreg[u][0]) : 0.0f;
+        const float d1 = ok1 ? f16_bits_to_f32(wreg[u][4] >> 16) : 0.0f;
         put_block(sB, sBd, BN, r, 2 * pp, d0, q0);
         put_block(sB, sBd, BN, r, 2 * pp + 1, d1, q1);
-      }
-    } else {
-      for (int i = tid; i < BN * KB; i += NT) {
+      } else {
+        if (i >= BN * KB) continue;
         const int r = i / KB, bb = i % KB;
-        const int n = n0 + r, b = kb + bb;
-        uint32_t q[4] = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-        float d = 0.0f;
-        if (n < N && b < kb1) {
-          const uint16_t* p = reinterpret_cast<const uint16_t*>(a.w + (int64_t)n * rb + (int64_t)b * 18);
-          uint32_t hw[9];
+        const bool ok = n0 + r < N && kb + bb < kb1;
+        uint32_t q[4];
 #pragma unroll
-          for (int j = 0; j < 9; ++j) hw[j] = p[j];
-          d = f16_bits_to_f32(hw[0]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) q[j] = hw[1 + 2 * j] | (hw[2 + 2 * j] << 16);
-        }
-        put_block(sB, sBd, BN, r, bb, d, q);
+        for (int j = 0; j < 4; ++j) q[j] = ok ? (wreg[u][1 + 2 * j] | (wreg[u][2 + 2 * j] << 16)) : 0x88888888u;
+        put_block(sB, sBd, BN, r, bb, ok ? f16_bits_to_f32(wreg[u][0]) : 0.0f, q);
       }
     }
-    // ---- stage activations: BM rows x KB*32 codes + scales
-    for (int i = tid; i < BM * KB * 2; i += NT) {
+#pragma unroll
+    for (int u = 0; u < AI; ++u) {
+      const int i = tid + u * NT;
+      if (i >= BM * KB * 2) continue;
       const int r = i / (KB * 2), c = i % (KB * 2);
-      const int m = m0 + r, b = kb + c / 2;
-      v4i v = {0, 0, 0, 0};
-      if (m < M && b < kb1)
-        v = *reinterpret_cast<const v4i*>(a.aq + (int64_t)m * K + (int64_t)kb * 32 + c * 16);
+      const bool ok = m0 + r < M && kb + c / 2 < kb1;
       uint2* p = reinterpret_cast<uint2*>(sA + r * PITCH + c * 16);
-      p[0] = make_uint2((uint32_t)v.x, (uint32_t)v.y);
-      p[1] = make_uint2((uint32_t)v.z, (uint32_t)v.w);
+      p[0] = make_uint2(ok ? (uint32_t)areg[u].x : 0u, ok ? (uint32_t)areg[u].y : 0u);
+      p[1] = make_uint2(ok ? (uint32_t)areg[u].z : 0u, ok ? (uint32_t)areg[u].w : 0u);
     }
-    for (int i = tid; i < BM * KB; i += NT) {
+#pragma unroll
+    for (int u = 0; u < SI; ++u) {
+      const int i = tid + u * NT;
+      if (i >= BM * KB) continue;
       const int r = i % BM, bb = i / BM;
-      const int m = m0 + r, b = kb + bb;
-      sAd[bb * BM + r] = (m < M && b < kb1) ? a.ad[(int64_t)m * nb + b] : 0.0f;
+      sAd[bb * BM + r] = (m0 + r < M && kb + bb < kb1) ? sreg[u] : 0.0f;
     }
-    __syncthreads();
+  };
 
+  load_stage(kb0);
+  for (int kb = kb0; kb < kb1; kb += KB) {
+    __syncthreads();                                // the last stage's MFMAs are done
+    store_stage(kb);
+    __syncthreads();
+    if (kb + KB < kb1) load_stage(kb + KB);         // uniform over the workgroup
     // ---- MFMA over the stage's blocks
     const int nblk = (kb1 - kb < KB) ? kb1 - kb : KB;
     for (int bb = 0; bb < nblk; ++bb) {
