@@ -146,7 +146,8 @@ size_t mm_mul_mat_q4_0_group_workspace_size(int count, const int64_t* Ns, int64_
  *   about 1e-6).  M > 16: src1 is rounded to binary16 for the f16 MFMA
  *   (relative effect about 1e-4).  Both inside the 1e-3 bound of this kind.
  *   ws: mm_mul_mat_workspace_size(MM_TYPE_F16, ...) bytes (0 when that is
- *   0); at 2 <= M <= 16 it holds split-K partial sums.
+ *   0); at 2 <= M <= 16 it holds split-K partial sums, at M > 16 src1 as
+ *   binary16 (converted once per call).
  */
 int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst,
                        int64_t M, int64_t N, int64_t K,

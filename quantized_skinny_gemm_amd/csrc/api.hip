@@ -130,7 +130,7 @@ int mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* 
     case KK_F_MMA: return run_f_mma(p, type, src0, src1, dst, M, N, K, ws, s);
     case KK_F16_WIDE:
       return hip_status(launch_f16_wide(p, (const uint16_t*)src0, src1, dst, (int)M, (int)N,
-                                        (int)K, s));
+                                        (int)K, ws, s));
     default: return MM_ERR_ARG;
   }
 }

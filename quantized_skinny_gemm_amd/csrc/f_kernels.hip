@@ -265,9 +265,29 @@ void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* _
 constexpr int KS = kF16WideKS;       // k per stage
 constexpr int HP = KS + 8;           // halves per LDS row (pad)
 
+// src1 -> binary16 (round to nearest even), [M][K] as given; the wide
+// kernel's A operand.  Four values per thread when src1 is 16-byte aligned
+// and the count a multiple of four.
+template <bool kVec>
+__global__ __launch_bounds__(256) void k_f32_to_f16(const float* __restrict__ x,
+                                                    uint16_t* __restrict__ y, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  if (kVec) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; 4 * i < n; i += stride) {
+      const float4 f = reinterpret_cast<const float4*>(x)[i];
+      v4h hv;
+      hv.x = (_Float16)f.x; hv.y = (_Float16)f.y; hv.z = (_Float16)f.z; hv.w = (_Float16)f.w;
+      reinterpret_cast<v4h*>(y)[i] = hv;
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+      y[i] = (uint16_t)f32_to_f16_bits(x[i]);
+  }
+}
+
 template <int BM, int BN, bool kVec>
 __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w,
-                                                  const float* __restrict__ x,
+                                                  const uint16_t* __restrict__ xh,
                                                   float* __restrict__ dst, int M, int N, int K,
                                                   int tiles_m, int tiles_n) {
   constexpr int WTM = BM / 2, WTN = BN / 2;
@@ -288,45 +308,74 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = v16f{};
 
-  for (int k0 = 0; k0 < K; k0 += KS) {
-    __syncthreads();
-    // src1 tile: BM x KS floats -> binary16 (round to nearest even)
-    for (int i = tid; i < BM * (KS / 4); i += 256) {
-      const int r = i / (KS / 4), c = i % (KS / 4);
-      const int m = m0 + r, k = k0 + 4 * c;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (m < M) {
-        if (kVec && k + 4 <= K) {
-          const float4 f = *reinterpret_cast<const float4*>(x + (int64_t)m * K + k);
-          v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? x[(int64_t)m * K + k + e] : 0.0f;
-        }
-      }
-      v4h hv;
-      hv.x = (_Float16)v[0]; hv.y = (_Float16)v[1]; hv.z = (_Float16)v[2]; hv.w = (_Float16)v[3];
-      *reinterpret_cast<v4h*>(sA + r * HP + 4 * c) = hv;
+  // Register prefetch: the next stage's pieces of 8 halves of src1 (binary16,
+  // converted beforehand) and src0 are loaded before the current stage's
+  // MFMAs; loads are unconditional with clamped addresses, and what lies
+  // outside the matrices is zeroed when the registers go to LDS.
+  constexpr int XI = BM * (KS / 8) / 256, WI = BN * (KS / 8) / 256;
+  static_assert(XI * 256 == BM * (KS / 8) && WI * 256 == BN * (KS / 8), "whole items per thread");
+  uint4 xr[XI], wr[WI];
+  auto load8 = [&](const uint16_t* base, int row, int k) -> uint4 {
+    if (kVec) {
+      const int kk = k < K ? k : 0;                  // K % 8 == 0: k < K means k + 8 <= K
+      const v4i v = *(const __attribute__((address_space(1))) v4i*)(base + (int64_t)row * K + kk);
+      return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
     }
-    // src0 tile: BN x KS halves
-    for (int i = tid; i < BN * (KS / 8); i += 256) {
+    uint32_t hw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hw[e] = base[(int64_t)row * K + (k + e < K ? k + e : 0)];
+    return make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16),
+                      hw[6] | (hw[7] << 16));
+  };
+  auto mask8 = [&](uint4 v, bool okrow, int k) -> uint4 {
+    if (kVec) {
+      const bool ok = okrow && k < K;
+      return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+    }
+    uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = (okrow && k + 2 * e < K) ? (d[e] & 0xffffu) : 0u;
+      const uint32_t hi = (okrow && k + 2 * e + 1 < K) ? (d[e] >> 16) : 0u;
+      d[e] = lo | (hi << 16);
+    }
+    return make_uint4(d[0], d[1], d[2], d[3]);
+  };
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < XI; ++u) {
+      const int i = tid + 256 * u;
       const int r = i / (KS / 8), c = i % (KS / 8);
-      const int n = n0 + r, k = k0 + 8 * c;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (n < N) {
-        if (kVec && k + 8 <= K) {
-          u = *reinterpret_cast<const uint4*>(w + (int64_t)n * K + k);
-        } else {
-          uint32_t hw[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) hw[e] = (k + e < K) ? w[(int64_t)n * K + k + e] : 0u;
-          u = make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16),
-                         hw[6] | (hw[7] << 16));
-        }
-      }
-      *reinterpret_cast<uint4*>(sB + r * HP + 8 * c) = u;
+      xr[u] = load8(xh, m0 + r < M ? m0 + r : M - 1, k0 + 8 * c);
     }
+#pragma unroll
+    for (int u = 0; u < WI; ++u) {
+      const int i = tid + 256 * u;
+      const int r = i / (KS / 8), c = i % (KS / 8);
+      wr[u] = load8(w, n0 + r < N ? n0 + r : N - 1, k0 + 8 * c);
+    }
+  };
+  auto store = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < XI; ++u) {
+      const int i = tid + 256 * u;
+      const int r = i / (KS / 8), c = i % (KS / 8);
+      *reinterpret_cast<uint4*>(sA + r * HP + 8 * c) = mask8(xr[u], m0 + r < M, k0 + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < WI; ++u) {
+      const int i = tid + 256 * u;
+      const int r = i / (KS / 8), c = i % (KS / 8);
+      *reinterpret_cast<uint4*>(sB + r * HP + 8 * c) = mask8(wr[u], n0 + r < N, k0 + 8 * c);
+    }
+  };
+
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += KS) {
+    __syncthreads();                                 // the last stage's MFMAs are done
+    store(k0);
     __syncthreads();
+    if (k0 + KS < K) load(k0 + KS);                  // uniform over the workgroup
 #pragma unroll
     for (int s = 0; s < KS / 16; ++s) {
       v8h A[WM], B[WN];
@@ -391,16 +440,24 @@ hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* 
 }
 
 hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, float* dst, int M,
-                           int N, int K, hipStream_t s) {
-  const bool vec = (K % 8 == 0) && ((uintptr_t)w % 16 == 0) && ((uintptr_t)x % 16 == 0);
+                           int N, int K, void* ws, hipStream_t s) {
+  // src1 -> binary16 into the workspace, then the tiled product
+  uint16_t* xh = reinterpret_cast<uint16_t*>((uint8_t*)ws + p.off_ah);
+  const int64_t n = (int64_t)M * K;
+  const bool cvec = (uintptr_t)x % 16 == 0 && n % 4 == 0;
+  int64_t cgrid = ((cvec ? n / 4 : n) + 255) / 256;
+  if (cgrid > 4096) cgrid = 4096;
+  if (cvec) hipLaunchKernelGGL((k_f32_to_f16<true>), dim3((unsigned)cgrid), dim3(256), 0, s, x, xh, n);
+  else hipLaunchKernelGGL((k_f32_to_f16<false>), dim3((unsigned)cgrid), dim3(256), 0, s, x, xh, n);
+  const bool vec = (K % 8 == 0) && ((uintptr_t)w % 16 == 0);    // xh is 256-byte aligned
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
   if (p.bm == 128) {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<128, 128, false>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<128, 128, false>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
   } else {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<64, 64, false>), grid, dim3(256), 0, s, w, x, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<64, 64, false>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
   }
   return hipGetLastError();
 }

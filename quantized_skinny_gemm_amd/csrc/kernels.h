@@ -60,8 +60,9 @@ hipError_t launch_q4_mma(const Plan& p, const Q4Args& a, hipStream_t s);
 
 hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* x, float* dst,
                            int M, int N, int K, hipStream_t s);
-hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, float* dst,
-                           int M, int N, int K, hipStream_t s);
+// src1 is converted to binary16 into ws + p.off_ah ([M][K]) first.
+hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, float* dst, int M,
+                           int N, int K, void* ws, hipStream_t s);
 // Skinny F16 / F32 MFMA kernel; needs f_mma_aligned() (src0 16-byte aligned,
 // K a multiple of 8 (F16) or 4 (F32)).  out = dst (one K slice) or the
 // partials [split][M][N].

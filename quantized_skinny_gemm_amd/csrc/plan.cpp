@@ -220,6 +220,10 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       p->tiles_n = ceil_div(N, p->bn);
     }
     p->kchunk = K;
+    // src1 as binary16 [M][K], converted once (not per tile and stage)
+    p->off_ah = 0;
+    p->ws_bytes = align_up((size_t)M * (size_t)K * 2, 256);
+    return MM_OK;
   }
   p->ws_bytes = 0;
   return MM_OK;

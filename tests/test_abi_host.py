@@ -162,6 +162,9 @@ def test_dispatch_threshold_and_workspace(m):
             assert frows == 16 and fcols == 8
             assert flaunch == 1 + (1 if fsplit > 1 else 0)
             assert qs.workspace_size(t, m, 4096, 4096) >= (fsplit * m * 4096 * 4 if fsplit > 1 else 0)
+        elif fv == 2:
+            # the wide F16 kernel converts src1 to binary16 in the workspace
+            assert fsplit == 1 and qs.workspace_size(t, m, 4096, 4096) >= m * 4096 * 2
         else:
             assert fsplit == 1 and qs.workspace_size(t, m, 4096, 4096) == 0
 
