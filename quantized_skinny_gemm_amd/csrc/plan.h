@@ -22,7 +22,8 @@ constexpr int kQ8Bytes = 34;       // bytes per Q8_0 block
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kWideI8KB = 4;       // Q4_0 blocks per LDS stage, int8 wide kernel
 constexpr int kWide16KB = 8;       // Q4_0 blocks per LDS stage, fp16 wide kernel
-constexpr int kWide16MaxM = 128;   // largest M the fp16 wide kernel takes by default
+constexpr int kWide16MaxM = 0;     // largest M the fp16 wide kernel takes by default (none: the
+                                   // int8 wide kernel with register prefetch is faster at every M)
 constexpr int kF16WideKS = 64;     // k elements per LDS stage in the f16 wide kernel
 constexpr int kFmSubF16 = 512;     // skinny F16 MFMA kernel: k per LDS sub-slice (16 MFMA steps)
 constexpr int kFmSubF32 = 256;     // skinny F32 MFMA kernel: k per LDS sub-slice

@@ -140,7 +140,7 @@ def test_dispatch_threshold_and_workspace(m):
     # M <= 2: narrow kernel with INIT fused (one launch); up to 32 src1 rows:
     # the skinny MFMA kernel; beyond: the wide kernel.  Both of the latter
     # run INIT first, and a split adds the reduce kernel.
-    want = 1 if m <= 2 else 3 if m <= 32 else 4 if m <= 128 else 2
+    want = 1 if m <= 2 else 3 if m <= 32 else 2
     assert variant == want
     assert launches == (0 if m <= 2 else 1) + 1 + (1 if split > 1 else 0)
     assert split >= 1
@@ -177,7 +177,7 @@ def test_split_k_when_grid_is_small():
     assert qs.workspace_size(Q4, 32, 64, 14336) >= split * 32 * 64 * 4
     # the wide kernels too
     v, split, _, _, _ = qs.dispatch(Q4, 64, 64, 14336)
-    assert v == 4 and split > 1
+    assert v == 2 and split > 1
     v, split, _, _, _ = qs.dispatch(Q4, 256, 64, 14336)
     assert v == 2 and split > 1
     # large grids do not split
