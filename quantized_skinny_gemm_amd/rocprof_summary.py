@@ -4,6 +4,11 @@
         Per-kernel table from DIR's *_kernel_stats.csv (calls, average and
         total duration), as markdown.
 
+    python -m quantized_skinny_gemm_amd.rocprof_summary shapes DIR [--only SUBSTR]
+        Per (kernel, grid) table from DIR's *_kernel_trace.csv: the same
+        kernel launched at different shapes gets one row per grid, with the
+        number of dispatches and their median and minimum duration.
+
     python -m quantized_skinny_gemm_amd.rocprof_summary traffic \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --kernel SUBSTR --copy-bytes B --source FILE --algo-bytes A --out JSON
@@ -58,6 +63,30 @@ def stats_markdown(directory: str) -> str:
         lines.append(f"| `{name}` | {d['calls']} | {d['avg_ns'] / 1e3:.3f} | "
                      f"{d['min_ns'] / 1e3:.3f} | {d['max_ns'] / 1e3:.3f} | "
                      f"{d['total_ns'] / 1e6:.3f} | {d['pct']:.2f} |")
+    return "\n".join(lines)
+
+
+def shapes_markdown(directory: str, only: str = "") -> str:
+    rows = _csv_rows(directory, "_kernel_trace.csv")
+    groups = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if only and only not in name:
+            continue
+        grid = (int(r["Grid_Size_X"]), int(r.get("Grid_Size_Y", 1) or 1),
+                int(r.get("Grid_Size_Z", 1) or 1))
+        wg = int(r["Workgroup_Size_X"]) * int(r.get("Workgroup_Size_Y", 1) or 1)
+        d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        groups.setdefault((name, grid, wg), []).append(d)
+    lines = ["| kernel | grid (threads x, y, z) | workgroup | dispatches | median us | min us |",
+             "|---|---|---:|---:|---:|---:|"]
+    for (name, grid, wg), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        ds.sort()
+        short = name.replace("|", "\\|")
+        if len(short) > 90:
+            short = short[:87] + "..."
+        lines.append(f"| `{short}` | {grid[0]} x {grid[1]} x {grid[2]} | {wg} | {len(ds)} | "
+                     f"{ds[len(ds) // 2] / 1e3:.3f} | {ds[0] / 1e3:.3f} |")
     return "\n".join(lines)
 
 
@@ -126,6 +155,9 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    sh = sub.add_parser("shapes")
+    sh.add_argument("dir")
+    sh.add_argument("--only", default="")
     t = sub.add_parser("traffic")
     for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--source", "--out"):
         t.add_argument(k, required=True)
@@ -134,6 +166,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats_markdown(args.dir))
+    elif args.cmd == "shapes":
+        print(shapes_markdown(args.dir, args.only))
     else:
         res = traffic(args)
         with open(args.out, "w") as fh:
