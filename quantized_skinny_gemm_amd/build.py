@@ -31,6 +31,9 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # packed fp32 VALU ops stay disabled (no v_pk_*_f32 in any kernel)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the scale epilogues read every output
+    # register, and an accumulation-register result costs one extra move each
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]
