@@ -1,4 +1,6 @@
-// Wide-M Q4_0 x Q8_0 product for gfx950 on fp16 MFMA (batches of 33..128 rows).
+// Wide-M Q4_0 x Q8_0 product for gfx950 on fp16 MFMA with exact block dots
+// (an alternative to the int8 wide kernel, reached through the debug variant 4:
+// the int8 kernel, which prefetches its stages, is faster at the measured M).
 //
 // Past the skinny kernels' range the product is a dense contraction (the
 // first-token / prefill regime, arXiv 2407.07304 section 2.2).  Every block

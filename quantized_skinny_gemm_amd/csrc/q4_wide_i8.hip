@@ -1,4 +1,5 @@
-// Wide-M Q4_0 x Q8_0 product for gfx950 on int8 MFMA (the larger batches).
+// Wide-M Q4_0 x Q8_0 product for gfx950 on int8 MFMA (every M past the skinny
+// kernel, M > 32).
 //
 // Past the narrow kernel's threshold the product is a dense contraction (the
 // first-token / prefill regime, arXiv 2407.07304 section 2.2), so it runs on

@@ -195,6 +195,40 @@ def test_misaligned_src0_uses_generic_path():
         _check_q4_product(view, wq, x, "misaligned", v, (0, 8))
 
 
+@pytest.mark.parametrize("m", [5, 40])
+def test_misaligned_f16_f32_operands(m):
+    """src0 and src1 off their 16-byte alignment (src0 by 2 bytes for F16, by 4 for
+    F32; src1 by 4): the skinny MFMA kernel falls back to the narrow one, the wide
+    F16 kernel and its src1 conversion take their element-wise paths."""
+    import torch
+    qs = _qs()
+    rng = np.random.default_rng(77 + m)
+    n, k = 200, 1024
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    wh = w.astype(np.float16)
+    say("misaligned f", m, n, k)
+    xb = torch.zeros(m * k + 4, dtype=torch.float32, device="cuda")
+    xv = xb[1:1 + m * k].view(m, k)
+    xv.copy_(torch.from_numpy(x).cuda())
+    assert xv.data_ptr() % 16 == 4
+    hb = torch.zeros(n * k + 8, dtype=torch.float16, device="cuda")
+    hv = hb[1:1 + n * k].view(n, k)
+    hv.copy_(torch.from_numpy(wh).cuda())
+    assert hv.data_ptr() % 16 == 2
+    fb = torch.zeros(n * k + 4, dtype=torch.float32, device="cuda")
+    fv = fb[1:1 + n * k].view(n, k)
+    fv.copy_(torch.from_numpy(w).cuda())
+    assert fv.data_ptr() % 16 == 4
+    assert_close(to_host(qs.mul_mat_f16_f32(hv, xv)), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, "f16")
+    assert_close(to_host(qs.mul_mat_f32(fv, xv)), mul_mat.mul_mat_f32(w, x), TOL_F, "f32")
+    # aligned weights, misaligned src1 only
+    assert_close(to_host(qs.mul_mat_f16_f32(to_dev(wh), xv)), mul_mat.mul_mat_f16_f32(wh, x), TOL_F,
+                 "f16 aligned src0")
+    assert_close(to_host(qs.mul_mat_f32(to_dev(w), xv)), mul_mat.mul_mat_f32(w, x), TOL_F,
+                 "f32 aligned src0")
+
+
 @pytest.mark.parametrize("m,n,k", [(1, 1, 1), (2, 33, 7), (5, 100, 1000), (16, 129, 257),
                                    (17, 70, 300), (40, 300, 64), (130, 129, 200)])
 def test_ragged_shapes_f16_f32(m, n, k):
