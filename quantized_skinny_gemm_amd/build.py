@@ -22,8 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqsgemm.so")
 
-HIP_SOURCES = ["api.hip", "quantize.hip", "q4_narrow.hip", "q4_mma.hip", "q4_wide_i8.hip",
-               "q4_wide16.hip", "f_kernels.hip"]
+HIP_SOURCES = ["api.hip", "quantize.hip", "q4_narrow.hip", "q4_mma.hip", "q4_skinny.hip",
+               "q4_wide_i8.hip", "q4_wide16.hip", "f_kernels.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 ARCH = "gfx950"

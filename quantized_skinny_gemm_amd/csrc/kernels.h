@@ -20,12 +20,22 @@ hipError_t launch_quantize_q8_0(const float* x, int64_t nrows, int64_t k, uint8_
 hipError_t launch_quantize_q4_0(const float* x, int64_t nrows, int64_t k, uint8_t* y,
                                 hipStream_t s);
 
+// INIT for the skinny MFMA kernel: the internal wdata (wq, wd, wb as above)
+// and the same codes and scales in that kernel's operand order (sq, ss) over
+// `rows` x `phases` * 8 blocks, zero past nrows and k.
+hipError_t launch_quantize_q8_0_skinny(const float* x, int64_t nrows, int64_t k, int8_t* wq,
+                                       float* wd, int32_t* wb, uint8_t* sq, float* ss,
+                                       int64_t rows, int64_t phases, hipStream_t s);
+
 struct Q4Args {
   const uint8_t* w;      // Q4_0 src0
   const int8_t* aq;      // wdata codes
   const float* ad;       // wdata scales
   const int32_t* ab;     // wdata -8*sum(q)
   const uint16_t* ah;    // wdata codes as binary16 (wide kernel; NULL otherwise)
+  const uint8_t* sq;     // skinny kernel: codes in operand order (NULL otherwise)
+  const float* ss;       // skinny kernel: scales in operand order
+  int sk_phases;         // skinny kernel: phases of 8 blocks per row
   float* dst;
   float* part;           // split-K partials [split][M][N]
   int M, N, K;
@@ -54,8 +64,11 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
 // block dots (reads a.ah).
 hipError_t launch_q4_wide_i8(const Plan& p, const Q4Args& a, hipStream_t s);
 hipError_t launch_q4_wide16(const Plan& p, const Q4Args& a, hipStream_t s);
-// Skinny MFMA kernel: reads the wdata in a (INIT must have run), writes a.dst
-// or, when p.split > 1, the partials in a.part.
+// Skinny MFMA kernel: reads the wdata in a (INIT must have run), writes
+// a.dst.  16-row workgroups when K % 64 == 0 and src0 is 4-byte aligned
+// (q4_skinny_ok); otherwise the 32-row kernel with LDS-staged chunks.
+bool q4_skinny_ok(int K, const void* w);
+hipError_t launch_q4_skinny(const Plan& p, const Q4Args& a, hipStream_t s);
 hipError_t launch_q4_mma(const Plan& p, const Q4Args& a, hipStream_t s);
 
 hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* x, float* dst,

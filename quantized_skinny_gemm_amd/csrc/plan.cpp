@@ -57,31 +57,44 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     const bool mma = variant == 3 || (variant == 0 && M > kFuseMaxM && M <= kMmaMaxM);
     const bool narrow = !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
     const bool wide16 = variant == 4 || (variant == 0 && M > kMmaMaxM && M <= kWide16MaxM);
+    // wdata: codes, scales, bias; the codes and scales are followed by 256
+    // spare bytes (the skinny kernel's last phase may read up to 7 blocks past
+    // the end, and drops them)
     size_t off = 0;
-    p->off_aq = off; off = align_up(off + (size_t)M * (size_t)K, 256);
-    p->off_ad = off; off = align_up(off + (size_t)M * (size_t)nb * 4, 256);
+    p->off_aq = off; off = align_up(off + (size_t)M * (size_t)K + 256, 256);
+    p->off_ad = off; off = align_up(off + (size_t)M * (size_t)nb * 4 + 256, 256);
     p->off_ab = off; off = align_up(off + (size_t)M * (size_t)nb * 4, 256);
     if (mma) {
+      // 16-row workgroups whose waves split K among themselves (no split
+      // across workgroups, so no partial sums in the workspace); passes of
+      // 16 or 32 src1 rows.
       p->kind = KK_Q4_MMA;
       p->variant = 3;
-      p->mt = M <= 8 ? 8 : M <= 16 ? 16 : 32;
-      p->waves = kMmaWaves;
+      p->mt = M <= 16 ? 16 : 32;
       p->tiles_m = ceil_div(M, p->mt);
-      p->tiles_n = ceil_div(N, 32);
-      // Split K across workgroups while the 32-row tiles do not give every
-      // CU a workgroup; at least one 32-block chunk per split.
-      const int64_t wgs = p->tiles_m * p->tiles_n;
-      int64_t split = 1;
-      if (allow_split && wgs < kCUs) {
-        split = ceil_div(kCUs, wgs);
-        const int64_t max_split = nb / 32 > 1 ? nb / 32 : 1;
-        if (split > max_split) split = max_split;
-        if (split > 16) split = 16;
-      }
-      int64_t kc = ceil_div(nb, split);
-      kc = ceil_div(kc, 8) * 8;                        // chunk starts stay 16-byte aligned
-      p->kchunk = kc;
-      p->split = (int)ceil_div(nb, kc);
+      p->tiles_n = ceil_div(N, 16);
+      p->split = 1;
+      // Waves per workgroup: enough workgroups x waves for about 16 waves
+      // per CU, each wave keeping at least one phase of block pairs; two m
+      // tiles hold twice the operands, so at most 8 waves (2 per SIMD, up
+      // to 256 registers each).
+      const int wmax = p->mt == 16 ? 16 : 8;
+      const int64_t tiles = p->tiles_m * p->tiles_n;
+      int w = 4;
+      while (w < wmax && tiles * w < 16 * kCUs && nb / 2 >= 2 * w * kSkinnyPairs) w *= 2;
+      p->waves = w;
+      // block pairs per wave: whole phases, so that every wave's phases
+      // start on a phase of the operand-order wdata
+      const int64_t pairs = nb / 2;
+      p->kchunk = ceil_div(ceil_div(pairs, w), kSkinnyPairs) * kSkinnyPairs;
+      // INIT also writes the codes and scales in the kernel's operand order:
+      // per 16-row tile and phase of 8 blocks, 4 KB of codes (lane l of pair
+      // j at 1024 j + 16 l) and 16 x 8 scales; padding rows and blocks are
+      // zero.
+      p->sk_rows = p->tiles_m * p->mt;
+      p->sk_phases = ceil_div(nb, 2 * kSkinnyPairs);
+      p->off_sq = off; off = align_up(off + (size_t)p->sk_rows * p->sk_phases * 256, 256);
+      p->off_ss = off; off = align_up(off + (size_t)p->sk_rows * p->sk_phases * 32, 256);
     } else if (narrow) {
       p->kind = KK_Q4_NARROW;
       p->variant = 1;

@@ -34,7 +34,9 @@ constexpr int kFuseMaxM = 2;       // narrow Q4_0 passes of at most this many ro
 constexpr int kNarrowMaxLds = 65536; // LDS bytes the narrow kernel may stage activations in
 constexpr int kNarrowMaxGrid = 512;  // narrow workgroups along N (2 per CU)
 constexpr int kMmaMaxM = 32;       // largest M the skinny MFMA kernel takes by default
-constexpr int kMmaWaves = 8;       // waves per skinny MFMA workgroup (they split K)
+constexpr int kSkinnyPairs = 4;    // skinny kernel: block pairs per wave phase
+constexpr int kMmaWaves = 8;       // waves per workgroup of the skinny kernel for unaligned
+                                   // weights or K % 64 != 0 (32 rows per workgroup)
 
 enum KernelKind {
   KK_NONE = 0,      // nothing to do (M == 0 or N == 0)
@@ -43,7 +45,7 @@ enum KernelKind {
   KK_Q4_WIDE = 3,
   KK_F_NARROW = 4,  // f16 or f32 src0
   KK_F16_WIDE = 5,
-  KK_Q4_MMA = 6,    // skinny Q4_0 on int8 MFMA (32 weight rows per workgroup)
+  KK_Q4_MMA = 6,    // skinny Q4_0 on int8 MFMA (16 weight rows per workgroup)
   KK_Q4_WIDE16 = 7, // wide Q4_0 on fp16 MFMA with exact block dots
   KK_F_MMA = 8,     // skinny F16 / F32 on the 16x16 MFMA (passes of 16 src1 rows)
 };
@@ -55,7 +57,7 @@ struct Plan {
   // narrow kernels
   int mt = 1;               // src1 rows per pass (compile-time tile)
   int rpw = 1;              // src0 rows per wave
-  int waves = 4;            // waves per workgroup
+  int waves = 4;            // waves per workgroup (skinny MFMA: they split K)
   // wide kernels
   int bm = 0, bn = 0, waves_m = 0, waves_n = 0;
   // grid
@@ -68,6 +70,10 @@ struct Plan {
   // workspace layout (bytes)
   size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0;
   size_t off_ah = 0;        // wide kernel: Q8_0 codes as binary16 [M][K] (0: not written)
+  size_t off_sq = 0, off_ss = 0;   // skinny MFMA kernel: its operand-order codes and scales
+                                   // (0: not written)
+  int64_t sk_rows = 0;      // skinny layout: src1 rows padded to 16-row tiles
+  int64_t sk_phases = 0;    // skinny layout: phases of 8 blocks (K padded to 256)
   size_t ws_bytes = 0;
 };
 

@@ -346,10 +346,15 @@ hipError_t launch_mt(const Plan& p, const Q4Args& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_q4_mma(const Plan& p, const Q4Args& a, hipStream_t s) {
-  if (p.waves != kMmaWaves) return hipErrorInvalidValue;
-  if (p.mt == 8) return launch_mt<8>(p, a, s);
-  if (p.mt == 16) return launch_mt<16>(p, a, s);
-  if (p.mt == 32) return launch_mt<32>(p, a, s);
+  // 32 weight rows per workgroup, the whole K range (the plan splits none)
+  if (p.split != 1) return hipErrorInvalidValue;
+  Plan q = p;
+  const int nb = a.K / 32;
+  q.tiles_n = (a.N + 31) / 32;
+  q.kchunk = (nb + 7) / 8 * 8;
+  if (q.mt == 8) return launch_mt<8>(q, a, s);
+  if (q.mt == 16) return launch_mt<16>(q, a, s);
+  if (q.mt == 32) return launch_mt<32>(q, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,271 @@
+// Skinny Q4_0 x Q8_0 product on the 16 x 16 int8 matrix cores, for batches
+// of a few src1 rows (2 < M <= 32 per pass).
+//
+// dst[m][n] = sum_b f32(d_w[n][b]) * f32(d_a[m][b]) * S_b[m][n],
+// S_b = sum_j (q4 - 8) * q8 (int32).
+//
+// With a few src1 rows the product is still bound by reading each weight
+// once (arXiv 2407.07304, section 2.2; DeepSpeed-Inference notes, III.A),
+// but per weight byte it does M times the dot-product work of the M = 1
+// kernel, so the block dots go to the matrix cores:
+// v_mfma_i32_16x16x32_i8 has K = 32, one Q4_0 / Q8_0 block, so every MFMA
+// output is one block dot and takes one scale pair.
+//
+//   * A workgroup owns 16 weight rows (the MFMA's rows); its W waves split
+//     their K range (each a contiguous run of block pairs), so that a large
+//     grid of small, equal shares keeps every CU's loads in flight, and add
+//     their partial tiles in LDS at the end in a fixed order (DeepSpeed-
+//     Inference notes, III.C: partial sums reduced on chip).
+//   * A wave walks its run in phases of 4 block pairs.  A phase's 16 rows x
+//     4 pairs x 36 bytes are loaded one unit (a row's block pair) per lane,
+//     consecutive lanes on consecutive bytes of a row: loading the MFMA
+//     operands straight from memory would give each instruction 16 partly
+//     used rows and reads far slower.  The units are reordered through a
+//     small LDS patch private to the wave (no workgroup barrier), and the
+//     next phase's loads are in flight while one phase is computed.
+//   * Lane (row i = l % 16, group g = l / 16) of the A operand takes code
+//     bytes 4g .. 4g+3 of its row's block: their low nibbles are elements
+//     4g .. 4g+3, their high nibbles elements 16+4g .. 19+4g, and the B
+//     operand (the Q8_0 codes of src1 row l % 16) holds the same elements.
+//     Nibbles become signed bytes 16 * (q - 8) with one xor and two masks
+//     ((q ^ 8) << 4 read as a signed byte is 16 (q - 8)), so the MFMA ends
+//     at 16 S_b exactly and no bias term is needed; the 1/16 joins the
+//     weight scale (exact: a power of two).
+//   * Output lane l holds src1 row l % 16 and weight rows 4 (l / 16) + r:
+//     one activation scale per lane and block, four weight scales (read
+//     from LDS, where the lanes that decoded them left them).  Epilogue per
+//     output and block: acc += f32(16 S_b) * (d_a * d_w / 16).
+#include "device.h"
+#include "kernels.h"
+
+namespace qsg {
+
+namespace {
+
+constexpr int kPH = kSkinnyPairs;        // block pairs per phase (16 rows x 4 = 64 units)
+constexpr int kRP = kPH * 36 + 4;        // LDS row pitch: 37 dwords, odd, so rows spread the banks
+constexpr int kStageBytes = 16 * kRP;    // one wave's patch of weights
+constexpr int kScaleBytes = 2 * kPH * 16 * 4;   // its weight scales, f32 [block][row]
+
+template <int MP>
+struct Phase {
+  uint32_t w[9];              // this lane's unit: one row's block pair
+  v4i act[MP][kPH];           // B operands of pair j: blocks 2j and 2j+1
+  float da[MP][2 * kPH];      // activation scale per m tile and block
+};
+
+__device__ __forceinline__ uint32_t gload32(const void* p) {
+  return *(const __attribute__((address_space(1))) uint32_t*)p;
+}
+__device__ __forceinline__ v4i gload128(const void* p) {
+  return *(const __attribute__((address_space(1))) v4i*)p;
+}
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4f gloadf4(const float* p) {
+  return *(const __attribute__((address_space(1))) v4f*)p;
+}
+
+// One phase's loads: this lane's weight unit (clamped to the row's last
+// pair) and, per m tile, the activations in operand order as INIT laid them
+// out (4 KB of codes per tile and phase, lane l of pair j at 1024 j + 16 l;
+// then the 16 rows' 8 scales), each instruction reading 1 KB in a row.
+// Blocks past K and rows past M hold zeros there, so no block is masked.
+template <int MP>
+__device__ __forceinline__ void load_phase(Phase<MP>& P, const Q4Args& a, const uint8_t* wrow,
+                                           int j0, int pairs, int ty) {
+  const int lane = threadIdx.x & 63;
+  int pc = j0 + (lane & 3);
+  pc = pc < pairs ? pc : pairs - 1;
+  const uint8_t* wp = wrow + 36 * (int64_t)pc;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) P.w[i] = gload32(wp + 4 * i);
+  const int f = j0 / kPH;
+#pragma unroll
+  for (int t = 0; t < MP; ++t) {
+    const int64_t tp = (int64_t)(ty * MP + t) * a.sk_phases + f;
+    const uint8_t* cb = a.sq + tp * 4096 + 16 * lane;
+#pragma unroll
+    for (int j = 0; j < kPH; ++j) P.act[t][j] = gload128(cb + 1024 * j);
+    const float* sb = a.ss + (tp * 16 + (lane & 15)) * 8;
+    const v4f s0 = gloadf4(sb), s1 = gloadf4(sb + 4);
+    P.da[t][0] = s0.x; P.da[t][1] = s0.y; P.da[t][2] = s0.z; P.da[t][3] = s0.w;
+    P.da[t][4] = s1.x; P.da[t][5] = s1.y; P.da[t][6] = s1.z; P.da[t][7] = s1.w;
+  }
+}
+
+// Signed bytes 16 (q - 8) of the low and high nibbles of four code bytes.
+__device__ __forceinline__ long nibbles_x16(uint32_t q) {
+  const uint32_t x = q ^ 0x88888888u;
+  const uint32_t lo = (x << 4) & 0xF0F0F0F0u;
+  const uint32_t hi = x & 0xF0F0F0F0u;
+  return (long)(((uint64_t)hi << 32) | lo);
+}
+
+template <int MP, bool kDump>
+__device__ __forceinline__ void compute_phase(const Phase<MP>& P, float (&acc)[MP][4],
+                                              uint8_t* stage, float* sdw, int j0, int j1,
+                                              int n0, int m0, const Q4Args& a) {
+  const int lane = threadIdx.x & 63;
+  const int i16 = lane & 15, g = lane >> 4;
+  {
+    // this lane's unit -> row lane / 4, pair lane % 4 of the patch
+    uint32_t* d = reinterpret_cast<uint32_t*>(stage + (lane >> 2) * kRP + 36 * (lane & 3));
+#pragma unroll
+    for (int i = 0; i < 9; ++i) d[i] = P.w[i];
+  }
+  // LDS operations of one wave complete in order: the reads below see the
+  // writes above, and the next phase's writes come after these reads.
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(stage + i16 * kRP);
+  const int nb = a.K / 32;
+#pragma unroll
+  for (int jj = 0; jj < kPH; ++jj) {
+    const int pair = j0 + jj;
+    const bool live = pair < j1;                   // for the dump (uniform over the wave)
+    const uint32_t* u = row + 9 * jj;
+    const uint32_t d0 = u[0], d4 = u[4];
+    const uint32_t qe = __builtin_amdgcn_alignbit(u[g + 1], u[g], 16);   // even block
+    const uint32_t qo = u[5 + g];                                      // odd block
+    // weight scales / 16 of row i16, blocks 2jj and 2jj+1 of the phase (the
+    // four lanes of a row store the same values; no branch)
+    sdw[(2 * jj) * 16 + i16] = f16_bits_to_f32(d0) * 0.0625f;
+    sdw[(2 * jj + 1) * 16 + i16] = f16_bits_to_f32(d4 >> 16) * 0.0625f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kb = 2 * jj + h;
+      const long A = nibbles_x16(h ? qo : qe);
+      const float4 dw = *reinterpret_cast<const float4*>(sdw + kb * 16 + 4 * g);
+#pragma unroll
+      for (int t = 0; t < MP; ++t) {
+        const v4i& ac = P.act[t][jj];
+        const long B = h ? (long)(((uint64_t)(uint32_t)ac.w << 32) | (uint32_t)ac.z)
+                         : (long)(((uint64_t)(uint32_t)ac.y << 32) | (uint32_t)ac.x);
+        const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const float da = P.da[t][kb];
+        acc[t][0] = fmaf((float)D.x, da * dw.x, acc[t][0]);
+        acc[t][1] = fmaf((float)D.y, da * dw.y, acc[t][1]);
+        acc[t][2] = fmaf((float)D.z, da * dw.z, acc[t][2]);
+        acc[t][3] = fmaf((float)D.w, da * dw.w, acc[t][3]);
+        if (kDump && live) {
+          const int m = m0 + 16 * t + i16;
+          const int b = 2 * pair + h;
+          const int Dv[4] = {D.x, D.y, D.z, D.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = n0 + 4 * g + r;
+            if (m < a.M && n >= a.n0 && n < a.n1)
+              a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + b] = Dv[r] / 16;
+          }
+        }
+      }
+    }
+    // one block pair's operands and results live at a time (the registers
+    // hold the next phase's loads instead)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int MP, int W, bool kDump>
+__global__ __launch_bounds__(64 * W)
+void k_q4_skinny(Q4Args a, int pp) {
+  // pp: block pairs per wave, a multiple of the phase (kPH pairs)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nb = a.K / 32, pairs = nb / 2;
+  const int64_t rb = (int64_t)nb * 18;
+  const int n0 = blockIdx.x * 16, ty = blockIdx.y, m0 = ty * 16 * MP;
+  // this wave's block pairs [j0w, j1w)
+  const int j0w = wave * pp < pairs ? wave * pp : pairs;
+  const int j1w = j0w + pp < pairs ? j0w + pp : pairs;
+  const int nph = (j1w - j0w + kPH - 1) / kPH;
+  uint8_t* stage = smem + wave * (kStageBytes + kScaleBytes);
+  float* sdw = reinterpret_cast<float*>(stage + kStageBytes);
+  int nrow = n0 + (lane >> 2);
+  nrow = nrow < a.N ? nrow : a.N - 1;
+  const uint8_t* wrow = a.w + nrow * rb;
+
+  float acc[MP][4];
+#pragma unroll
+  for (int t = 0; t < MP; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+
+  // Two register sets; every load in the loop is unconditional, and the
+  // last one or two phases are computed after it.
+  // (The scheduling barriers keep the loads of one set from being hoisted
+  // above the computation of the other, which would hold three sets.)
+  Phase<MP> P0, P1;
+  if (nph > 0) load_phase<MP>(P0, a, wrow, j0w, pairs, ty);
+  int f = 0;
+  for (; f + 2 < nph; f += 2) {
+    load_phase<MP>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase<MP, kDump>(P0, acc, stage, sdw, j0w + f * kPH, j1w, n0, m0, a);
+    __builtin_amdgcn_sched_barrier(0);
+    load_phase<MP>(P0, a, wrow, j0w + (f + 2) * kPH, pairs, ty);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase<MP, kDump>(P1, acc, stage, sdw, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (f + 1 < nph) {
+    load_phase<MP>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase<MP, kDump>(P0, acc, stage, sdw, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase<MP, kDump>(P1, acc, stage, sdw, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+  } else if (f < nph) {
+    compute_phase<MP, kDump>(P0, acc, stage, sdw, j0w + f * kPH, j1w, n0, m0, a);
+  }
+
+  // ---- add the W waves' partial tiles in a fixed order (LDS reused)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int t = 0; t < MP; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((wave * MP + t) * 4 + r) * 64 + lane] = acc[t][r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MP * 256; idx += 64 * W) {
+    const int t = idx >> 8, r = (idx >> 6) & 3, l = idx & 63;
+    float s = 0.0f;
+    for (int w2 = 0; w2 < W; ++w2) s += red[((w2 * MP + t) * 4 + r) * 64 + l];
+    const int m = m0 + 16 * t + (l & 15);
+    const int n = n0 + 4 * (l >> 4) + r;
+    if (m < a.M && n < a.N) a.dst[(int64_t)m * a.N + n] = s;
+  }
+}
+
+template <int MP, int W>
+hipError_t launch_w(const Plan& p, const Q4Args& a, int pp, hipStream_t s) {
+  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1u);
+  const size_t stage = (size_t)W * (kStageBytes + kScaleBytes);
+  const size_t red = (size_t)W * MP * 4 * 64 * 4;
+  const size_t lds = stage > red ? stage : red;
+  if (a.dots) hipLaunchKernelGGL((k_q4_skinny<MP, W, true>), grid, dim3(64 * W), lds, s, a, pp);
+  else hipLaunchKernelGGL((k_q4_skinny<MP, W, false>), grid, dim3(64 * W), lds, s, a, pp);
+  return hipGetLastError();
+}
+
+template <int MP>
+hipError_t launch_mp(const Plan& p, const Q4Args& a, hipStream_t s) {
+  const int pp = (int)p.kchunk;                     // block pairs per wave
+  if (!a.sq || pp % kPH) return hipErrorInvalidValue;
+  if (p.waves == 4) return launch_w<MP, 4>(p, a, pp, s);
+  if (p.waves == 8) return launch_w<MP, 8>(p, a, pp, s);
+  if (p.waves == 16 && MP == 1) return launch_w<MP, 16>(p, a, pp, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool q4_skinny_ok(int K, const void* w) {
+  return K % 64 == 0 && (uintptr_t)w % 4 == 0;
+}
+
+hipError_t launch_q4_skinny(const Plan& p, const Q4Args& a, hipStream_t s) {
+  if (p.split != 1 || !q4_skinny_ok(a.K, a.w)) return hipErrorInvalidValue;
+  if (p.mt == 16) return launch_mp<1>(p, a, s);
+  if (p.mt == 32) return launch_mp<2>(p, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qsg

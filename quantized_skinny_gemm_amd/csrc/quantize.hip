@@ -130,6 +130,55 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q4_0(const float* __restr
   store_u16(b + 4 + 4 * g, bytes >> 16);
 }
 
+// INIT of the skinny MFMA kernel: the plain wdata of the real blocks, and
+// over the padded domain (rows x phases * 8 blocks; zeros past the real ones)
+// the codes and scales in that kernel's operand order.  Row m = 16 t + i,
+// block b = 8 f + 2 j + e: the 4 code bytes 4g .. 4g+3 (lane h = 0) or
+// 16+4g .. 19+4g (h = 1) go to byte 8e + 4h of the 16 bytes that lane
+// 16g + i of the MFMA loads for pair j of phase f of tile t.
+__global__ __launch_bounds__(kThreads) void k_quantize_q8_0_skinny(
+    const float* __restrict__ x, int M, int K, int phases, int64_t nblocks,
+    int8_t* __restrict__ wq, float* __restrict__ wd, int32_t* __restrict__ wb,
+    uint8_t* __restrict__ sq, float* __restrict__ ss) {
+  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t blk = gtid >> 1;                    // over the padded domain
+  const int h = threadIdx.x & 1;
+  const int nbp = 8 * phases, nb = K / 32;
+  const int m = (int)(blk / nbp), b = (int)(blk % nbp);
+  const bool active = blk < nblocks;
+  const bool real = active && m < M && b < nb;
+  float v[16];
+  if (real) {
+    const float4* p = reinterpret_cast<const float4*>(x + (int64_t)m * K + 32 * b + 16 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 f = p[i];
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+  }
+  uint32_t packed[4], dbits;
+  int sum;
+  q8_0_pair(v, packed, dbits, sum);
+  if (!active) return;
+  if (real) {
+    const int64_t pb = (int64_t)m * nb + b;
+    *reinterpret_cast<uint4*>(wq + pb * 32 + 16 * h) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    if (h == 0) {
+      wd[pb] = f16_bits_to_f32(dbits);
+      wb[pb] = -8 * sum;
+    }
+  }
+  const int t = m >> 4, i = m & 15;
+  const int f = b >> 3, kb = b & 7, j = kb >> 1, e = kb & 1;
+  uint8_t* base = sq + (((int64_t)t * phases + f) * 4 + j) * 1024 + 8 * e + 4 * h;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) *reinterpret_cast<uint32_t*>(base + 16 * (16 * g + i)) = packed[g];
+  if (h == 0) ss[(((int64_t)t * phases + f) * 16 + i) * 8 + kb] = f16_bits_to_f32(dbits);
+}
+
 int64_t grid_for(int64_t nblocks, int lanes) { return (nblocks * lanes + kThreads - 1) / kThreads; }
 
 }  // namespace
@@ -151,6 +200,17 @@ hipError_t launch_quantize_q4_0(const float* x, int64_t nrows, int64_t k, uint8_
   const int64_t grid = grid_for(nblocks, 8);
   if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL(k_quantize_q4_0, dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_q8_0_skinny(const float* x, int64_t nrows, int64_t k, int8_t* wq,
+                                       float* wd, int32_t* wb, uint8_t* sq, float* ss,
+                                       int64_t rows, int64_t phases, hipStream_t s) {
+  const int64_t nblocks = rows * phases * 8;
+  const int64_t grid = grid_for(nblocks, 2);
+  if (grid < 1) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize_q8_0_skinny, dim3((unsigned)grid), dim3(kThreads), 0, s, x,
+                     (int)nrows, (int)k, (int)phases, nblocks, wq, wd, wb, sq, ss);
   return hipGetLastError();
 }
 

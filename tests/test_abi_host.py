@@ -150,7 +150,9 @@ def test_dispatch_threshold_and_workspace(m):
     if variant == 1:
         assert rows >= m or rows == 8
     if variant == 3:
-        assert rows in (8, 16, 32) and rows >= min(m, 32) and cols == 8
+        # 16-row workgroups of 4, 8 or 16 waves, passes of 16 or 32 src1 rows
+        assert rows in (16, 32) and rows >= min(m, 32) and cols in (4, 8, 16)
+        assert split == 1
     # F16: M = 1 narrow, up to 16 rows the skinny MFMA kernel (K slices
     # through the workspace), beyond the wide kernel; F32: narrow at M = 1,
     # skinny MFMA from 2 rows
@@ -170,12 +172,15 @@ def test_dispatch_threshold_and_workspace(m):
 
 
 def test_split_k_when_grid_is_small():
-    # a narrow N at the skinny MFMA kernel must split K (and its workspace
-    # holds the partials)
-    v, split, _, _, _ = qs.dispatch(Q4, 32, 64, 14336)
-    assert v == 3 and split > 1
-    assert qs.workspace_size(Q4, 32, 64, 14336) >= split * 32 * 64 * 4
-    # the wide kernels too
+    # the skinny MFMA kernel splits K among the waves of a workgroup, never
+    # across workgroups: no partials in the workspace even for a narrow N
+    v, split, _, cols, _ = qs.dispatch(Q4, 32, 64, 14336)
+    assert v == 3 and split == 1 and cols == 8
+    # the wdata (codes, scales, bias) and its operand-order copy (codes and
+    # scales: 36 bytes per src1 row and block), nothing for partial sums
+    need = 32 * 14336 + 2 * 4 * 32 * 448 + 36 * 32 * 448
+    assert need <= qs.workspace_size(Q4, 32, 64, 14336) < need + 4096
+    # the wide kernels split across workgroups
     v, split, _, _, _ = qs.dispatch(Q4, 64, 64, 14336)
     assert v == 2 and split > 1
     v, split, _, _, _ = qs.dispatch(Q4, 256, 64, 14336)
@@ -186,17 +191,15 @@ def test_split_k_when_grid_is_small():
     assert qs.dispatch(Q4, 16, 14336, 4096)[1] == 1
 
 
-def test_skinny_mfma_split_keeps_whole_chunks():
-    # K is split across workgroups only while the 32-row tiles leave CUs
-    # idle, with at least one 32-block chunk per split and 8-block aligned
-    # split boundaries
-    for m, n, k in ((32, 14336, 4096), (32, 4096, 14336), (8, 64, 32), (16, 64, 14336)):
-        v, split, rows, _, _ = qs.dispatch(Q4, m, n, k)
-        assert v == 3
-        nb = k // 32
-        assert split == 1 or nb // split >= 24
-        if n >= 8192:
-            assert split == 1
+def test_skinny_mfma_waves_per_workgroup():
+    # waves per 16-row workgroup: about 16 waves per CU over the grid, every
+    # wave at least one phase of 4 block pairs, at most 8 waves with 32 rows
+    for m, n, k, want in ((8, 14336, 4096, 8), (16, 4096, 14336, 16), (32, 4096, 14336, 8),
+                          (16, 11008, 4096, 8), (8, 256, 512, 4), (4, 4096, 4096, 16)):
+        v, split, rows, cols, _ = qs.dispatch(Q4, m, n, k)
+        assert v == 3 and split == 1
+        assert rows == (16 if m <= 16 else 32)
+        assert cols == want, (m, n, k, cols)
 
 
 def test_workspace_size_of_invalid_shapes_is_zero():
