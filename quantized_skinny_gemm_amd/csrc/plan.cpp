@@ -71,13 +71,17 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       p->kind = KK_Q4_MMA;
       p->variant = 3;
       p->mt = M <= 16 ? 16 : 32;
+      // 16 weight rows per workgroup (and per wave).  (32, two MFMA row
+      // tiles sharing each activation load, measured no faster at 14336 rows
+      // and slower at 4096: half the workgroups.)
+      p->rpw = 16;
       p->tiles_m = ceil_div(M, p->mt);
-      p->tiles_n = ceil_div(N, 16);
+      p->tiles_n = ceil_div(N, p->rpw);
       p->split = 1;
       // Waves per workgroup: enough workgroups x waves for about 16 waves
-      // per CU, each wave keeping at least one phase of block pairs; two m
-      // tiles hold twice the operands, so at most 8 waves (2 per SIMD, up
-      // to 256 registers each).
+      // per CU, each wave keeping at least one phase of block pairs; with
+      // two m tiles a wave holds twice the activations, so at most 8 waves
+      // (2 per SIMD, up to 256 registers each).
       const int wmax = p->mt == 16 ? 16 : 8;
       const int64_t tiles = p->tiles_m * p->tiles_n;
       int w = 4;

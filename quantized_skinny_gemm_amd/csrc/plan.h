@@ -56,7 +56,7 @@ struct Plan {
   int variant = 0;          // 1 narrow, 2 wide (Q4_0: int8; F16: fp16), 3 skinny MFMA, 4 wide (Q4_0, fp16)
   // narrow kernels
   int mt = 1;               // src1 rows per pass (compile-time tile)
-  int rpw = 1;              // src0 rows per wave
+  int rpw = 1;              // src0 rows per wave (skinny MFMA: per workgroup)
   int waves = 4;            // waves per workgroup (skinny MFMA: they split K)
   // wide kernels
   int bm = 0, bn = 0, waves_m = 0, waves_n = 0;

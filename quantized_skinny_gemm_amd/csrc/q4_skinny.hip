@@ -44,12 +44,16 @@ namespace {
 
 constexpr int kPH = kSkinnyPairs;        // block pairs per phase (16 rows x 4 = 64 units)
 constexpr int kRP = kPH * 36 + 4;        // LDS row pitch: 37 dwords, odd, so rows spread the banks
-constexpr int kStageBytes = 16 * kRP;    // one wave's patch of weights
-constexpr int kScaleBytes = 2 * kPH * 16 * 4;   // its weight scales, f32 [block][row]
 
-template <int MP>
+// LDS of one wave: its patch of RT x 16 weight rows.
+template <int RT>
+struct WaveLds {
+  static constexpr int kBytes = RT * 16 * kRP;
+};
+
+template <int MP, int RT>
 struct Phase {
-  uint32_t w[9];              // this lane's unit: one row's block pair
+  uint32_t w[RT][9];          // this lane's units: one row's block pair per row tile
   v4i act[MP][kPH];           // B operands of pair j: blocks 2j and 2j+1
   float da[MP][2 * kPH];      // activation scale per m tile and block
 };
@@ -65,20 +69,25 @@ __device__ __forceinline__ v4f gloadf4(const float* p) {
   return *(const __attribute__((address_space(1))) v4f*)p;
 }
 
-// One phase's loads: this lane's weight unit (clamped to the row's last
-// pair) and, per m tile, the activations in operand order as INIT laid them
-// out (4 KB of codes per tile and phase, lane l of pair j at 1024 j + 16 l;
-// then the 16 rows' 8 scales), each instruction reading 1 KB in a row.
-// Blocks past K and rows past M hold zeros there, so no block is masked.
-template <int MP>
-__device__ __forceinline__ void load_phase(Phase<MP>& P, const Q4Args& a, const uint8_t* wrow,
-                                           int j0, int pairs, int ty) {
+// One phase's loads: this lane's weight units (row lane / 4 of each row
+// tile, pair lane % 4, clamped to the row's last pair) and, per m tile, the
+// activations in operand order as INIT laid them out (4 KB of codes per
+// tile and phase, lane l of pair j at 1024 j + 16 l; then the 16 rows' 8
+// scales), each instruction reading 1 KB in a row.  Blocks past K and rows
+// past M hold zeros there, so no block is masked.
+template <int MP, int RT>
+__device__ __forceinline__ void load_phase(Phase<MP, RT>& P, const Q4Args& a,
+                                           const uint8_t* const (&wrow)[RT], int j0, int pairs,
+                                           int ty) {
   const int lane = threadIdx.x & 63;
   int pc = j0 + (lane & 3);
   pc = pc < pairs ? pc : pairs - 1;
-  const uint8_t* wp = wrow + 36 * (int64_t)pc;
 #pragma unroll
-  for (int i = 0; i < 9; ++i) P.w[i] = gload32(wp + 4 * i);
+  for (int rt = 0; rt < RT; ++rt) {
+    const uint8_t* wp = wrow[rt] + 36 * (int64_t)pc;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) P.w[rt][i] = gload32(wp + 4 * i);
+  }
   const int f = j0 / kPH;
 #pragma unroll
   for (int t = 0; t < MP; ++t) {
@@ -101,157 +110,181 @@ __device__ __forceinline__ long nibbles_x16(uint32_t q) {
   return (long)(((uint64_t)hi << 32) | lo);
 }
 
-template <int MP, bool kDump>
-__device__ __forceinline__ void compute_phase(const Phase<MP>& P, float (&acc)[MP][4],
-                                              uint8_t* stage, float* sdw, int j0, int j1,
-                                              int n0, int m0, const Q4Args& a) {
+// The 16 x 16 tile of scale products d_w[row] * d_a[col] in the layout of
+// the MFMA results: an outer product on the fp32 matrix cores (K = 4, only
+// k = 0 non-zero, so each product is rounded once), in place of four
+// multiplies per lane and of a trip through LDS to bring each lane the
+// weight scales of its rows.
+__device__ __forceinline__ v4f scale_tile(float dw_row, float da_col, bool k0) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(k0 ? dw_row : 0.0f, k0 ? da_col : 0.0f,
+                                              v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+}
+
+template <int MP, int RT, bool kDump>
+__device__ __forceinline__ void compute_phase(const Phase<MP, RT>& P, float (&acc)[RT][MP][4],
+                                              uint8_t* stage, int j0, int j1, int n0, int m0,
+                                              const Q4Args& a) {
   const int lane = threadIdx.x & 63;
   const int i16 = lane & 15, g = lane >> 4;
-  {
-    // this lane's unit -> row lane / 4, pair lane % 4 of the patch
-    uint32_t* d = reinterpret_cast<uint32_t*>(stage + (lane >> 2) * kRP + 36 * (lane & 3));
 #pragma unroll
-    for (int i = 0; i < 9; ++i) d[i] = P.w[i];
+  for (int rt = 0; rt < RT; ++rt) {
+    // this lane's unit -> row 16 rt + lane / 4, pair lane % 4 of the patch
+    uint32_t* d = reinterpret_cast<uint32_t*>(stage + (16 * rt + (lane >> 2)) * kRP + 36 * (lane & 3));
+#pragma unroll
+    for (int i = 0; i < 9; ++i) d[i] = P.w[rt][i];
   }
   // LDS operations of one wave complete in order: the reads below see the
   // writes above, and the next phase's writes come after these reads.
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(stage + i16 * kRP);
   const int nb = a.K / 32;
 #pragma unroll
   for (int jj = 0; jj < kPH; ++jj) {
     const int pair = j0 + jj;
     const bool live = pair < j1;                   // for the dump (uniform over the wave)
-    const uint32_t* u = row + 9 * jj;
-    const uint32_t d0 = u[0], d4 = u[4];
-    const uint32_t qe = __builtin_amdgcn_alignbit(u[g + 1], u[g], 16);   // even block
-    const uint32_t qo = u[5 + g];                                      // odd block
-    // weight scales / 16 of row i16, blocks 2jj and 2jj+1 of the phase (the
-    // four lanes of a row store the same values; no branch)
-    sdw[(2 * jj) * 16 + i16] = f16_bits_to_f32(d0) * 0.0625f;
-    sdw[(2 * jj + 1) * 16 + i16] = f16_bits_to_f32(d4 >> 16) * 0.0625f;
+    long A[RT][2];
+    float dw[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const uint32_t* u = reinterpret_cast<const uint32_t*>(stage + (16 * rt + i16) * kRP) + 9 * jj;
+      A[rt][0] = nibbles_x16(__builtin_amdgcn_alignbit(u[g + 1], u[g], 16));   // even block
+      A[rt][1] = nibbles_x16(u[5 + g]);                                       // odd block
+      dw[rt][0] = f16_bits_to_f32(u[0]);                                      // row 16 rt + i16
+      dw[rt][1] = f16_bits_to_f32(u[4] >> 16);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kb = 2 * jj + h;
-      const long A = nibbles_x16(h ? qo : qe);
-      const float4 dw = *reinterpret_cast<const float4*>(sdw + kb * 16 + 4 * g);
 #pragma unroll
-      for (int t = 0; t < MP; ++t) {
-        const v4i& ac = P.act[t][jj];
-        const long B = h ? (long)(((uint64_t)(uint32_t)ac.w << 32) | (uint32_t)ac.z)
-                         : (long)(((uint64_t)(uint32_t)ac.y << 32) | (uint32_t)ac.x);
-        const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
-        const float da = P.da[t][kb];
-        acc[t][0] = fmaf((float)D.x, da * dw.x, acc[t][0]);
-        acc[t][1] = fmaf((float)D.y, da * dw.y, acc[t][1]);
-        acc[t][2] = fmaf((float)D.z, da * dw.z, acc[t][2]);
-        acc[t][3] = fmaf((float)D.w, da * dw.w, acc[t][3]);
-        if (kDump && live) {
-          const int m = m0 + 16 * t + i16;
-          const int b = 2 * pair + h;
-          const int Dv[4] = {D.x, D.y, D.z, D.w};
+      for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int n = n0 + 4 * g + r;
-            if (m < a.M && n >= a.n0 && n < a.n1)
-              a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + b] = Dv[r] / 16;
+        for (int t = 0; t < MP; ++t) {
+          const v4i& ac = P.act[t][jj];
+          const long B = h ? (long)(((uint64_t)(uint32_t)ac.w << 32) | (uint32_t)ac.z)
+                           : (long)(((uint64_t)(uint32_t)ac.y << 32) | (uint32_t)ac.x);
+          const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt][h], B, v4i{0, 0, 0, 0}, 0, 0, 0);
+          // d_w * d_a / 16 (INIT stores d_a / 16: the MFMA gives 16 S_b)
+          const v4f sc = scale_tile(dw[rt][h], P.da[t][kb], g == 0);
+          acc[rt][t][0] = fmaf((float)D.x, sc.x, acc[rt][t][0]);
+          acc[rt][t][1] = fmaf((float)D.y, sc.y, acc[rt][t][1]);
+          acc[rt][t][2] = fmaf((float)D.z, sc.z, acc[rt][t][2]);
+          acc[rt][t][3] = fmaf((float)D.w, sc.w, acc[rt][t][3]);
+          if (kDump && live) {
+            const int m = m0 + 16 * t + i16;
+            const int b = 2 * pair + h;
+            const int Dv[4] = {D.x, D.y, D.z, D.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int n = n0 + 16 * rt + 4 * g + r;
+              if (m < a.M && n >= a.n0 && n < a.n1)
+                a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + b] = Dv[r] / 16;
+            }
           }
         }
       }
     }
-    // one block pair's operands and results live at a time (the registers
-    // hold the next phase's loads instead)
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int MP, int W, bool kDump>
+// Workgroup: RT x 16 weight rows; its W waves split K into runs of pp block
+// pairs (a multiple of the phase).
+template <int MP, int RT, int W, bool kDump>
 __global__ __launch_bounds__(64 * W)
 void k_q4_skinny(Q4Args a, int pp) {
-  // pp: block pairs per wave, a multiple of the phase (kPH pairs)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nb = a.K / 32, pairs = nb / 2;
   const int64_t rb = (int64_t)nb * 18;
-  const int n0 = blockIdx.x * 16, ty = blockIdx.y, m0 = ty * 16 * MP;
+  const int n0 = blockIdx.x * 16 * RT, ty = blockIdx.y, m0 = ty * 16 * MP;
   // this wave's block pairs [j0w, j1w)
   const int j0w = wave * pp < pairs ? wave * pp : pairs;
   const int j1w = j0w + pp < pairs ? j0w + pp : pairs;
   const int nph = (j1w - j0w + kPH - 1) / kPH;
-  uint8_t* stage = smem + wave * (kStageBytes + kScaleBytes);
-  float* sdw = reinterpret_cast<float*>(stage + kStageBytes);
-  int nrow = n0 + (lane >> 2);
-  nrow = nrow < a.N ? nrow : a.N - 1;
-  const uint8_t* wrow = a.w + nrow * rb;
+  uint8_t* stage = smem + wave * WaveLds<RT>::kBytes;
+  const uint8_t* wrow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int nrow = n0 + 16 * rt + (lane >> 2);
+    nrow = nrow < a.N ? nrow : a.N - 1;
+    wrow[rt] = a.w + nrow * rb;
+  }
 
-  float acc[MP][4];
+  float acc[RT][MP][4];
 #pragma unroll
-  for (int t = 0; t < MP; ++t)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+    for (int t = 0; t < MP; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[rt][t][r] = 0.0f;
 
   // Two register sets; every load in the loop is unconditional, and the
   // last one or two phases are computed after it.
   // (The scheduling barriers keep the loads of one set from being hoisted
   // above the computation of the other, which would hold three sets.)
-  Phase<MP> P0, P1;
-  if (nph > 0) load_phase<MP>(P0, a, wrow, j0w, pairs, ty);
+  Phase<MP, RT> P0, P1;
+  if (nph > 0) load_phase<MP, RT>(P0, a, wrow, j0w, pairs, ty);
   int f = 0;
   for (; f + 2 < nph; f += 2) {
-    load_phase<MP>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
+    load_phase<MP, RT>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase<MP, kDump>(P0, acc, stage, sdw, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
     __builtin_amdgcn_sched_barrier(0);
-    load_phase<MP>(P0, a, wrow, j0w + (f + 2) * kPH, pairs, ty);
+    load_phase<MP, RT>(P0, a, wrow, j0w + (f + 2) * kPH, pairs, ty);
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase<MP, kDump>(P1, acc, stage, sdw, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (f + 1 < nph) {
-    load_phase<MP>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
+    load_phase<MP, RT>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase<MP, kDump>(P0, acc, stage, sdw, j0w + f * kPH, j1w, n0, m0, a);
-    compute_phase<MP, kDump>(P1, acc, stage, sdw, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
   } else if (f < nph) {
-    compute_phase<MP, kDump>(P0, acc, stage, sdw, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
   }
 
   // ---- add the W waves' partial tiles in a fixed order (LDS reused)
+  constexpr int NT = RT * MP;                      // 16 x 16 tiles per wave
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int t = 0; t < MP; ++t)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[((wave * MP + t) * 4 + r) * 64 + lane] = acc[t][r];
+    for (int t = 0; t < MP; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[((wave * NT + rt * MP + t) * 4 + r) * 64 + lane] = acc[rt][t][r];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < MP * 256; idx += 64 * W) {
-    const int t = idx >> 8, r = (idx >> 6) & 3, l = idx & 63;
+  for (int idx = threadIdx.x; idx < NT * 256; idx += 64 * W) {
+    const int tt = idx >> 8, r = (idx >> 6) & 3, l = idx & 63;
+    const int rt = tt / MP, t = tt - rt * MP;
     float s = 0.0f;
-    for (int w2 = 0; w2 < W; ++w2) s += red[((w2 * MP + t) * 4 + r) * 64 + l];
+    for (int w2 = 0; w2 < W; ++w2) s += red[((w2 * NT + tt) * 4 + r) * 64 + l];
     const int m = m0 + 16 * t + (l & 15);
-    const int n = n0 + 4 * (l >> 4) + r;
+    const int n = n0 + 16 * rt + 4 * (l >> 4) + r;
     if (m < a.M && n < a.N) a.dst[(int64_t)m * a.N + n] = s;
   }
 }
 
-template <int MP, int W>
+template <int MP, int RT, int W>
 hipError_t launch_w(const Plan& p, const Q4Args& a, int pp, hipStream_t s) {
   const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1u);
-  const size_t stage = (size_t)W * (kStageBytes + kScaleBytes);
-  const size_t red = (size_t)W * MP * 4 * 64 * 4;
+  const size_t stage = (size_t)W * WaveLds<RT>::kBytes;
+  const size_t red = (size_t)W * RT * MP * 4 * 64 * 4;
   const size_t lds = stage > red ? stage : red;
-  if (a.dots) hipLaunchKernelGGL((k_q4_skinny<MP, W, true>), grid, dim3(64 * W), lds, s, a, pp);
-  else hipLaunchKernelGGL((k_q4_skinny<MP, W, false>), grid, dim3(64 * W), lds, s, a, pp);
+  if (a.dots) hipLaunchKernelGGL((k_q4_skinny<MP, RT, W, true>), grid, dim3(64 * W), lds, s, a, pp);
+  else hipLaunchKernelGGL((k_q4_skinny<MP, RT, W, false>), grid, dim3(64 * W), lds, s, a, pp);
   return hipGetLastError();
 }
 
-template <int MP>
+template <int MP, int RT>
 hipError_t launch_mp(const Plan& p, const Q4Args& a, hipStream_t s) {
   const int pp = (int)p.kchunk;                     // block pairs per wave
   if (!a.sq || pp % kPH) return hipErrorInvalidValue;
-  if (p.waves == 4) return launch_w<MP, 4>(p, a, pp, s);
-  if (p.waves == 8) return launch_w<MP, 8>(p, a, pp, s);
-  if (p.waves == 16 && MP == 1) return launch_w<MP, 16>(p, a, pp, s);
+  if (p.waves == 4) return launch_w<MP, RT, 4>(p, a, pp, s);
+  if (p.waves == 8) return launch_w<MP, RT, 8>(p, a, pp, s);
+  if constexpr (MP == 1) {
+    if (p.waves == 16) return launch_w<MP, RT, 16>(p, a, pp, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -263,8 +296,8 @@ bool q4_skinny_ok(int K, const void* w) {
 
 hipError_t launch_q4_skinny(const Plan& p, const Q4Args& a, hipStream_t s) {
   if (p.split != 1 || !q4_skinny_ok(a.K, a.w)) return hipErrorInvalidValue;
-  if (p.mt == 16) return launch_mp<1>(p, a, s);
-  if (p.mt == 32) return launch_mp<2>(p, a, s);
+  if (p.mt == 16 && p.rpw == 16) return launch_mp<1, 1>(p, a, s);
+  if (p.mt == 32 && p.rpw == 16) return launch_mp<2, 1>(p, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -16,7 +16,8 @@
 //     fp32, both into LDS;
 //   * the Q8_0 activation codes (wdata) and scales are copied into LDS;
 //   * each wave runs WM x WN MFMAs per block and applies the fp32 scale
-//     epilogue acc += f32(S_b) * (d_a * d_w);
+//     epilogue acc += f32(S_b) * (d_a * d_w), the scale products coming
+//     from a second (fp16) MFMA as an outer product, off the vector ALU;
 // and, when the tiles cannot fill the device, K is split across workgroups
 // whose partial tiles a second kernel adds in fixed order (smallbard
 // "Generer a plusieurs", "La courbe, une premiere fois"; DeepSpeed-Inference
@@ -58,6 +59,18 @@ __device__ __forceinline__ v4i lds_operand(const int8_t* row, int bb, int h) {
   const uint2 y = *reinterpret_cast<const uint2*>(row + bb * 32 + 16 + 8 * h);
   v4i v;
   v.x = (int)x.x; v.y = (int)x.y; v.z = (int)y.x; v.w = (int)y.y;
+  return v;
+}
+
+// Operand of the 32 x 32 x 16 fp16 MFMA that forms the outer product of
+// two scale vectors: element k = 0 of lane l < 32 is the scale of row (or
+// column) l, every other element zero, so the MFMA's result is
+// d_a[row] * d_w[col] in the layout of the int32 block dots.  The scales
+// are binary16 values (widened to fp32 when staged), so the conversion back
+// and their product are exact.
+__device__ __forceinline__ v8h scale_operand(float d, int h) {
+  v8h v = {};
+  v[0] = h == 0 ? (_Float16)d : (_Float16)0.0f;
   return v;
 }
 
@@ -207,29 +220,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
     const int nblk = (kb1 - kb < KB) ? kb1 - kb : KB;
     for (int bb = 0; bb < nblk; ++bb) {
       v4i A[WM], B[WN];
-      float dw[WN];
+      v8h Ad[WM], Bd[WN];
 #pragma unroll
-      for (int i = 0; i < WM; ++i) A[i] = lds_operand(sA + (wm * WTM + 32 * i + l32) * PITCH, bb, h);
+      for (int i = 0; i < WM; ++i) {
+        A[i] = lds_operand(sA + (wm * WTM + 32 * i + l32) * PITCH, bb, h);
+        Ad[i] = scale_operand(sAd[bb * BM + wm * WTM + 32 * i + l32], h);
+      }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         B[j] = lds_operand(sB + (wn * WTN + 32 * j + l32) * PITCH, bb, h);
-        dw[j] = sBd[bb * BN + wn * WTN + 32 * j + l32];
+        Bd[j] = scale_operand(sBd[bb * BN + wn * WTN + 32 * j + l32], h);
       }
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
-        // output row of accumulator r: 8*(r/4) + 4*h + (r%4) within the 32x32 tile
-        float da[16];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 v = *reinterpret_cast<const float4*>(sAd + bb * BM + wm * WTM + 32 * i + 8 * g + 4 * h);
-          da[4 * g + 0] = v.x; da[4 * g + 1] = v.y; da[4 * g + 2] = v.z; da[4 * g + 3] = v.w;
-        }
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           const v16i zero = {};
           const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[i], B[j], zero, 0, 0, 0);
+          // d_a[row] * d_w[col] for every output of the tile, in the MFMA
+          // result layout (output row of register r: 8*(r/4) + 4*h + (r%4))
+          const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ad[i], Bd[j], v16f{}, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf((float)c[r], da[r] * dw[j], acc[i][j][r]);
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf((float)c[r], sc[r], acc[i][j][r]);
           if (kDump) {
             const int n = n0 + wn * WTN + 32 * j + l32;
 #pragma unroll

@@ -176,7 +176,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q8_0_skinny(
   uint8_t* base = sq + (((int64_t)t * phases + f) * 4 + j) * 1024 + 8 * e + 4 * h;
 #pragma unroll
   for (int g = 0; g < 4; ++g) *reinterpret_cast<uint32_t*>(base + 16 * (16 * g + i)) = packed[g];
-  if (h == 0) ss[(((int64_t)t * phases + f) * 16 + i) * 8 + kb] = f16_bits_to_f32(dbits);
+  // d_a / 16 (exact): the skinny kernel's MFMA yields 16 S_b
+  if (h == 0) ss[(((int64_t)t * phases + f) * 16 + i) * 8 + kb] = f16_bits_to_f32(dbits) * 0.0625f;
 }
 
 int64_t grid_for(int64_t nblocks, int lanes) { return (nblocks * lanes + kThreads - 1) / kThreads; }

@@ -150,7 +150,7 @@ def test_dispatch_threshold_and_workspace(m):
     if variant == 1:
         assert rows >= m or rows == 8
     if variant == 3:
-        # 16-row workgroups of 4, 8 or 16 waves, passes of 16 or 32 src1 rows
+        # workgroups of 4, 8 or 16 waves, passes of 16 or 32 src1 rows
         assert rows in (16, 32) and rows >= min(m, 32) and cols in (4, 8, 16)
         assert split == 1
     # F16: M = 1 narrow, up to 16 rows the skinny MFMA kernel (K slices
@@ -193,9 +193,11 @@ def test_split_k_when_grid_is_small():
 
 def test_skinny_mfma_waves_per_workgroup():
     # waves per 16-row workgroup: about 16 waves per CU over the grid, every
-    # wave at least one phase of 4 block pairs, at most 8 waves with 32 rows
+    # wave at least one phase of 4 block pairs, at most 8 waves with 32-row
+    # passes (twice the activations per wave)
     for m, n, k, want in ((8, 14336, 4096, 8), (16, 4096, 14336, 16), (32, 4096, 14336, 8),
-                          (16, 11008, 4096, 8), (8, 256, 512, 4), (4, 4096, 4096, 16)):
+                          (16, 11008, 4096, 8), (8, 256, 512, 4), (4, 4096, 4096, 16),
+                          (32, 14336, 4096, 8)):
         v, split, rows, cols, _ = qs.dispatch(Q4, m, n, k)
         assert v == 3 and split == 1
         assert rows == (16 if m <= 16 else 32)
