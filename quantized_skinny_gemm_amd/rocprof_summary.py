@@ -9,6 +9,13 @@
         kernel launched at different shapes gets one row per grid, with the
         number of dispatches and their median and minimum duration.
 
+    python -m quantized_skinny_gemm_amd.rocprof_summary counters DIR [DIR ...] [--only SUBSTR]
+        Per (kernel, grid) averages per dispatch of every counter in the
+        DIRs' *_counter_collection.csv (one --pmc pass per DIR), with the
+        ratios that read directly: VALU and LDS instructions and MFMAs per
+        wave, share of wave cycles waiting on a dependency, share of LDS
+        cycles lost to bank conflicts.
+
     python -m quantized_skinny_gemm_amd.rocprof_summary traffic \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --kernel SUBSTR --copy-bytes B --source FILE --algo-bytes A --out JSON
@@ -90,6 +97,50 @@ def shapes_markdown(directory: str, only: str = "") -> str:
     return "\n".join(lines)
 
 
+def counters_markdown(directories, only: str = "") -> str:
+    sums = {}
+    for directory in directories:
+        for r in _csv_rows(directory, "_counter_collection.csv"):
+            name = r["Kernel_Name"]
+            if only and only not in name:
+                continue
+            key = (name, int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            cnt = sums.setdefault(key, {})
+            c = cnt.setdefault(r["Counter_Name"], [0.0, set()])
+            c[0] += float(r["Counter_Value"])
+            c[1].add((directory, r.get("Process_Id", ""), r["Dispatch_Id"]))
+    lines = []
+    for (name, grid, wg), cnt in sorted(sums.items()):
+        avg = {k: v[0] / len(v[1]) for k, v in cnt.items()}
+        short = name.replace("|", "\\|")
+        if len(short) > 90:
+            short = short[:87] + "..."
+        lines.append(f"### `{short}`, grid {grid} threads, workgroup {wg}")
+        lines.append("")
+        lines.append("| counter | per dispatch |")
+        lines.append("|---|---:|")
+        for k in sorted(avg):
+            lines.append(f"| {k} | {avg[k]:.0f} |")
+        waves = avg.get("SQ_WAVES")
+        derived = []
+        if waves:
+            for k, label in (("SQ_INSTS_VALU", "VALU instructions per wave"),
+                             ("SQ_INSTS_LDS", "LDS instructions per wave"),
+                             ("SQ_INSTS_MFMA", "MFMA instructions per wave")):
+                if k in avg:
+                    derived.append((label, f"{avg[k] / waves:.1f}"))
+        if "SQ_WAIT_INST_ANY" in avg and avg.get("SQ_WAVE_CYCLES"):
+            derived.append(("wave cycles waiting on a dependency",
+                            f"{avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.2f}"))
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+            derived.append(("LDS cycles lost to bank conflicts",
+                            f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.2f}"))
+        for label, v in derived:
+            lines.append(f"| {label} | {v} |")
+        lines.append("")
+    return "\n".join(lines)
+
+
 def _counter_per_dispatch(directory: str, counter: str):
     """{dispatch id: (kernel name, value)} for one counter."""
     rows = _csv_rows(directory, "_counter_collection.csv")
@@ -158,6 +209,9 @@ def main(argv=None):
     sh = sub.add_parser("shapes")
     sh.add_argument("dir")
     sh.add_argument("--only", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("dir", nargs="+")
+    c.add_argument("--only", default="")
     t = sub.add_parser("traffic")
     for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--source", "--out"):
         t.add_argument(k, required=True)
@@ -168,6 +222,8 @@ def main(argv=None):
         print(stats_markdown(args.dir))
     elif args.cmd == "shapes":
         print(shapes_markdown(args.dir, args.only))
+    elif args.cmd == "counters":
+        print(counters_markdown(args.dir, args.only))
     else:
         res = traffic(args)
         with open(args.out, "w") as fh:
