@@ -47,6 +47,8 @@ Q4Args q4_args(const Plan& p, const void* src0, float* dst, int32_t* dots, int64
   a.sq = p.off_sq ? (const uint8_t*)(base + p.off_sq) : nullptr;
   a.ss = p.off_ss ? (const float*)(base + p.off_ss) : nullptr;
   a.sk_phases = (int)p.sk_phases;
+  a.sq_bytes = (int)(p.sk_rows * p.sk_phases * 256);
+  a.ss_bytes = (int)(p.sk_rows * p.sk_phases * 32);
   a.dst = dst;
   a.part = p.split > 1 ? (float*)(base + p.off_part) : nullptr;
   a.M = (int)M; a.N = (int)N; a.K = (int)K;
@@ -61,7 +63,7 @@ int q4_init(const Plan& p, const float* src1, int64_t M, int64_t K, void* ws, hi
     return hip_status(launch_quantize_q8_0_skinny(
         src1, M, K, (int8_t*)(base + p.off_aq), (float*)(base + p.off_ad),
         (int32_t*)(base + p.off_ab), base + p.off_sq, (float*)(base + p.off_ss), p.sk_rows,
-        p.sk_phases, s));
+        p.sk_phases, p.mt == 8, s));
   return hip_status(launch_quantize_q8_0(src1, M, K, nullptr, (int8_t*)(base + p.off_aq),
                                          (float*)(base + p.off_ad), (int32_t*)(base + p.off_ab),
                                          p.off_ah ? (uint16_t*)(base + p.off_ah) : nullptr, s));
@@ -81,7 +83,7 @@ Q4Mats single_mat(const void* src0, float* dst, int64_t N) {
 // The product kernel (x != NULL: INIT fused), then the split-K reduction.
 int q4_product(const Plan& p, const Q4Args& a, const float* x, hipStream_t s) {
   hipError_t e = p.kind == KK_Q4_NARROW   ? launch_q4_narrow(p, a, single_mat(a.w, a.dst, a.N), x, s)
-                 : p.kind == KK_Q4_MMA    ? (q4_skinny_ok(a.K, a.w) ? launch_q4_skinny(p, a, s)
+                 : p.kind == KK_Q4_MMA    ? (a.sq && q4_skinny_ok(a.K, a.w) ? launch_q4_skinny(p, a, s)
                                                                       : launch_q4_mma(p, a, s))
                  : p.kind == KK_Q4_WIDE16 ? launch_q4_wide16(p, a, s)
                                           : launch_q4_wide_i8(p, a, s);

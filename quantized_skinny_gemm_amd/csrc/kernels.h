@@ -20,12 +20,13 @@ hipError_t launch_quantize_q8_0(const float* x, int64_t nrows, int64_t k, uint8_
 hipError_t launch_quantize_q4_0(const float* x, int64_t nrows, int64_t k, uint8_t* y,
                                 hipStream_t s);
 
-// INIT for the skinny MFMA kernel: the internal wdata (wq, wd, wb as above)
+// INIT for the skinny MFMA kernels: the internal wdata (wq, wd, wb as above)
 // and the same codes and scales in that kernel's operand order (sq, ss) over
-// `rows` x `phases` * 8 blocks, zero past nrows and k.
+// `rows` x `phases` * 8 blocks, zero past nrows and k; `rows8` selects the
+// layout of the 8-row kernel (16-row tiles otherwise).
 hipError_t launch_quantize_q8_0_skinny(const float* x, int64_t nrows, int64_t k, int8_t* wq,
                                        float* wd, int32_t* wb, uint8_t* sq, float* ss,
-                                       int64_t rows, int64_t phases, hipStream_t s);
+                                       int64_t rows, int64_t phases, bool rows8, hipStream_t s);
 
 struct Q4Args {
   const uint8_t* w;      // Q4_0 src0
@@ -36,6 +37,7 @@ struct Q4Args {
   const uint8_t* sq;     // skinny kernel: codes in operand order (NULL otherwise)
   const float* ss;       // skinny kernel: scales in operand order
   int sk_phases;         // skinny kernel: phases of 8 blocks per row
+  int sq_bytes, ss_bytes; // skinny kernel: sizes of those two ranges
   float* dst;
   float* part;           // split-K partials [split][M][N]
   int M, N, K;

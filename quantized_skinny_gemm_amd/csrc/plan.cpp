@@ -67,10 +67,10 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     if (mma) {
       // 16-row workgroups whose waves split K among themselves (no split
       // across workgroups, so no partial sums in the workspace); passes of
-      // 16 or 32 src1 rows.
+      // 8 src1 rows (two blocks per MFMA), 16 or 32.
       p->kind = KK_Q4_MMA;
       p->variant = 3;
-      p->mt = M <= 16 ? 16 : 32;
+      p->mt = M <= 8 ? 8 : M <= 16 ? 16 : 32;
       // 16 weight rows per workgroup (and per wave).  (32, two MFMA row
       // tiles sharing each activation load, measured no faster at 14336 rows
       // and slower at 4096: half the workgroups.)
@@ -82,7 +82,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       // per CU, each wave keeping at least one phase of block pairs; with
       // two m tiles a wave holds twice the activations, so at most 8 waves
       // (2 per SIMD, up to 256 registers each).
-      const int wmax = p->mt == 16 ? 16 : 8;
+      const int wmax = p->mt <= 16 ? 16 : 8;
       const int64_t tiles = p->tiles_m * p->tiles_n;
       int w = 4;
       while (w < wmax && tiles * w < 16 * kCUs && nb / 2 >= 2 * w * kSkinnyPairs) w *= 2;
@@ -92,13 +92,17 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       const int64_t pairs = nb / 2;
       p->kchunk = ceil_div(ceil_div(pairs, w), kSkinnyPairs) * kSkinnyPairs;
       // INIT also writes the codes and scales in the kernel's operand order:
-      // per 16-row tile and phase of 8 blocks, 4 KB of codes (lane l of pair
-      // j at 1024 j + 16 l) and 16 x 8 scales; padding rows and blocks are
-      // zero.
-      p->sk_rows = p->tiles_m * p->mt;
-      p->sk_phases = ceil_div(nb, 2 * kSkinnyPairs);
-      p->off_sq = off; off = align_up(off + (size_t)p->sk_rows * p->sk_phases * 256, 256);
-      p->off_ss = off; off = align_up(off + (size_t)p->sk_rows * p->sk_phases * 32, 256);
+      // per tile and phase of 8 blocks, mt x 256 bytes of codes and 16 x 8
+      // (8-row tiles: 16 x 4) scales; padding rows and blocks are zero.  The
+      // kernels address these ranges with 32-bit offsets: past 1 GiB of codes
+      // the layout is not written and the product takes the fallback kernel.
+      const int64_t sk_rows = p->tiles_m * p->mt, sk_phases = ceil_div(nb, 2 * kSkinnyPairs);
+      if (sk_rows * sk_phases * 256 <= ((int64_t)1 << 30)) {
+        p->sk_rows = sk_rows;
+        p->sk_phases = sk_phases;
+        p->off_sq = off; off = align_up(off + (size_t)sk_rows * sk_phases * 256, 256);
+        p->off_ss = off; off = align_up(off + (size_t)sk_rows * sk_phases * 32, 256);
+      }
     } else if (narrow) {
       p->kind = KK_Q4_NARROW;
       p->variant = 1;

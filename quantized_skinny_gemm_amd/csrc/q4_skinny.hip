@@ -27,14 +27,19 @@
 //     bytes 4g .. 4g+3 of its row's block: their low nibbles are elements
 //     4g .. 4g+3, their high nibbles elements 16+4g .. 19+4g, and the B
 //     operand (the Q8_0 codes of src1 row l % 16) holds the same elements.
-//     Nibbles become signed bytes 16 * (q - 8) with one xor and two masks
-//     ((q ^ 8) << 4 read as a signed byte is 16 (q - 8)), so the MFMA ends
-//     at 16 S_b exactly and no bias term is needed; the 1/16 joins the
-//     weight scale (exact: a power of two).
-//   * Output lane l holds src1 row l % 16 and weight rows 4 (l / 16) + r:
-//     one activation scale per lane and block, four weight scales (read
-//     from LDS, where the lanes that decoded them left them).  Epilogue per
-//     output and block: acc += f32(16 S_b) * (d_a * d_w / 16).
+//     Nibbles become signed bytes 16 * (q - 8) with a shift and two masked
+//     xors ((q ^ 8) << 4 read as a signed byte is 16 (q - 8)), so the MFMA
+//     ends at 16 S_b exactly and no bias term is needed; the 1/16 joins the
+//     activation scale (exact: a power of two).
+//   * Output lane l holds src1 row l % 16 and weight rows 4 (l / 16) + r.
+//     The scale of each output, d_w[row] * d_a[col] / 16, comes from a
+//     second MFMA (an outer product on the fp32 matrix cores), already in
+//     the result layout; the epilogue per output and block is a convert and
+//     an fma: acc += f32(16 S_b) * (d_w * d_a / 16).
+//   * M <= 8 (k_q4_skinny8): v_mfma_i32_16x16x64_i8 takes two blocks at once,
+//     its 16 columns being 8 src1 rows x the pair's two blocks (the B operand
+//     of column (m, e) is zero outside block e), which halves the MFMAs, the
+//     scale products and the epilogue per block, and reads no padding rows.
 #include "device.h"
 #include "kernels.h"
 
@@ -61,20 +66,29 @@ struct Phase {
 __device__ __forceinline__ uint32_t gload32(const void* p) {
   return *(const __attribute__((address_space(1))) uint32_t*)p;
 }
-__device__ __forceinline__ v4i gload128(const void* p) {
-  return *(const __attribute__((address_space(1))) v4i*)p;
-}
 typedef float v4f __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v4f gloadf4(const float* p) {
-  return *(const __attribute__((address_space(1))) v4f*)p;
+
+// Activation loads go through a buffer resource over the operand-order
+// wdata: a lane whose offset is at or past the end of the range reads zeros
+// and sends no request, which is how lanes of rows past M (and, in the
+// 8-row kernel, lanes that hold no activation) skip their loads without a
+// branch.
+constexpr int kSkip = 0x7FFFFFF0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wdata_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ v4i bload128(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
 // One phase's loads: this lane's weight units (row lane / 4 of each row
 // tile, pair lane % 4, clamped to the row's last pair) and, per m tile, the
 // activations in operand order as INIT laid them out (4 KB of codes per
 // tile and phase, lane l of pair j at 1024 j + 16 l; then the 16 rows' 8
-// scales), each instruction reading 1 KB in a row.  Blocks past K and rows
-// past M hold zeros there, so no block is masked.
+// scales).  Lanes of rows past M load nothing (zeros), and only lanes 0-15
+// load scales: the scale MFMA reads its B operand from k = 0 alone, so the
+// other lanes' zeros keep it a plain outer product.  Blocks past K hold
+// zeros in the wdata.
 template <int MP, int RT>
 __device__ __forceinline__ void load_phase(Phase<MP, RT>& P, const Q4Args& a,
                                            const uint8_t* const (&wrow)[RT], int j0, int pairs,
@@ -89,35 +103,40 @@ __device__ __forceinline__ void load_phase(Phase<MP, RT>& P, const Q4Args& a,
     for (int i = 0; i < 9; ++i) P.w[rt][i] = gload32(wp + 4 * i);
   }
   const int f = j0 / kPH;
+  const __amdgpu_buffer_rsrc_t rq = wdata_rsrc(a.sq, a.sq_bytes);
+  const __amdgpu_buffer_rsrc_t rs = wdata_rsrc(a.ss, a.ss_bytes);
 #pragma unroll
   for (int t = 0; t < MP; ++t) {
-    const int64_t tp = (int64_t)(ty * MP + t) * a.sk_phases + f;
-    const uint8_t* cb = a.sq + tp * 4096 + 16 * lane;
+    const int tp = (ty * MP + t) * a.sk_phases + f;
+    const bool rv = (lane & 15) < a.M - (ty * MP + t) * 16;
+    const int qo = rv ? tp * 4096 + 16 * lane : kSkip;
 #pragma unroll
-    for (int j = 0; j < kPH; ++j) P.act[t][j] = gload128(cb + 1024 * j);
-    const float* sb = a.ss + (tp * 16 + (lane & 15)) * 8;
-    const v4f s0 = gloadf4(sb), s1 = gloadf4(sb + 4);
-    P.da[t][0] = s0.x; P.da[t][1] = s0.y; P.da[t][2] = s0.z; P.da[t][3] = s0.w;
-    P.da[t][4] = s1.x; P.da[t][5] = s1.y; P.da[t][6] = s1.z; P.da[t][7] = s1.w;
+    for (int j = 0; j < kPH; ++j) P.act[t][j] = bload128(rq, rv ? qo + 1024 * j : kSkip);
+    const bool sv = rv && lane < 16;
+    const v4i s0 = bload128(rs, sv ? (tp * 16 + lane) * 32 : kSkip);
+    const v4i s1 = bload128(rs, sv ? (tp * 16 + lane) * 32 + 16 : kSkip);
+    P.da[t][0] = __int_as_float(s0[0]); P.da[t][1] = __int_as_float(s0[1]);
+    P.da[t][2] = __int_as_float(s0[2]); P.da[t][3] = __int_as_float(s0[3]);
+    P.da[t][4] = __int_as_float(s1[0]); P.da[t][5] = __int_as_float(s1[1]);
+    P.da[t][6] = __int_as_float(s1[2]); P.da[t][7] = __int_as_float(s1[3]);
   }
 }
 
 // Signed bytes 16 (q - 8) of the low and high nibbles of four code bytes.
 __device__ __forceinline__ long nibbles_x16(uint32_t q) {
-  const uint32_t x = q ^ 0x88888888u;
-  const uint32_t lo = (x << 4) & 0xF0F0F0F0u;
-  const uint32_t hi = x & 0xF0F0F0F0u;
+  const uint32_t lo = ((q << 4) ^ 0x80808080u) & 0xF0F0F0F0u;
+  const uint32_t hi = (q ^ 0x88888888u) & 0xF0F0F0F0u;
   return (long)(((uint64_t)hi << 32) | lo);
 }
 
 // The 16 x 16 tile of scale products d_w[row] * d_a[col] in the layout of
-// the MFMA results: an outer product on the fp32 matrix cores (K = 4, only
-// k = 0 non-zero, so each product is rounded once), in place of four
-// multiplies per lane and of a trip through LDS to bring each lane the
-// weight scales of its rows.
-__device__ __forceinline__ v4f scale_tile(float dw_row, float da_col, bool k0) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(k0 ? dw_row : 0.0f, k0 ? da_col : 0.0f,
-                                              v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+// the MFMA results: an outer product on the fp32 matrix cores (K = 4; the
+// B operand is zero outside k = 0, so each product is rounded once), in
+// place of four multiplies per lane and of a trip through LDS to bring each
+// lane the weight scales of its rows.  Every lane passes its row's weight
+// scale (finite), and only lanes 0-15 a non-zero activation scale.
+__device__ __forceinline__ v4f scale_tile(float dw_row, float da_col) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(dw_row, da_col, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 }
 
 template <int MP, int RT, bool kDump>
@@ -162,7 +181,7 @@ __device__ __forceinline__ void compute_phase(const Phase<MP, RT>& P, float (&ac
                            : (long)(((uint64_t)(uint32_t)ac.y << 32) | (uint32_t)ac.x);
           const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt][h], B, v4i{0, 0, 0, 0}, 0, 0, 0);
           // d_w * d_a / 16 (INIT stores d_a / 16: the MFMA gives 16 S_b)
-          const v4f sc = scale_tile(dw[rt][h], P.da[t][kb], g == 0);
+          const v4f sc = scale_tile(dw[rt][h], P.da[t][kb]);
           acc[rt][t][0] = fmaf((float)D.x, sc.x, acc[rt][t][0]);
           acc[rt][t][1] = fmaf((float)D.y, sc.y, acc[rt][t][1]);
           acc[rt][t][2] = fmaf((float)D.z, sc.z, acc[rt][t][2]);
@@ -288,6 +307,156 @@ hipError_t launch_mp(const Plan& p, const Q4Args& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+
+// ---- M <= 8: two blocks per MFMA.  v_mfma_i32_16x16x64_i8 contracts 64
+// elements; the 16 columns are 8 src1 rows x the pair's two blocks, and the
+// B operand of column (m, e) is zero outside block e, so output (n, (m, e))
+// is the block dot of block e alone.  Lane (row i, group g) of A holds half
+// g & 1 of block g >> 1 of its row.
+struct Phase8 {
+  uint32_t w[9];
+  v4i act[kPH];
+  v4i da;                     // d_a / 16 of pair j's block for this column (zero elsewhere)
+};
+
+__device__ __forceinline__ void load_phase8(Phase8& P, const Q4Args& a, const uint8_t* wrow,
+                                            int j0, int pairs, int ty) {
+  const int lane = threadIdx.x & 63;
+  int pc = j0 + (lane & 3);
+  pc = pc < pairs ? pc : pairs - 1;
+  const uint8_t* wp = wrow + 36 * (int64_t)pc;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) P.w[i] = gload32(wp + 4 * i);
+  const __amdgpu_buffer_rsrc_t rq = wdata_rsrc(a.sq, a.sq_bytes);
+  const __amdgpu_buffer_rsrc_t rs = wdata_rsrc(a.ss, a.ss_bytes);
+  const int tp = ty * a.sk_phases + j0 / kPH;
+  const int c = lane & 15, g = lane >> 4, e = c >> 3;
+  const bool mv = (c & 7) < a.M - ty * 8;
+  const bool rv = mv && (g >> 1) == e;
+  const int qo = tp * 2048 + 16 * (2 * c + (g & 1));
+#pragma unroll
+  for (int j = 0; j < kPH; ++j) P.act[j] = bload128(rq, rv ? qo + 512 * j : kSkip);
+  P.da = bload128(rs, (mv && g == e) ? (tp * 16 + c) * 16 : kSkip);
+}
+
+template <bool kDump>
+__device__ __forceinline__ void compute_phase8(const Phase8& P, float (&acc)[4], uint8_t* stage,
+                                               int j0, int j1, int n0, int m0, const Q4Args& a) {
+  const int lane = threadIdx.x & 63;
+  const int i16 = lane & 15, g = lane >> 4;
+  {
+    uint32_t* d = reinterpret_cast<uint32_t*>(stage + (lane >> 2) * kRP + 36 * (lane & 3));
+#pragma unroll
+    for (int i = 0; i < 9; ++i) d[i] = P.w[i];
+  }
+  const int b = g < 2 ? 2 * g : 2 * g + 1;       // first code dword of this lane's half block
+  const int sh = g < 2 ? 16 : 0;                 // block 0's codes start 2 bytes into a dword
+  const int ds = (g & 1) ? 4 : 0, dsh = (g & 1) * 16;
+  const int nb = a.K / 32;
+#pragma unroll
+  for (int jj = 0; jj < kPH; ++jj) {
+    const uint32_t* u = reinterpret_cast<const uint32_t*>(stage + i16 * kRP) + 9 * jj;
+    const uint32_t x0 = u[b], x1 = u[b + 1], x2 = u[b + 2];
+    const long A0 = nibbles_x16(__builtin_amdgcn_alignbit(x1, x0, sh));
+    const long A1 = nibbles_x16(__builtin_amdgcn_alignbit(x2, x1, sh));
+    const v4i A = v4i{(int)(uint32_t)A0, (int)(uint32_t)((uint64_t)A0 >> 32),
+                      (int)(uint32_t)A1, (int)(uint32_t)((uint64_t)A1 >> 32)};
+    const float dw = f16_bits_to_f32((u[ds] >> dsh) & 0xFFFFu);
+    const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, P.act[jj], v4i{0, 0, 0, 0}, 0, 0, 0);
+    const v4f sc = __builtin_amdgcn_mfma_f32_16x16x4f32(dw, __int_as_float(P.da[jj]), v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    acc[0] = fmaf((float)D.x, sc.x, acc[0]);
+    acc[1] = fmaf((float)D.y, sc.y, acc[1]);
+    acc[2] = fmaf((float)D.z, sc.z, acc[2]);
+    acc[3] = fmaf((float)D.w, sc.w, acc[3]);
+    if (kDump && j0 + jj < j1) {
+      const int m = m0 + (i16 & 7);
+      const int bk = 2 * (j0 + jj) + (i16 >> 3);
+      const int Dv[4] = {D.x, D.y, D.z, D.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = n0 + 4 * g + r;
+        if (m < a.M && n >= a.n0 && n < a.n1)
+          a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + bk] = Dv[r] / 16;
+      }
+    }
+  }
+}
+
+template <int W, bool kDump>
+__global__ __launch_bounds__(64 * W)
+void k_q4_skinny8(Q4Args a, int pp) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nb = a.K / 32, pairs = nb / 2;
+  const int64_t rb = (int64_t)nb * 18;
+  const int n0 = blockIdx.x * 16, ty = blockIdx.y, m0 = ty * 8;
+  const int j0w = wave * pp < pairs ? wave * pp : pairs;
+  const int j1w = j0w + pp < pairs ? j0w + pp : pairs;
+  const int nph = (j1w - j0w + kPH - 1) / kPH;
+  uint8_t* stage = smem + wave * WaveLds<1>::kBytes;
+  int nrow = n0 + (lane >> 2);
+  nrow = nrow < a.N ? nrow : a.N - 1;
+  const uint8_t* wrow = a.w + nrow * rb;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  Phase8 P0, P1;
+  if (nph > 0) load_phase8(P0, a, wrow, j0w, pairs, ty);
+  int f = 0;
+  for (; f + 2 < nph; f += 2) {
+    load_phase8(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase8<kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+    __builtin_amdgcn_sched_barrier(0);
+    load_phase8(P0, a, wrow, j0w + (f + 2) * kPH, pairs, ty);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase8<kDump>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (f + 1 < nph) {
+    load_phase8(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase8<kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase8<kDump>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+  } else if (f < nph) {
+    compute_phase8<kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+  }
+  // the W waves' partial tiles, then the two block halves of each column,
+  // added in a fixed order
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 128; idx += 64 * W) {
+    const int r = idx & 3, m = (idx >> 2) & 7, gq = idx >> 5;
+    const int l = 16 * gq + m;
+    float s = 0.0f;
+    for (int w2 = 0; w2 < W; ++w2) s += red[(w2 * 4 + r) * 64 + l] + red[(w2 * 4 + r) * 64 + l + 8];
+    const int n = n0 + 4 * gq + r;
+    if (m0 + m < a.M && n < a.N) a.dst[(int64_t)(m0 + m) * a.N + n] = s;
+  }
+}
+
+template <int W>
+hipError_t launch_w8(const Plan& p, const Q4Args& a, int pp, hipStream_t s) {
+  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1u);
+  const size_t stage = (size_t)W * WaveLds<1>::kBytes;
+  const size_t red = (size_t)W * 4 * 64 * 4;
+  const size_t lds = stage > red ? stage : red;
+  if (a.dots) hipLaunchKernelGGL((k_q4_skinny8<W, true>), grid, dim3(64 * W), lds, s, a, pp);
+  else hipLaunchKernelGGL((k_q4_skinny8<W, false>), grid, dim3(64 * W), lds, s, a, pp);
+  return hipGetLastError();
+}
+
+hipError_t launch_8(const Plan& p, const Q4Args& a, hipStream_t s) {
+  const int pp = (int)p.kchunk;
+  if (!a.sq || pp % kPH) return hipErrorInvalidValue;
+  if (p.waves == 4) return launch_w8<4>(p, a, pp, s);
+  if (p.waves == 8) return launch_w8<8>(p, a, pp, s);
+  if (p.waves == 16) return launch_w8<16>(p, a, pp, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 bool q4_skinny_ok(int K, const void* w) {
@@ -296,8 +465,10 @@ bool q4_skinny_ok(int K, const void* w) {
 
 hipError_t launch_q4_skinny(const Plan& p, const Q4Args& a, hipStream_t s) {
   if (p.split != 1 || !q4_skinny_ok(a.K, a.w)) return hipErrorInvalidValue;
+  if (p.mt == 8 && p.rpw == 16) return launch_8(p, a, s);
   if (p.mt == 16 && p.rpw == 16) return launch_mp<1, 1>(p, a, s);
   if (p.mt == 32 && p.rpw == 16) return launch_mp<2, 1>(p, a, s);
+  if (p.mt == 16 && p.rpw == 32) return launch_mp<1, 2>(p, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -130,16 +130,17 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q4_0(const float* __restr
   store_u16(b + 4 + 4 * g, bytes >> 16);
 }
 
-// INIT of the skinny MFMA kernel: the plain wdata of the real blocks, and
+// INIT of the skinny MFMA kernels: the plain wdata of the real blocks, and
 // over the padded domain (rows x phases * 8 blocks; zeros past the real ones)
-// the codes and scales in that kernel's operand order.  Row m = 16 t + i,
-// block b = 8 f + 2 j + e: the 4 code bytes 4g .. 4g+3 (lane h = 0) or
-// 16+4g .. 19+4g (h = 1) go to byte 8e + 4h of the 16 bytes that lane
-// 16g + i of the MFMA loads for pair j of phase f of tile t.
+// the codes and scales in that kernel's operand order.  16-row tiles: row
+// m = 16 t + i, block b = 8 f + 2 j + e: the 4 code bytes 4g .. 4g+3 (lane
+// h = 0) or 16+4g .. 19+4g (h = 1) go to byte 8e + 4h of the 16 bytes that
+// lane 16g + i of the MFMA loads for pair j of phase f of tile t.  8-row
+// tiles (rows8): see below.
 __global__ __launch_bounds__(kThreads) void k_quantize_q8_0_skinny(
     const float* __restrict__ x, int M, int K, int phases, int64_t nblocks,
     int8_t* __restrict__ wq, float* __restrict__ wd, int32_t* __restrict__ wb,
-    uint8_t* __restrict__ sq, float* __restrict__ ss) {
+    uint8_t* __restrict__ sq, float* __restrict__ ss, bool rows8) {
   const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t blk = gtid >> 1;                    // over the padded domain
   const int h = threadIdx.x & 1;
@@ -170,6 +171,23 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q8_0_skinny(
       wd[pb] = f16_bits_to_f32(dbits);
       wb[pb] = -8 * sum;
     }
+  }
+  if (rows8) {
+    // 8-row tiles: row m = 8 t + i, block b = 8 f + 2 j + e is column
+    // c = 8 e + i of pair j's 16 x 16 x 64 MFMA; the lane of column c in
+    // group 2 e + s loads slot 2 c + s (16 bytes) of the pair's 512: elements
+    // 8s .. 8s+3, 16+8s .. 19+8s, 8s+4 .. 8s+7, 20+8s .. 23+8s, i.e. this
+    // thread's code dword qd (elements 16 h + 4 qd ..) goes to slot
+    // 2 c + qd / 2, dword 2 (qd % 2) + h.  Scales: d_a / 16 at (c, j).
+    const int t = m >> 3, i = m & 7;
+    const int f = b >> 3, kb = b & 7, j = kb >> 1, e = kb & 1;
+    const int c = 8 * e + i;
+    uint8_t* base = sq + (((int64_t)t * phases + f) * 4 + j) * 512;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+      *reinterpret_cast<uint32_t*>(base + 16 * (2 * c + (qd >> 1)) + 4 * (2 * (qd & 1) + h)) = packed[qd];
+    if (h == 0) ss[(((int64_t)t * phases + f) * 16 + c) * 4 + j] = f16_bits_to_f32(dbits) * 0.0625f;
+    return;
   }
   const int t = m >> 4, i = m & 15;
   const int f = b >> 3, kb = b & 7, j = kb >> 1, e = kb & 1;
@@ -206,12 +224,12 @@ hipError_t launch_quantize_q4_0(const float* x, int64_t nrows, int64_t k, uint8_
 
 hipError_t launch_quantize_q8_0_skinny(const float* x, int64_t nrows, int64_t k, int8_t* wq,
                                        float* wd, int32_t* wb, uint8_t* sq, float* ss,
-                                       int64_t rows, int64_t phases, hipStream_t s) {
+                                       int64_t rows, int64_t phases, bool rows8, hipStream_t s) {
   const int64_t nblocks = rows * phases * 8;
   const int64_t grid = grid_for(nblocks, 2);
   if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL(k_quantize_q8_0_skinny, dim3((unsigned)grid), dim3(kThreads), 0, s, x,
-                     (int)nrows, (int)k, (int)phases, nblocks, wq, wd, wb, sq, ss);
+                     (int)nrows, (int)k, (int)phases, nblocks, wq, wd, wb, sq, ss, rows8);
   return hipGetLastError();
 }
 

@@ -150,8 +150,9 @@ def test_dispatch_threshold_and_workspace(m):
     if variant == 1:
         assert rows >= m or rows == 8
     if variant == 3:
-        # workgroups of 4, 8 or 16 waves, passes of 16 or 32 src1 rows
-        assert rows in (16, 32) and rows >= min(m, 32) and cols in (4, 8, 16)
+        # workgroups of 4, 8 or 16 waves, passes of 8 (two blocks per
+        # MFMA), 16 or 32 src1 rows
+        assert rows == (8 if m <= 8 else 16 if m <= 16 else 32) and cols in (4, 8, 16)
         assert split == 1
     # F16: M = 1 narrow, up to 16 rows the skinny MFMA kernel (K slices
     # through the workspace), beyond the wide kernel; F32: narrow at M = 1,
@@ -200,7 +201,7 @@ def test_skinny_mfma_waves_per_workgroup():
                           (32, 14336, 4096, 8)):
         v, split, rows, cols, _ = qs.dispatch(Q4, m, n, k)
         assert v == 3 and split == 1
-        assert rows == (16 if m <= 16 else 32)
+        assert rows == (8 if m <= 8 else 16 if m <= 16 else 32)
         assert cols == want, (m, n, k, cols)
 
 
