@@ -10,7 +10,8 @@
 // the weights into floats ahead of the product can cost as much as the
 // product itself at these M).
 //
-// Per workgroup: an output tile BM x BN; per stage, KB = 4 blocks (128 k):
+// Per workgroup: an output tile BM x BN (32 x 64, 64 x 64, 64 x 128 or
+// 128 x 128, four waves); per stage, KB = 4 blocks (128 k):
 //   * weight rows are loaded as 36-byte block pairs (4-byte aligned when K/32
 //     is even), the nibbles unpacked to signed int8 (q - 8) and the scales to
 //     fp32, both into LDS;
@@ -293,6 +294,7 @@ hipError_t launch_q4_wide_i8(const Plan& p, const Q4Args& a, hipStream_t s) {
   const bool pairs = ((a.K / 32) % 2 == 0) && ((uintptr_t)a.w % 4 == 0);
   if (p.bm == 32 && p.bn == 64) return launch_cfg<32, 64, 1, 2>(p, a, pairs, s);
   if (p.bm == 64 && p.bn == 64) return launch_cfg<64, 64, 2, 2>(p, a, pairs, s);
+  if (p.bm == 64 && p.bn == 128) return launch_cfg<64, 128, 2, 2>(p, a, pairs, s);
   if (p.bm == 128 && p.bn == 64) return launch_cfg<128, 64, 2, 2>(p, a, pairs, s);
   if (p.bm == 128 && p.bn == 128) return launch_cfg<128, 128, 2, 2>(p, a, pairs, s);
   return hipErrorInvalidValue;
