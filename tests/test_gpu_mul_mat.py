@@ -179,6 +179,27 @@ def test_ragged_shapes_q4_0(m, n, k):
         _check_q4_product(wq_dev, wq, x, f"ragged {m}x{n}x{k}", v, (0, min(n, 40)))
 
 
+# The skinny MFMA kernels (2 < M <= 32, K % 64 == 0): a last phase of fewer
+# than 4 block pairs, a last wave with a shorter run, a single block pair,
+# N off the 16-row workgroup and M off the 8- and 16-row tiles.
+@pytest.mark.parametrize("m,n,k", [
+    (3, 100, 4160), (5, 17, 64), (7, 333, 1088), (8, 40, 192), (9, 50, 4160),
+    (13, 257, 320), (16, 31, 2112), (17, 99, 4160), (31, 65, 576), (32, 48, 128),
+])
+def test_ragged_shapes_skinny_q4_0(m, n, k):
+    qs = _qs()
+    assert qs.dispatch(qs.MM_TYPE_Q4_0, m, n, k)[0] == 3
+    rng = np.random.default_rng(m * 7_000_003 + n * 131 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    wq = codec.quantize_q4_0(w)
+    wq_dev = to_dev(wq)
+    y = _check_q4_product(wq_dev, wq, x, f"skinny ragged {m}x{n}x{k}", 0)
+    _check_q4_product(wq_dev, wq, x, f"skinny ragged {m}x{n}x{k}", 3)
+    # the production instantiation (no block-dot dump) gives the same bits
+    assert np.array_equal(to_host(qs.mul_mat_q4_0_f32(wq_dev, to_dev(x))), y)
+
+
 def test_misaligned_src0_uses_generic_path():
     """src0 at a 2-byte (not 4-byte) offset: the kernels fall back to 16-bit loads."""
     import torch
