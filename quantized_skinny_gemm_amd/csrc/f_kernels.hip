@@ -3,8 +3,10 @@
 //
 // Narrow (VALU) kernel: each weight row is streamed once with 16-byte loads
 // and widened to fp32 in registers; src1 stays fp32; fp32 FMA accumulation;
-// 64-lane butterfly reduction.  Rows of src1 beyond 16 are handled by further
-// passes (grid.y).
+// 64-lane butterfly reduction.  At M = 1 a wave owns one weight row and
+// issues the loads of several 16-byte chunks per lane before their FMAs
+// (four rows per wave for F16 beyond 8192 rows).  Rows of src1 beyond 16
+// are handled by further passes (grid.y).
 //
 // Skinny MFMA kernel (F16 at 2 <= M <= 16, F32 at M >= 2; rows 16-byte
 // aligned): passes of 16 src1 rows on the 16 x 16 matrix cores.  Each wave
@@ -79,8 +81,31 @@ __global__ __launch_bounds__(256) void k_f_narrow(const WT* __restrict__ w,
 
   int kdone = 0;
   if (kVec) {
+    // U chunks per lane per step, all loads of a step issued before its
+    // FMAs: one row per wave keeps few bytes in flight per step otherwise
+    constexpr int U = R == 1 ? (sizeof(WT) == 2 ? 4 : 2) : 1;
     const int nchunks = K / 8;
-    for (int c = lane; c < nchunks; c += 64) {
+    int c = lane;
+    for (; c + 64 * (U - 1) < nchunks; c += 64 * U) {
+      float wv[U][R][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) WLoad<WT>::load8(rowp[r] + 8 * (c + 64 * u), wv[u][r]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const float4 xa = reinterpret_cast<const float4*>(xp[m] + 8 * (c + 64 * u))[0];
+          const float4 xb = reinterpret_cast<const float4*>(xp[m] + 8 * (c + 64 * u))[1];
+          const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[r][m] = fmaf(wv[u][r][e], xv[e], acc[r][m]);
+        }
+    }
+    for (; c < nchunks; c += 64) {
       float wv[R][8];
 #pragma unroll
       for (int r = 0; r < R; ++r) WLoad<WT>::load8(rowp[r] + 8 * c, wv[r]);
@@ -135,7 +160,8 @@ hipError_t launch_f_typed(const Plan& p, const WT* w, const float* x, float* dst
                           int K, hipStream_t s) {
   const bool vec = (K % 8 == 0) && ((uintptr_t)w % 16 == 0) && ((uintptr_t)x % 16 == 0);
   switch (p.mt) {
-    case 1: return launch_f_mt<WT, 1, 4>(p, w, x, dst, M, N, K, vec, s);
+    case 1: return p.rpw == 1 ? launch_f_mt<WT, 1, 1>(p, w, x, dst, M, N, K, vec, s)
+                              : launch_f_mt<WT, 1, 4>(p, w, x, dst, M, N, K, vec, s);
     case 2: return launch_f_mt<WT, 2, 4>(p, w, x, dst, M, N, K, vec, s);
     case 4: return launch_f_mt<WT, 4, 4>(p, w, x, dst, M, N, K, vec, s);
     case 8: return launch_f_mt<WT, 8, 2>(p, w, x, dst, M, N, K, vec, s);

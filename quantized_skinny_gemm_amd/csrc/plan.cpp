@@ -232,6 +232,12 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     p->variant = 1;
     p->mt = narrow_mt(M, kNarrowFMaxM);
     p->rpw = p->mt >= 8 ? 2 : 4;
+    // M = 1: one weight row per wave (four times the workgroups, each wave's
+    // loads of several chunks in flight) except for F16 with many rows,
+    // where four rows per wave stay faster (measured: F32 4096 x 4096
+    // 18.6 -> 14.1 us, 11008 x 4096 42.6 -> 33.9; F16 4096 x 4096 9.6 -> 8.2;
+    // F16 11008 x 4096 19.0 with four rows against 20.1)
+    if (p->mt == 1 && (type == MM_TYPE_F32 || N <= 8192)) p->rpw = 1;
     p->tiles_m = ceil_div(M, p->mt);
     p->tiles_n = ceil_div(N, 4 * p->rpw);
   } else {
