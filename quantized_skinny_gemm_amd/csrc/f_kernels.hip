@@ -13,7 +13,8 @@
 // owns 16 weight rows of a K slice and loads their 16-byte pieces straight
 // into MFMA operand order (no unpacking, no per-block epilogue: the weights
 // are the B operand as stored); the workgroup's src1 slice is staged in LDS
-// once and read by its 8 waves.  F16 uses v_mfma_f32_16x16x32_f16 with src1
+// per sub-slice (128-512 k) and read by its 4 or 8 waves (both chosen in the
+// plan by type and row count).  F16 uses v_mfma_f32_16x16x32_f16 with src1
 // split into two binary16 terms hi + lo (their sum carries about 22 bits of
 // the f32 value; each f16 x f16 product is exact in fp32), F32 uses
 // v_mfma_f32_16x16x4_f32 on the values as they are.  K slices beyond one
@@ -173,10 +174,11 @@ hipError_t launch_f_typed(const Plan& p, const WT* w, const float* x, float* dst
 // ------------------------------------------------------------ skinny MFMA (F16, F32)
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <bool kF16>
+template <bool kF16, int SUB_>
 struct FmCfg {
-  static constexpr int kSub = kF16 ? kFmSubF16 : kFmSubF32;   // k per sub-slice: 16 steps
-  static constexpr int kStep = kSub / 16;                       // k per step (32 or 16)
+  static constexpr int kSub = SUB_;                             // k per LDS sub-slice
+  static constexpr int kStep = kF16 ? 32 : 16;                  // k per MFMA step
+  static constexpr int kSteps = kSub / kStep;
   static constexpr int kPitch = kSub + (kF16 ? 8 : 4);          // LDS row pitch (elements)
   static constexpr int kLds = kF16 ? 2 * 16 * kPitch * 2 : 16 * kPitch * 4;
 };
@@ -185,17 +187,17 @@ struct FmCfg {
 // step s of a sub-slice starting at k0 it holds k = k0 + kStep s + 8 kq ..
 // +7 (F16) or k0 + kStep s + 4 kq .. +3 (F32: one element per 16x16x4 MFMA,
 // the same k in the A operand).  Output: rows m0 + 4 kq .. +3, column n.
-template <bool kF16, bool kVecX>
-__global__ __launch_bounds__(512, 2)
+template <bool kF16, bool kVecX, int W, int SUB_>
+__global__ __launch_bounds__(64 * W, 2)
 void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* __restrict__ out,
              int M, int N, int K, int krange) {
-  typedef FmCfg<kF16> C;
-  constexpr int SUB = C::kSub, XP = C::kPitch, ST = C::kStep;
+  typedef FmCfg<kF16, SUB_> C;
+  constexpr int SUB = C::kSub, XP = C::kPitch, ST = C::kStep, NSTEP = C::kSteps, NT = 64 * W;
   __shared__ __attribute__((aligned(16))) uint8_t xs[C::kLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kq = lane >> 4;
   const int m0 = blockIdx.y * 16, z = blockIdx.z;
-  const int n = blockIdx.x * (16 * kFmWaves) + 16 * wave + l16;
+  const int n = blockIdx.x * (16 * W) + 16 * wave + l16;
   const int nr = n < N ? n : N - 1;
   const int kbeg = z * krange;
   const int kend = kbeg + krange < K ? kbeg + krange : K;
@@ -204,7 +206,8 @@ void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* _
   const int kl = kF16 ? 8 * kq : 4 * kq;             // this lane's k offset within a step
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  constexpr int IT = 16 * SUB / 4 / 512;              // src1 float4 items per thread
+  constexpr int IT = 16 * SUB / 4 / NT;               // src1 float4 items per thread
+  static_assert(IT * NT == 16 * SUB / 4, "src1 items must fill the threads");
   for (int k0 = kbeg; k0 < kend; k0 += SUB) {
     // src1 rows m0 .. m0+15, k0 .. k0+SUB-1 first (their wait then leaves
     // the weights in flight), clamped into range and zeroed past M and kend
@@ -212,7 +215,7 @@ void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* _
     float4 xv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int i = tid + 512 * it;
+      const int i = tid + NT * it;
       const int r = i / (SUB / 4), c = i % (SUB / 4);
       const int m = m0 + r < M ? m0 + r : M - 1, k = k0 + 4 * c < kend ? k0 + 4 * c : kbeg;
       const float* px = x + (int64_t)m * K + k;
@@ -224,9 +227,9 @@ void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* _
     }
     // this lane's 16 weight pieces of the sub-slice (past kend: clamped,
     // then zeroed)
-    v4i wp[16];
+    v4i wp[NSTEP];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
+    for (int s = 0; s < NSTEP; ++s) {
       const int k = k0 + ST * s + kl;
       const int kc = k < kend ? k : 0;
       wp[s] = *(const __attribute__((address_space(1))) v4i*)(wrow + (int64_t)kc * (kF16 ? 2 : 4));
@@ -234,7 +237,7 @@ void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* _
     __syncthreads();                                 // the last sub-slice's LDS reads are done
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int i = tid + 512 * it;
+      const int i = tid + NT * it;
       const int r = i / (SUB / 4), c = i % (SUB / 4);
       const bool ok = m0 + r < M && k0 + 4 * c < kend;
       const float v[4] = {ok ? xv[it].x : 0.0f, ok ? xv[it].y : 0.0f, ok ? xv[it].z : 0.0f,
@@ -255,7 +258,7 @@ void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* _
     }
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
+    for (int s = 0; s < NSTEP; ++s) {
       const bool in = k0 + ST * s + kl < kend;
       v4i b = wp[s];
       b.x = in ? b.x : 0; b.y = in ? b.y : 0; b.z = in ? b.z : 0; b.w = in ? b.w : 0;
@@ -492,19 +495,29 @@ bool f_mma_aligned(int type, const void* w, int K) {
   return (uintptr_t)w % 16 == 0 && K % (type == MM_TYPE_F16 ? 8 : 4) == 0;
 }
 
-hipError_t launch_f_mma(const Plan& p, int type, const void* w, const float* x, float* out, int M,
-                        int N, int K, hipStream_t s) {
+template <bool kF16, int W, int SUB>
+hipError_t launch_f_mma_cfg(const Plan& p, const void* w, const float* x, float* out, int M, int N,
+                            int K, hipStream_t s) {
   const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.split);
   const int kr = (int)p.kchunk;
-  const bool vx = (uintptr_t)x % 16 == 0;
-  if (type == MM_TYPE_F16) {
-    if (vx) hipLaunchKernelGGL((k_f_mma<true, true>), grid, dim3(512), 0, s, w, x, out, M, N, K, kr);
-    else hipLaunchKernelGGL((k_f_mma<true, false>), grid, dim3(512), 0, s, w, x, out, M, N, K, kr);
-  } else {
-    if (vx) hipLaunchKernelGGL((k_f_mma<false, true>), grid, dim3(512), 0, s, w, x, out, M, N, K, kr);
-    else hipLaunchKernelGGL((k_f_mma<false, false>), grid, dim3(512), 0, s, w, x, out, M, N, K, kr);
-  }
+  if ((uintptr_t)x % 16 == 0)
+    hipLaunchKernelGGL((k_f_mma<kF16, true, W, SUB>), grid, dim3(64 * W), 0, s, w, x, out, M, N, K, kr);
+  else
+    hipLaunchKernelGGL((k_f_mma<kF16, false, W, SUB>), grid, dim3(64 * W), 0, s, w, x, out, M, N, K, kr);
   return hipGetLastError();
+}
+
+hipError_t launch_f_mma(const Plan& p, int type, const void* w, const float* x, float* out, int M,
+                        int N, int K, hipStream_t s) {
+  // (waves, k per sub-slice) as the plan chose them
+  if (type == MM_TYPE_F16) {
+    if (p.waves == 8 && p.bn == 512) return launch_f_mma_cfg<true, 8, 512>(p, w, x, out, M, N, K, s);
+    if (p.waves == 8 && p.bn == 256) return launch_f_mma_cfg<true, 8, 256>(p, w, x, out, M, N, K, s);
+  } else {
+    if (p.waves == 4 && p.bn == 128) return launch_f_mma_cfg<false, 4, 128>(p, w, x, out, M, N, K, s);
+    if (p.waves == 8 && p.bn == 128) return launch_f_mma_cfg<false, 8, 128>(p, w, x, out, M, N, K, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_zero(float* dst, int64_t n, hipStream_t s) {

@@ -202,12 +202,18 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     p->kind = KK_F_MMA;
     p->variant = 3;
     p->mt = 16;
-    p->waves = kFmWaves;
+    // Waves (16 weight rows each) per workgroup and k per LDS sub-slice
+    // (p->bn), as measured at M = 4 and 16 (us, before -> after): F16 at
+    // more than 8192 rows 256 instead of 512 (11008 x 4096: 28.2 -> 24.5);
+    // F32 128 instead of 256, with 4 waves up to 8192 rows (4096 x 4096:
+    // 23.3 -> 19.5) and 8 beyond (11008 x 4096: 49.3 -> 45.5).
+    if (f16) { p->waves = 8; p->bn = N > 8192 ? 256 : 512; }
+    else { p->waves = N > 8192 ? 8 : 4; p->bn = 128; }
     p->tiles_m = ceil_div(M, 16);
-    p->tiles_n = ceil_div(N, 16 * kFmWaves);
+    p->tiles_n = ceil_div(N, 16 * p->waves);
     // K slices of whole sub-slices until there are about two workgroups per
     // CU (each slice adds M * N partial sums, written and read once)
-    const int64_t sub = f16 ? kFmSubF16 : kFmSubF32;
+    const int64_t sub = p->bn;
     const int64_t subs = ceil_div(K, sub);
     int64_t split = 1;
     if (allow_split) {

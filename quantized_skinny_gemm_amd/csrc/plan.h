@@ -25,9 +25,6 @@ constexpr int kWide16KB = 8;       // Q4_0 blocks per LDS stage, fp16 wide kerne
 constexpr int kWide16MaxM = 0;     // largest M the fp16 wide kernel takes by default (none: the
                                    // int8 wide kernel with register prefetch is faster at every M)
 constexpr int kF16WideKS = 64;     // k elements per LDS stage in the f16 wide kernel
-constexpr int kFmSubF16 = 512;     // skinny F16 MFMA kernel: k per LDS sub-slice (16 MFMA steps)
-constexpr int kFmSubF32 = 256;     // skinny F32 MFMA kernel: k per LDS sub-slice
-constexpr int kFmWaves = 8;        // skinny F MFMA kernel: waves (16 weight rows each) per workgroup
 constexpr int kNarrowQ4MaxM = 8;   // largest M the Q4_0 narrow kernel takes in one pass
 constexpr int kNarrowFMaxM = 16;   // largest M the f16/f32 narrow kernel takes in one pass
 constexpr int kFuseMaxM = 2;       // narrow Q4_0 passes of at most this many rows fuse INIT
@@ -59,7 +56,7 @@ struct Plan {
   int rpw = 1;              // src0 rows per wave (skinny MFMA: per workgroup)
   int waves = 4;            // waves per workgroup (skinny MFMA: they split K)
   // wide kernels
-  int bm = 0, bn = 0, waves_m = 0, waves_n = 0;
+  int bm = 0, bn = 0, waves_m = 0, waves_n = 0;   // (skinny F MFMA kernel: bn = k per LDS sub-slice)
   // grid
   int64_t tiles_m = 1;      // wide: output tile rows; narrow: passes over M
   int64_t tiles_n = 1;      // output tile columns (narrow: row groups of waves*rpw src0 rows)
