@@ -162,13 +162,20 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       // Output tile by M.  The 128 x 128 tile does about three times the
       // MFMA work per staged byte of a 128 x 64 one, so a grid that cannot
       // fill the device splits K (below) rather than shrinking the tile.
-      // Up to M = 64 with few weight rows (N <= 8192, so K is split at least
-      // 4 ways), a 64 x 128 tile whose waves hold two MFMA tiles each beat
-      // 64 x 64 (4096 x 14336, M = 64: 34.7 against 43.7 us); with many rows
-      // it is no faster.  Tiles with 8 or 16 waves were slower everywhere.
+      // Measured tile choices (us):  up to M = 64 with few weight rows
+      // (N <= 8192, so K is split at least 4 ways) a 64 x 128 tile, whose
+      // waves hold two MFMA tiles each, beats 64 x 64 (4096 x 14336, M = 64:
+      // 34.7 against 43.7), with many rows it does not; from M = 65 to 128 it
+      // is the reverse: with many rows two 64-row tiles sharing each weight
+      // tile through L2 beat one 128 x 128 tile (14336 x 4096, M = 128: 51.7
+      // against 57.6; M = 100: 47.9 against 55.2), with few rows they lose
+      // (4096 x 14336: 56.3 against 52.7).  Tiles with 8 or 16 waves were
+      // slower everywhere.
+      const bool many_rows = N > 8192;
       if (M <= 32) { p->bm = 32; p->bn = 64; p->waves_m = 1; p->waves_n = 2; }
-      else if (M <= 64 && N <= 8192) { p->bm = 64; p->bn = 128; p->waves_m = 2; p->waves_n = 2; }
+      else if (M <= 64 && !many_rows) { p->bm = 64; p->bn = 128; p->waves_m = 2; p->waves_n = 2; }
       else if (M <= 64) { p->bm = 64; p->bn = 64; p->waves_m = 2; p->waves_n = 2; }
+      else if (M <= 128 && many_rows) { p->bm = 64; p->bn = 128; p->waves_m = 2; p->waves_n = 2; }
       else { p->bm = 128; p->bn = 128; p->waves_m = 2; p->waves_n = 2; }
       p->tiles_m = ceil_div(M, p->bm);
       p->tiles_n = ceil_div(N, p->bn);

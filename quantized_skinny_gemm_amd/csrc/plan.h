@@ -29,7 +29,7 @@ constexpr int kNarrowQ4MaxM = 8;   // largest M the Q4_0 narrow kernel takes in 
 constexpr int kNarrowFMaxM = 16;   // largest M the f16/f32 narrow kernel takes in one pass
 constexpr int kFuseMaxM = 2;       // narrow Q4_0 passes of at most this many rows fuse INIT
 constexpr int kNarrowMaxLds = 65536; // LDS bytes the narrow kernel may stage activations in
-constexpr int kNarrowMaxGrid = 512;  // narrow workgroups along N (2 per CU)
+constexpr int kNarrowMaxGrid = 768;  // narrow workgroups along N (3 per CU)
 constexpr int kMmaMaxM = 32;       // largest M the skinny MFMA kernel takes by default
 constexpr int kSkinnyPairs = 4;    // skinny kernel: block pairs per wave phase
 constexpr int kMmaWaves = 8;       // waves per workgroup of the skinny kernel for unaligned

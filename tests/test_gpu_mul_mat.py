@@ -167,7 +167,7 @@ def test_decode_f16_f32(kind, j):
 @pytest.mark.parametrize("m,n,k", [
     (1, 1, 32), (1, 1000, 96), (3, 257, 4128), (8, 129, 2080), (9, 77, 1056),
     (16, 300, 544), (33, 65, 3200), (100, 190, 512), (130, 33, 8192), (513, 70, 256),
-    (1, 64, 14336), (32, 64, 14336), (2, 7, 32),
+    (1, 64, 14336), (32, 64, 14336), (2, 7, 32), (100, 8200, 256),
 ])
 def test_ragged_shapes_q4_0(m, n, k):
     rng = np.random.default_rng(m * 1_000_003 + n * 101 + k)
