@@ -230,3 +230,19 @@ def test_group_argument_checks():
     dst3 = (ctypes.c_void_p * 2)(FAKE + 2**31, FAKE + 2**20 + 8)
     assert g(2, src, dst3, n, FAKE + 2**30, 1, 64, FAKE + 2**32, ws, None) == ALIAS
     assert qs.group_workspace_size([64, -1], 1, 64) == 0
+
+
+def test_measured_tile_and_wave_choices():
+    # Q4_0 wide int8 tiles (rows, cols): 64 x 128 up to M = 64 with few weight
+    # rows and from M = 65 to 128 with many, 64 x 64 / 128 x 128 otherwise
+    for m, n, want in ((64, 4096, (64, 128)), (64, 14336, (64, 64)), (128, 14336, (64, 128)),
+                       (100, 11008, (64, 128)), (128, 4096, (128, 128)), (512, 14336, (128, 128))):
+        v, _, rows, cols, _ = qs.dispatch(Q4, m, n, 4096 if n > 4096 else 14336)
+        assert v == 2 and (rows, cols) == want, (m, n, rows, cols)
+    # F16 / F32 at M = 1: one weight row per wave, except F16 beyond 8192 rows
+    assert qs.dispatch(F32, 1, 11008, 4096)[3] == 1
+    assert qs.dispatch(F16, 1, 4096, 4096)[3] == 1
+    assert qs.dispatch(F16, 1, 11008, 4096)[3] == 4
+    # skinny F MFMA: waves per workgroup (F32 beyond 8192 rows: 8)
+    assert qs.dispatch(F32, 4, 11008, 4096)[3] == 8
+    assert qs.dispatch(F16, 16, 11008, 4096)[3] == 8
