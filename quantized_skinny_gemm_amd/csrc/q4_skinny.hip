@@ -349,8 +349,14 @@ __device__ __forceinline__ void compute_phase8(const Phase8& P, float (&acc)[4],
 #pragma unroll
     for (int i = 0; i < 9; ++i) d[i] = P.w[i];
   }
-  const int b = g < 2 ? 2 * g : 2 * g + 1;       // first code dword of this lane's half block
-  const int sh = g < 2 ? 16 : 0;                 // block 0's codes start 2 bytes into a dword
+  // Code dwords of this lane's half block: block 0's codes start 2 bytes into
+  // the unit (a funnel shift by 16 of dwords b .. b+2), block 1's are dword
+  // aligned (shift 0, so dword b+2 -- for g = 3 the row's pad dword after the
+  // last pair -- is read but not used).
+  const int b = g < 2 ? 2 * g : 2 * g + 1;
+  const int sh = g < 2 ? 16 : 0;
+  // Weight scale of block g & 1 (unit bytes 0-1 or 18-19): the scale MFMA's
+  // k = g; for g = 2, 3 the B operand is zero there, any finite value works.
   const int ds = (g & 1) ? 4 : 0, dsh = (g & 1) * 16;
   const int nb = a.K / 32;
 #pragma unroll
