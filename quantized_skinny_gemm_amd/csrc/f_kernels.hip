@@ -291,8 +291,6 @@ void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* _
 }
 
 // ------------------------------------------------------------ wide f16
-constexpr int KS = kF16WideKS;       // k per stage
-constexpr int HP = KS + 8;           // halves per LDS row (pad)
 
 // src1 -> binary16 (round to nearest even), [M][K] as given; the wide
 // kernel's A operand.  Four values per thread when src1 is 16-byte aligned
@@ -314,11 +312,17 @@ __global__ __launch_bounds__(256) void k_f32_to_f16(const float* __restrict__ x,
   }
 }
 
-template <int BM, int BN, bool kVec>
+// KS: k per LDS stage.  128 x 128 tiles take 64 (more would cost the
+// prefetch registers two waves per SIMD need), 64 x 64 tiles 128 (half the
+// barriers per MFMA: M = 512, 4096 x 4096 61.4 -> 45.6 us; M = 64,
+// 14336 x 4096 61.6 -> 45.0 us; 128 x 128 at 14336 / 128256 rows gains
+// nothing from it).
+template <int BM, int BN, bool kVec, int KS>
 __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w,
                                                   const uint16_t* __restrict__ xh,
                                                   float* __restrict__ dst, int M, int N, int K,
                                                   int tiles_m, int tiles_n) {
+  constexpr int HP = KS + 8;         // halves per LDS row (pad)
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int WM = WTM / 32, WN = WTN / 32;
   __shared__ __attribute__((aligned(16))) _Float16 sA[BM * HP];
@@ -482,11 +486,11 @@ hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, flo
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
   if (p.bm == 128) {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<128, 128, false>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true, 64>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<128, 128, false, 64>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
   } else {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<64, 64, false>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true, 128>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<64, 64, false, 128>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
   }
   return hipGetLastError();
 }

@@ -203,7 +203,12 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   // from 2 rows the skinny MFMA kernel; F16 beyond the wide kernel.
   if (variant == 4 || (variant == 2 && type != MM_TYPE_F16)) return MM_ERR_ARG;
   const bool f16 = type == MM_TYPE_F16;
-  const bool wide = f16 && (variant == 2 || (variant == 0 && M > kNarrowFMaxM));
+  // F16 from 17 rows: the wide kernel, except up to 64 rows with at most
+  // 8192 weight rows, where its 64 x 64 tiles give too few workgroups and
+  // passes of the skinny kernel are faster (4096 x 4096: M = 32 17.0 against
+  // 39.6 us, M = 64 23.7 against 39.9; 11008 rows tie at M = 32, 14336 rows
+  // favour the wide kernel at M = 64: 45.5 against 74.2).
+  const bool wide = f16 && (variant == 2 || (variant == 0 && M > kNarrowFMaxM && (M > 64 || N > 8192)));
   const bool fmma = !wide && (variant == 3 || (variant == 0 && M >= 2));
   if (fmma) {
     p->kind = KK_F_MMA;

@@ -24,7 +24,6 @@ constexpr int kWideI8KB = 4;       // Q4_0 blocks per LDS stage, int8 wide kerne
 constexpr int kWide16KB = 8;       // Q4_0 blocks per LDS stage, fp16 wide kernel
 constexpr int kWide16MaxM = 0;     // largest M the fp16 wide kernel takes by default (none: the
                                    // int8 wide kernel with register prefetch is faster at every M)
-constexpr int kF16WideKS = 64;     // k elements per LDS stage in the f16 wide kernel
 constexpr int kNarrowQ4MaxM = 8;   // largest M the Q4_0 narrow kernel takes in one pass
 constexpr int kNarrowFMaxM = 16;   // largest M the f16/f32 narrow kernel takes in one pass
 constexpr int kFuseMaxM = 2;       // narrow Q4_0 passes of at most this many rows fuse INIT
