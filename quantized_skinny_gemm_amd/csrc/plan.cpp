@@ -199,8 +199,9 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     return MM_OK;
   }
 
-  // F16 / F32: M = 1 the narrow kernel; F16 up to kNarrowFMaxM rows and F32
-  // from 2 rows the skinny MFMA kernel; F16 beyond the wide kernel.
+  // F16 / F32: M = 1 the narrow kernel; from 2 rows the skinny MFMA kernel
+  // (passes of 16 rows), for F16 only up to the limit below, beyond which
+  // the wide kernel takes it.
   if (variant == 4 || (variant == 2 && type != MM_TYPE_F16)) return MM_ERR_ARG;
   const bool f16 = type == MM_TYPE_F16;
   // F16 from 17 rows: the wide kernel, except up to 64 rows with at most
