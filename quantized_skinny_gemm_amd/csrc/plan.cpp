@@ -108,6 +108,10 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       p->variant = 1;
       p->mt = narrow_mt(M, kNarrowQ4MaxM);
       p->rpw = p->mt <= 2 ? 2 : 4;
+      // M = 1 with many rows: one weight row per wave (twice the row groups;
+      // decode step: q,k,v grouped 8.6 -> 8.2 us, gate,up grouped 12.7 ->
+      // 11.4 us); up to 8192 rows two rows per wave stay as fast or faster.
+      if (p->mt == 1 && N > 8192) p->rpw = 1;
       p->waves = p->mt <= 2 ? 8 : 4;
       p->tiles_m = ceil_div(M, p->mt);
       p->tiles_n = ceil_div(N, p->waves * p->rpw);

@@ -495,14 +495,15 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
 // Fused small-M kernel (MT <= 2 rows of src1, K/32 even, 4-byte aligned
 // weights, no K split): the common decode case, kept as lean as possible.
 // Each workgroup quantizes src1 into LDS once, then walks row groups
-// g = blockIdx.x, blockIdx.x + gridDim.x, ...; wave w of the group owns rows
-// 16g + 2w and 16g + 2w + 1, and lane l the K units (block pairs) l, l + 64,
+// g = blockIdx.x, blockIdx.x + gridDim.x, ...; wave w of the group owns R
+// rows (R = 2, or 1 for M = 1 with many rows: twice the row groups), rows
+// 8R g + R w .. 8R g + R w + R - 1, and lane l the K units (block pairs) l, l + 64,
 // ...  The steps (group, K unit range) of a wave form one flat sequence
 // whose next step's weights are loaded before the current one is computed.
-template <int MT, int NR>
+template <int MT, int NR, int R>
 __global__ __launch_bounds__(512)
 void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
-  constexpr int R = 2, WAVES = 8, NT = 64 * WAVES, RPG = WAVES * R;
+  constexpr int WAVES = 8, NT = 64 * WAVES, RPG = WAVES * R;
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -540,7 +541,9 @@ void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
   int g = blockIdx.x, i = 0;                         // current step: group g, K step i
   uint32_t wv[R][9];
   {
-    const uint8_t* rp[R] = {rowptr(g, 0), rowptr(g, 1)};
+    const uint8_t* rp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rp[r] = rowptr(g, r);
     const int u = lane < units ? lane : 0;
     load_unit<R, true>(wv, rp, u);
   }
@@ -571,7 +574,9 @@ void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
 #pragma unroll
       for (int j = 0; j < 9; ++j) cur[r][j] = wv[r][j];
     {
-      const uint8_t* rp[R] = {rowptr(gn, 0), rowptr(gn, 1)};
+      const uint8_t* rp[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) rp[r] = rowptr(gn, r);
       int un = lane + 64 * in;
       un = un < units ? un : 0;
       load_unit<R, true>(wv, rp, un);
@@ -600,8 +605,11 @@ void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
         ldo[r] = mats.row0[mi + 1] - mats.row0[mi];
       }
       const int r = lane / MT, m = lane % MT;
-      float* o = r == 0 ? out[0] : out[1];
-      const int ld = r == 0 ? ldo[0] : ldo[1];
+      float* o = out[0];
+      int ld = ldo[0];
+#pragma unroll
+      for (int rr = 1; rr < R; ++rr)
+        if (r == rr) { o = out[rr]; ld = ldo[rr]; }
       if (lane < R * MT && m < rows && nw + r < N) o[(int64_t)(m0 + m) * ld] = mine;
     }
     g = gn;
@@ -670,20 +678,25 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
   // (in units) doubles and the split count is unchanged.
   Plan q = p;
   if (!pairs && nb % 2 == 0) q.kchunk = p.kchunk * 2;
-  if (x && pairs && p.split == 1 && a.dots == nullptr && p.mt <= 2 && p.rpw == 2 && p.waves == 8) {
+  if (x && pairs && p.split == 1 && a.dots == nullptr && p.mt <= 2 && p.waves == 8 &&
+      (p.rpw == 2 || (p.rpw == 1 && p.mt == 1))) {
     const dim3 grid((unsigned)p.grid_n, (unsigned)p.tiles_m, 1u);
     const size_t lds = (size_t)p.mt * nb * 40;
     const int rounds = (int)(((int64_t)p.mt * nb * 2 + 511) / 512);
-    if (p.mt == 1) {
-      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<1, 1>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
-      else hipLaunchKernelGGL((k_q4_fused<1, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+    if (p.mt == 1 && p.rpw == 1) {
+      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<1, 1, 1>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+      else hipLaunchKernelGGL((k_q4_fused<1, 2, 1>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+    } else if (p.mt == 1) {
+      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<1, 1, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+      else hipLaunchKernelGGL((k_q4_fused<1, 2, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
     } else {
-      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<2, 1>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
-      else hipLaunchKernelGGL((k_q4_fused<2, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<2, 1, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+      else hipLaunchKernelGGL((k_q4_fused<2, 2, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
     }
     return hipGetLastError();
   }
   // rows per wave and waves per workgroup must match make_plan()
+  if (p.mt == 1 && p.rpw == 1 && p.waves == 8) return launch_mt<1, 1, 8>(q, a, mats, x, pairs, s);
   if (p.mt == 1 && p.rpw == 2 && p.waves == 8) return launch_mt<1, 2, 8>(q, a, mats, x, pairs, s);
   if (p.mt == 2 && p.rpw == 2 && p.waves == 8) return launch_mt<2, 2, 8>(q, a, mats, x, pairs, s);
   if (p.mt == 4 && p.rpw == 4 && p.waves == 4) return launch_mt<4, 4, 4>(q, a, mats, x, pairs, s);

@@ -70,7 +70,10 @@ def test_llama7b_decode_m1(j):
     n, k = workloads.WORKLOADS[1]["shapes"][j]
     wq_dev, wq = _q4_weights(1, j, n, k)
     x = workloads.activations(workloads.activation_seed(1, 1), 1, k)
-    _check_q4_product(wq_dev, wq, x, f"7B decode w{j}", 0, (0, n))
+    y = _check_q4_product(wq_dev, wq, x, f"7B decode w{j}", 0, (0, n))
+    # the production call (fused INIT; one row per wave beyond 8192 rows)
+    # gives the same bits as the block-dot dump instantiation
+    assert np.array_equal(to_host(_qs().mul_mat_q4_0_f32(wq_dev, to_dev(x))), y)
 
 
 @pytest.mark.parametrize("j", [0, 1])
