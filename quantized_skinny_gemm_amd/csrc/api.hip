@@ -354,7 +354,7 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
     out[1] = p.split;
     const bool tiled = p.variant == 2 || p.variant == 4;
     out[2] = tiled ? p.bm : p.mt;
-    out[3] = tiled ? p.bn : p.variant == 3 ? p.waves : p.rpw;
+    out[3] = tiled ? p.bn : p.variant == 3 ? p.waves : p.kind == KK_Q4_NARROW && p.fuse ? p.fuse_rpw : p.rpw;
     const int init = (p.type == MM_TYPE_Q4_0 && !(p.kind == KK_Q4_NARROW && p.fuse)) ? 1 : 0;
     out[4] = init + 1 + (p.split > 1 ? 1 : 0);
   }

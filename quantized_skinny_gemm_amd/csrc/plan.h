@@ -62,6 +62,8 @@ struct Plan {
   int64_t grid_n = 1;       // narrow: workgroups along N (each walks tiles_n / grid_n row groups)
   int split = 1;            // split-K factor
   bool fuse = false;        // narrow Q4_0: quantize src1 inside the product kernel
+  int fuse_rpw = 2, fuse_waves = 8;  // fused kernel: rows per wave and waves per workgroup
+  int64_t fuse_grid = 0;    // fused kernel: workgroups along N
   int64_t kchunk = 0;       // K per split (Q4 narrow: units; Q4 wide / skinny: blocks; F: elements)
   // workspace layout (bytes)
   size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0;

@@ -500,10 +500,10 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
 // 8R g + R w .. 8R g + R w + R - 1, and lane l the K units (block pairs) l, l + 64,
 // ...  The steps (group, K unit range) of a wave form one flat sequence
 // whose next step's weights are loaded before the current one is computed.
-template <int MT, int NR, int R>
-__global__ __launch_bounds__(512)
+template <int MT, int NR, int R, int WAVES>
+__global__ __launch_bounds__(64 * WAVES)
 void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
-  constexpr int WAVES = 8, NT = 64 * WAVES, RPG = WAVES * R;
+  constexpr int NT = 64 * WAVES, RPG = WAVES * R;
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -678,22 +678,25 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
   // (in units) doubles and the split count is unchanged.
   Plan q = p;
   if (!pairs && nb % 2 == 0) q.kchunk = p.kchunk * 2;
-  if (x && pairs && p.split == 1 && a.dots == nullptr && p.mt <= 2 && p.waves == 8 &&
-      (p.rpw == 2 || (p.rpw == 1 && p.mt == 1))) {
-    const dim3 grid((unsigned)p.grid_n, (unsigned)p.tiles_m, 1u);
+  if (x && pairs && p.split == 1 && a.dots == nullptr && p.fuse) {
+    const dim3 grid((unsigned)p.fuse_grid, (unsigned)p.tiles_m, 1u);
     const size_t lds = (size_t)p.mt * nb * 40;
-    const int rounds = (int)(((int64_t)p.mt * nb * 2 + 511) / 512);
-    if (p.mt == 1 && p.rpw == 1) {
-      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<1, 1, 1>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
-      else hipLaunchKernelGGL((k_q4_fused<1, 2, 1>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
-    } else if (p.mt == 1) {
-      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<1, 1, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
-      else hipLaunchKernelGGL((k_q4_fused<1, 2, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
-    } else {
-      if (rounds <= 1) hipLaunchKernelGGL((k_q4_fused<2, 1, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
-      else hipLaunchKernelGGL((k_q4_fused<2, 2, 2>), grid, dim3(512), lds, s, mats, x, a.M, a.N, a.K);
+    const int nt = 64 * p.fuse_waves;
+    const int rounds = (int)(((int64_t)p.mt * nb * 2 + nt - 1) / nt);
+#define QSG_FUSED(MT_, R_, W_)                                                                     \
+    if (p.mt == MT_ && p.fuse_rpw == R_ && p.fuse_waves == W_) {                                   \
+      if (rounds <= 1)                                                                             \
+        hipLaunchKernelGGL((k_q4_fused<MT_, 1, R_, W_>), grid, dim3(nt), lds, s, mats, x, a.M, a.N, a.K); \
+      else                                                                                         \
+        hipLaunchKernelGGL((k_q4_fused<MT_, 2, R_, W_>), grid, dim3(nt), lds, s, mats, x, a.M, a.N, a.K); \
+      return hipGetLastError();                                                                    \
     }
-    return hipGetLastError();
+    QSG_FUSED(1, 2, 8)
+    QSG_FUSED(1, 1, 8)
+    QSG_FUSED(1, 1, 16)
+    QSG_FUSED(2, 2, 8)
+#undef QSG_FUSED
+    return hipErrorInvalidValue;
   }
   // rows per wave and waves per workgroup must match make_plan()
   if (p.mt == 1 && p.rpw == 1 && p.waves == 8) return launch_mt<1, 1, 8>(q, a, mats, x, pairs, s);
