@@ -203,6 +203,23 @@ def test_ragged_shapes_skinny_q4_0(m, n, k):
     assert np.array_equal(to_host(qs.mul_mat_q4_0_f32(wq_dev, to_dev(x))), y)
 
 
+# The M <= 8 skinny kernel over many row tiles: N off the 16-row tiles, K off
+# the phases, waves with no K range (K = 256 is one phase), M below 8.
+@pytest.mark.parametrize("m,n,k", [(8, 8192, 4096), (5, 8200, 4160), (1, 8192, 256), (3, 12000, 1088)])
+def test_many_tiles_skinny_q4_0(m, n, k):
+    qs = _qs()
+    if m > 2:
+        assert qs.dispatch(qs.MM_TYPE_Q4_0, m, n, k)[0] == 3
+    rng = np.random.default_rng(m * 5_000_011 + n * 37 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    wq = codec.quantize_q4_0(w)
+    wq_dev = to_dev(wq)
+    y = _check_q4_product(wq_dev, wq, x, f"skinny many tiles {m}x{n}x{k}", 3)
+    if m > 2:
+        assert np.array_equal(to_host(qs.mul_mat_q4_0_f32(wq_dev, to_dev(x))), y)
+
+
 def test_misaligned_src0_uses_generic_path():
     """src0 at a 2-byte (not 4-byte) offset: the kernels fall back to 16-bit loads."""
     import torch
