@@ -140,13 +140,15 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       const int64_t kblocks = (nb % 2 == 0) ? 2 * p->kchunk : p->kchunk;
       p->fuse = p->mt <= kFuseMaxM && (int64_t)p->mt * kblocks * 40 <= kNarrowMaxLds;
       // The fused kernel's own geometry (same arithmetic per row): as the
-      // narrow plan, except at M = 1 with at most 8192 rows and K > 8192,
-      // where one row per wave and 16 waves per workgroup (the same 16 rows
-      // per group) keep twice the waves per CU in flight (decode step, down
-      // projection 4096 x 11008: 8.19 -> 7.61 us).
+      // narrow plan, except at M = 1 with at most 8192 rows, where it also
+      // takes one row per wave: with 8 waves per workgroup (twice the row
+      // groups; us per call: 2048 x 4096 4.25 -> 3.61, 8192 x 4096 7.00 ->
+      // 6.88, 4096 x 4096 unchanged), and for K > 8192 with 16 (the same 16
+      // rows per group, twice the waves per CU in flight: decode step, down
+      // projection 4096 x 11008, 8.19 -> 7.61).
       p->fuse_rpw = p->rpw;
       p->fuse_waves = p->waves;
-      if (p->fuse && p->mt == 1 && N <= 8192 && K > 8192) { p->fuse_rpw = 1; p->fuse_waves = 16; }
+      if (p->fuse && p->mt == 1 && N <= 8192) { p->fuse_rpw = 1; p->fuse_waves = K > 8192 ? 16 : 8; }
       {
         const int64_t groups = ceil_div(N, (int64_t)p->fuse_rpw * p->fuse_waves);
         p->fuse_grid = groups < kNarrowMaxGrid ? groups : kNarrowMaxGrid;

@@ -240,6 +240,9 @@ def test_measured_tile_and_wave_choices():
                        (100, 11008, (64, 128)), (128, 4096, (128, 128)), (512, 14336, (128, 128))):
         v, _, rows, cols, _ = qs.dispatch(Q4, m, n, 4096 if n > 4096 else 14336)
         assert v == 2 and (rows, cols) == want, (m, n, rows, cols)
+    # Q4_0 at M = 1 (the fused kernel): one weight row per wave at every size
+    for n, k in ((256, 512), (4096, 4096), (4096, 11008), (11008, 4096), (12288, 4096)):
+        assert qs.dispatch(Q4, 1, n, k)[3] == 1, (n, k)
     # F16 / F32 at M = 1: one weight row per wave, except F16 beyond 8192 rows
     assert qs.dispatch(F32, 1, 11008, 4096)[3] == 1
     assert qs.dispatch(F16, 1, 4096, 4096)[3] == 1
