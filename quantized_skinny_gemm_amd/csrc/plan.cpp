@@ -79,13 +79,17 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       p->tiles_n = ceil_div(N, p->rpw);
       p->split = 1;
       // Waves per workgroup: enough workgroups x waves for about 16 waves
-      // per CU, each wave keeping at least one phase of block pairs; with
-      // two m tiles a wave holds twice the activations, so at most 8 waves
-      // (2 per SIMD, up to 256 registers each).
-      const int wmax = p->mt <= 16 ? 16 : 8;
+      // per CU (8 with 32-row passes, whose waves hold twice the
+      // activations), each wave keeping at least one phase of block pairs;
+      // at most 16 waves with 8-row passes, 8 otherwise (measured, us per
+      // call: M = 32, 14336 x 4096 with 4 waves instead of 8, 27.6 -> 23.9;
+      // M = 16, 4096 x 14336 with 8 instead of 16, 17.6 -> 17.1; fewer waves
+      // at M = 8 / 16 on 14336 x 4096, or more anywhere, are slower).
+      const int wmax = p->mt <= 8 ? 16 : 8;
+      const int64_t wtarget = (p->mt == 32 ? 8 : 16) * (int64_t)kCUs;
       const int64_t tiles = p->tiles_m * p->tiles_n;
       int w = 4;
-      while (w < wmax && tiles * w < 16 * kCUs && nb / 2 >= 2 * w * kSkinnyPairs) w *= 2;
+      while (w < wmax && tiles * w < wtarget && nb / 2 >= 2 * w * kSkinnyPairs) w *= 2;
       p->waves = w;
       // block pairs per wave: whole phases, so that every wave's phases
       // start on a phase of the operand-order wdata

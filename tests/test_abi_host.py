@@ -195,12 +195,12 @@ def test_split_k_when_grid_is_small():
 
 
 def test_skinny_mfma_waves_per_workgroup():
-    # waves per 16-row workgroup: about 16 waves per CU over the grid, every
-    # wave at least one phase of 4 block pairs, at most 8 waves with 32-row
-    # passes (twice the activations per wave)
-    for m, n, k, want in ((8, 14336, 4096, 8), (16, 4096, 14336, 16), (32, 4096, 14336, 8),
+    # waves per 16-row workgroup: about 16 waves per CU over the grid (8 with
+    # 32-row passes), every wave at least one phase of 4 block pairs, at most
+    # 16 waves with 8-row passes and 8 with 16- or 32-row passes
+    for m, n, k, want in ((8, 14336, 4096, 8), (16, 4096, 14336, 8), (32, 4096, 14336, 8),
                           (16, 11008, 4096, 8), (8, 256, 512, 4), (4, 4096, 4096, 16),
-                          (32, 14336, 4096, 8)):
+                          (8, 4096, 14336, 16), (32, 14336, 4096, 4), (32, 4096, 4096, 8)):
         v, split, rows, cols, _ = qs.dispatch(Q4, m, n, k)
         assert v == 3 and split == 1
         assert rows == (8 if m <= 8 else 16 if m <= 16 else 32)
