@@ -168,10 +168,17 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       p->tiles_n = ceil_div(N, p->bn);
       const int64_t tiles = p->tiles_m * p->tiles_n;
       const int64_t stages = ceil_div(nb, kWide16KB);
+      // Fewer tiles than CUs: split K for about two workgroups per CU, at
+      // least 4 stages per split (us per call, against one workgroup per CU
+      // and 2 stages: M = 512, 4096 x 4096 58.7 -> 49.5; M = 128, 4096 x 14336
+      // 54.2 -> 47.3-48.8; M = 256, 4096 x 4096 39.2 -> 34.5; M = 40,
+      // 11008 x 4096 33.9 -> 31.8; M = 64, 14336 x 4096 35.4 -> 36.3).  With
+      // enough tiles it does not pay (M = 512, 14336 x 4096, split 2: 127 ->
+      // 142).
       int64_t split = 1;
       if (allow_split && tiles < kCUs) {
-        split = ceil_div(kCUs, tiles);
-        const int64_t max_split = stages / 2;          // >= 2 stages per split
+        split = ceil_div(2 * kCUs, tiles);
+        const int64_t max_split = stages / 4;          // >= 4 stages per split
         if (split > max_split) split = max_split;
         if (split > 16) split = 16;
         if (split < 1) split = 1;
@@ -203,10 +210,17 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       p->tiles_n = ceil_div(N, p->bn);
       const int64_t tiles = p->tiles_m * p->tiles_n;
       const int64_t stages = ceil_div(nb, kWideI8KB);
+      // Fewer tiles than CUs: split K for about two workgroups per CU, at
+      // least 4 stages per split (us per call, against one workgroup per CU
+      // and 2 stages: M = 512, 4096 x 4096 58.7 -> 49.5; M = 128, 4096 x 14336
+      // 54.2 -> 47.3-48.8; M = 256, 4096 x 4096 39.2 -> 34.5; M = 40,
+      // 11008 x 4096 33.9 -> 31.8; M = 64, 14336 x 4096 35.4 -> 36.3).  With
+      // enough tiles it does not pay (M = 512, 14336 x 4096, split 2: 127 ->
+      // 142).
       int64_t split = 1;
       if (allow_split && tiles < kCUs) {
-        split = ceil_div(kCUs, tiles);
-        const int64_t max_split = stages / 2;          // >= 2 stages per split
+        split = ceil_div(2 * kCUs, tiles);
+        const int64_t max_split = stages / 4;          // >= 4 stages per split
         if (split > max_split) split = max_split;
         if (split > 16) split = 16;
         if (split < 1) split = 1;
