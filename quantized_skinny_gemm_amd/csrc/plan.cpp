@@ -246,7 +246,11 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   // 39.6 us, M = 64 23.7 against 39.9; 11008 rows tie at M = 32, 14336 rows
   // favour the wide kernel at M = 64: 45.5 against 74.2).
   const bool wide = f16 && (variant == 2 || (variant == 0 && M > kNarrowFMaxM && (M > 64 || N > 8192)));
-  const bool fmma = !wide && (variant == 3 || (variant == 0 && M >= 2));
+  // F16 at M = 2 with at most 8192 rows stays on the narrow kernel (us per
+  // call against the matrix cores: 4096 x 4096 11.2 / 12.4, 8192 x 4096
+  // 16.2 / 19.9, 4096 x 11008 26.2 / 30.7; 11008 x 4096 ties at 24.3).
+  const bool f16_narrow2 = f16 && M == 2 && N <= 8192;
+  const bool fmma = !wide && (variant == 3 || (variant == 0 && M >= 2 && !f16_narrow2));
   if (fmma) {
     p->kind = KK_F_MMA;
     p->variant = 3;

@@ -154,13 +154,13 @@ def test_dispatch_threshold_and_workspace(m):
         # MFMA), 16 or 32 src1 rows
         assert rows == (8 if m <= 8 else 16 if m <= 16 else 32) and cols in (4, 8, 16)
         assert split == 1
-    # F16: M = 1 narrow, up to 16 rows the skinny MFMA kernel (K slices
-    # through the workspace), beyond the wide kernel; F32: narrow at M = 1,
-    # skinny MFMA from 2 rows
+    # F16: M = 1 narrow (and M = 2 up to 8192 rows), up to 16 rows the
+    # skinny MFMA kernel (K slices through the workspace), beyond the wide
+    # kernel; F32: narrow at M = 1, skinny MFMA from 2 rows
     for t in (F16, F32):
         fv, fsplit, frows, fcols, flaunch = qs.dispatch(t, m, 4096, 4096)
         # (F16 up to 64 rows at this N = 4096 also takes the skinny kernel)
-        fwant = 1 if m == 1 else 3 if (m <= 64 or t == F32) else 2
+        fwant = 1 if (m == 1 or (m == 2 and t == F16)) else 3 if (m <= 64 or t == F32) else 2
         assert fv == fwant
         if fv == 3:
             # 16-row passes; workgroups of 8 waves (F32 up to 8192 rows: 4)
