@@ -153,6 +153,9 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       p->fuse_rpw = p->rpw;
       p->fuse_waves = p->waves;
       if (p->fuse && p->mt == 1 && N <= 8192) { p->fuse_rpw = 1; p->fuse_waves = K > 8192 ? 16 : 8; }
+      // M = 2: only the long-K case pays (4096 x 11008: 11.0 -> 9.8 us; one
+      // row per wave elsewhere is slower, 4096 x 4096 5.2 -> 5.4)
+      if (p->fuse && p->mt == 2 && N <= 8192 && K > 8192) { p->fuse_rpw = 1; p->fuse_waves = 16; }
       {
         const int64_t groups = ceil_div(N, (int64_t)p->fuse_rpw * p->fuse_waves);
         p->fuse_grid = groups < kNarrowMaxGrid ? groups : kNarrowMaxGrid;

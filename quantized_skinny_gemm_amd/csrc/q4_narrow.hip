@@ -695,6 +695,7 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
     QSG_FUSED(1, 1, 8)
     QSG_FUSED(1, 1, 16)
     QSG_FUSED(2, 2, 8)
+    QSG_FUSED(2, 1, 16)
 #undef QSG_FUSED
     return hipErrorInvalidValue;
   }

@@ -243,6 +243,9 @@ def test_measured_tile_and_wave_choices():
     # Q4_0 at M = 1 (the fused kernel): one weight row per wave at every size
     for n, k in ((256, 512), (4096, 4096), (4096, 11008), (11008, 4096), (12288, 4096)):
         assert qs.dispatch(Q4, 1, n, k)[3] == 1, (n, k)
+    # M = 2: one row per wave only with long K at up to 8192 rows
+    assert qs.dispatch(Q4, 2, 4096, 11008)[3] == 1
+    assert qs.dispatch(Q4, 2, 4096, 4096)[3] == 2
     # F16 / F32 at M = 1: one weight row per wave, except F16 beyond 8192 rows
     assert qs.dispatch(F32, 1, 11008, 4096)[3] == 1
     assert qs.dispatch(F16, 1, 4096, 4096)[3] == 1

@@ -220,6 +220,21 @@ def test_many_tiles_skinny_q4_0(m, n, k):
         assert np.array_equal(to_host(qs.mul_mat_q4_0_f32(wq_dev, to_dev(x))), y)
 
 
+# M = 2 with long K (one weight row per wave, 16 waves per workgroup in the
+# fused kernel): N off the row groups; the production call against the
+# oracle and bit for bit against the narrow kernel's dump instantiation.
+def test_fused_m2_long_k():
+    qs = _qs()
+    m, n, k = 2, 4100, 8448
+    rng = np.random.default_rng(424242)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    wq = codec.quantize_q4_0(w)
+    wq_dev = to_dev(wq)
+    y = _check_q4_product(wq_dev, wq, x, "fused M=2 long K", 1, (0, 64))
+    assert np.array_equal(to_host(qs.mul_mat_q4_0_f32(wq_dev, to_dev(x))), y)
+
+
 def test_misaligned_src0_uses_generic_path():
     """src0 at a 2-byte (not 4-byte) offset: the kernels fall back to 16-bit loads."""
     import torch
