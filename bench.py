@@ -318,13 +318,18 @@ def run_sweep(reps: int, out_path: str | None):
         gbs = nb / (us * 1e-6) / 1e9
         tops = product_ops(m, n, k) / (us * 1e-6) / 1e12
         if t == "q4_0" and m >= 32:
-            bound, frac = "int8 MFMA", tops / INT8_PEAK_TOPS
+            bound, frac, peak = "int8 MFMA", tops / INT8_PEAK_TOPS, INT8_PEAK_TOPS
         elif t == "f16" and m >= 32:
-            bound, frac = "fp16 MFMA", tops / FP16_PEAK_TFLOPS
+            bound, frac, peak = "fp16 MFMA", tops / FP16_PEAK_TFLOPS, FP16_PEAK_TFLOPS
         else:
-            bound, frac = "hbm", gbs / HBM_PEAK_GBS
+            bound, frac, peak = "hbm", gbs / HBM_PEAK_GBS, None
+        # against the lower of the compute peak and what 8 TB/s of the
+        # algorithmic bytes allows (M = 32 .. 128 are still HBM-capped)
+        cap_frac = frac if peak is None else \
+            tops / min(peak, HBM_PEAK_GBS * 1e9 * product_ops(m, n, k) / nb / 1e12)
         r = dict(workload=w, type=t, M=m, N=n, K=k, us=round(us, 3), GBs=round(gbs, 1),
                  TOPS=round(tops, 2), bound=bound, frac=round(frac, 4),
+                 frac_of_cap=round(cap_frac, 4),
                  kernel=({1: "narrow", 2: "wide i8", 3: "skinny mfma", 4: "wide fp16"} if t == "q4_0"
                          else {1: "narrow", 2: "wide fp16", 3: "skinny mfma"}).get(variant, str(variant)),
                  split=split, launches=launches,
@@ -341,9 +346,11 @@ def run_sweep(reps: int, out_path: str | None):
 
 
 # ------------------------------------------------------------ cpu leg
-def cpu_baseline(budget_s: float = 10.0):
-    """The CPU oracle (as it stands) on one layer's 7 products, repeated for
-    about `budget_s` seconds of work; weights quantized by the oracle itself."""
+def _oracle_layers(budget_s: float):
+    """One worker's leg: the CPU oracle (as it stands) on one Llama-7B layer's 7
+    products at M = 1, repeated for about budget_s seconds; returns (layers done,
+    wall seconds, cpu seconds).  Weights are quantized by the oracle itself,
+    outside the timed loop."""
     import workloads
     from oracle import codec, mul_mat
 
@@ -351,24 +358,98 @@ def cpu_baseline(budget_s: float = 10.0):
     wq = [codec.quantize_q4_0(workloads.weights_f32(workloads.weight_seed(1, j), n, k))
           for j, (n, k) in enumerate(shapes)]
     xs = {k: workloads.activations(workloads.activation_seed(1, 1), 1, k) for _, k in shapes}
-    layer_bytes = sum(q4_step_bytes(1, *shapes[s]) for s in LAYER_SLOTS)
     done = 0
     c0 = os.times()
     t0 = time.perf_counter()
     while True:
-        for s in LAYER_SLOTS:
-            n, k = shapes[s]
-            mul_mat.mul_mat_q4_0_f32(wq[s], xs[k])
+        for sl in LAYER_SLOTS:
+            n, k = shapes[sl]
+            mul_mat.mul_mat_q4_0_f32(wq[sl], xs[k])
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     wall = time.perf_counter() - t0
     c1 = os.times()
-    cpu = (c1.user - c0.user) + (c1.system - c0.system)
+    return done, wall, (c1.user - c0.user) + (c1.system - c0.system)
+
+
+def _one_thread_env():
+    for v in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[v] = "1"
+
+
+def _pool_worker(budget_s: float):
+    _one_thread_env()
+    return _oracle_layers(budget_s)
+
+
+def cpu_baseline(budget_s: float = 8.0, max_workers: int = 16):
+    """The CPU oracle timed on the host: one worker (one thread), then one
+    worker per host core (at most max_workers, the host share of one GPU),
+    each running the same layer loop on its own copy of the inputs.  Returns
+    the all-cores figure with the one-core figure inside it."""
+    import multiprocessing as mp
+
+    layer_bytes = sum(q4_step_bytes(1, *_shapes()[sl]) for sl in LAYER_SLOTS)
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(1) as pool:
+        done1, wall1, cpu1 = pool.apply(_pool_worker, (budget_s,))
+    workers = max(1, min(max_workers, os.cpu_count() or 1))
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_pool_worker, [budget_s] * workers)
+    done = sum(r[0] for r in res)
+    wall = max(r[1] for r in res)
+    cpu = sum(r[2] for r in res)
     return {"value": layer_bytes * done / wall / 1e9, "unit": "GB/s",
             "cores": max(1, round(cpu / wall)), "kind": "oracle",
-            "sample": f"{done} x one Llama-7B layer at M=1 (7 Q4_0 products incl. Q8_0 "
-                      f"quantize of src1), {wall:.1f} s wall, host: {os.cpu_count()} cpus"}
+            "sample": f"one Llama-7B layer at M=1 (7 Q4_0 products incl. Q8_0 quantize of "
+                      f"src1) repeated: {workers} single-threaded workers x {wall:.1f} s "
+                      f"({done} layers); host: {os.cpu_count()} cpus",
+            "one_core": {"value": layer_bytes * done1 / wall1 / 1e9, "unit": "GB/s",
+                         "cores": max(1, round(cpu1 / wall1)),
+                         "sample": f"{done1} layers in {wall1:.1f} s on one thread"}}
+
+
+# ------------------------------------------------------------ read ceiling
+BENCH_READ_LIB = os.path.join(ROOT, "bench_read.so")
+
+
+def read_ceiling(st, reps: int, s, grid: int = 1024):
+    """A plain streaming read (bench_read.so, not the library) of the same
+    weight buffers in the same launch pattern as the grouped step: per layer
+    q,k,v in one launch, o, gate,up in one, down; 128 launches per step as one
+    HIP graph.  Returns the whole-step GB/s (weight bytes only) and the
+    average us per launch of each kind."""
+    import ctypes
+    torch = st["torch"]
+    if not os.path.exists(BENCH_READ_LIB):
+        return None
+    rl = ctypes.CDLL(BENCH_READ_LIB)
+    rl.qsg_bench_stream_read.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    rl.qsg_bench_stream_read.restype = ctypes.c_int
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    keep = []
+    kinds = {}
+    step = []
+    for row in st["weights"]:
+        for kind, slots in (("qkv", [0, 1, 2]), ("o", [3]), ("gate_up", [4, 5]), ("down", [6])):
+            ptrs = (ctypes.c_void_p * len(slots))(*[row[sl].data_ptr() for sl in slots])
+            nb = (ctypes.c_int64 * len(slots))(*[row[sl].numel() for sl in slots])
+            keep.append((ptrs, nb))
+            c = (kind, rl.qsg_bench_stream_read,
+                 (ptrs, nb, len(slots), sink.data_ptr(), grid, s.cuda_stream),
+                 float(sum(row[sl].numel() for sl in slots)))
+            step.append(c)
+            kinds.setdefault(kind, []).append(c)
+    ms = time_graph(torch, s, step, reps)
+    total = sum(c[3] for c in step)
+    per = {k: round(time_graph(torch, s, v, reps) * 1e3 / len(v), 4) for k, v in kinds.items()}
+    return {"GBs": round(total / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 5),
+            "per_kind_us": per, "grid": grid,
+            "what": "plain 16-byte streaming read of the step's weight buffers, same 128-launch "
+                    "graph (bench_read.hip)"}
 
 
 # ------------------------------------------------------------------ main
@@ -379,6 +460,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config table (every product of the five workloads)")
+    ap.add_argument("--config-reps", type=int, default=5)
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--only-step", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
@@ -399,6 +483,13 @@ def main():
     if args.sweep is not None:
         run_sweep(max(2, args.kernel_reps // 4), args.sweep or None)
         return
+
+    # the CPU leg first, before this process touches the GPU (its workers are
+    # separate processes)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on 1 core and on all cores (about 20 s)")
+        cpu = cpu_baseline()
 
     st = setup_gpu(args.layers)
     torch = st["torch"]
@@ -494,9 +585,21 @@ def main():
             "per_kind_us": {r["kind"]: round(r["avg_us"], 4) for r in kern},
         },
     }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle (about 10 s)")
-        out["cpu_baseline"] = cpu_baseline()
+    ceiling = read_ceiling(st, args.kernel_reps, s)
+    if ceiling is not None:
+        out["read_ceiling"] = ceiling
+        log(f"plain read of the step's weights, same launch pattern: {ceiling['GBs']} GB/s "
+            f"({ceiling['per_kind_us']} us per launch)")
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    if not args.no_configs:
+        del st, grouped, single, step_calls, graph
+        torch.cuda.empty_cache()
+        log("timing every product of the five workloads")
+        out["configs"] = [
+            {k: r[k] for k in ("workload", "type", "M", "N", "K", "us", "GBs", "TOPS", "bound",
+                               "frac", "frac_of_cap", "kernel", "launches")}
+            for r in run_sweep(args.config_reps, None)]
     print(json.dumps(out), flush=True)
 
 

@@ -68,9 +68,12 @@ typedef enum mm_type {
 
 /*
  * mm_quantize_q4_0 -- x[nrows][k] (f32) -> y[nrows][k/32] Q4_0 blocks (18 B each).
- * Weight quantisation (setup, outside the decode loop): the Q4_0 encoding
- * above.  k % 32 == 0.  x must be 16-byte aligned; y needs 2-byte alignment.
- * y must not overlap x.
+ * Weight quantisation (setup, outside the decode loop): src0 of the
+ * quantized MUL_MAT kind arrives as one of the block types the mulmat tune
+ * PR lists in its Introduction (Q4_0 among them; its Results section names
+ * Q4_0, Q5_0 and Q8_0); the encoding is the Q4_0 one above.  k % 32 == 0.
+ * x must be 16-byte aligned; y needs 2-byte alignment.  y must not overlap
+ * x.
  */
 int mm_quantize_q4_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream);
 
@@ -138,16 +141,24 @@ size_t mm_mul_mat_q4_0_group_workspace_size(int count, const int64_t* Ns, int64_
 
 /*
  * mm_mul_mat_f16_f32 -- dst[M][N] = src1[M][K] . f32(src0[N][K])^T, fp32 accumulation.
+ * The F16 x F32 kind of llama.cpp PR 1632 "mulmat tune", Introduction
+ * (src0 F16, src1 and dst F32; no INIT stage).
  *   src0: IEEE binary16 [N][K], 2-byte aligned.  src1: f32 [M][K], 4-byte
- *   aligned.  dst: f32, 4-byte aligned.  Any K >= 0.  M = 1: src1 is used
- *   in f32.  2 <= M <= 16 (src0 16-byte aligned and K a multiple of 8, else
- *   as M = 1): src1 enters the f16 MFMA as two binary16 terms hi + lo whose
- *   sum carries about 22 significant bits of each value (relative effect
- *   about 1e-6).  M > 16: src1 is rounded to binary16 for the f16 MFMA
- *   (relative effect about 1e-4).  Both inside the 1e-3 bound of this kind.
+ *   aligned.  dst: f32, 4-byte aligned.  Any K >= 0.
+ *   Precision: M = 1 (and any M whose operands are not 16-byte aligned or
+ *   whose K is not a multiple of 8): fp32 FMA of src1 as given and the
+ *   widened weights.  2 <= M <= 16, and up to 64 with at most 8192 weight
+ *   rows: the same exact fp32 products on the fp32 matrix cores.  Both
+ *   hold for every finite src1 in the fp32 range.  Larger M: src1 is
+ *   rounded to binary16 for the fp16 matrix cores after scaling each row
+ *   by a power of two that puts its largest magnitude in [2^14, 2^15)
+ *   (undone exactly on the outputs), so every row keeps 11 significant bits
+ *   whatever its magnitude (row-normwise effect about 1e-4; only elements
+ *   below 2^-28 of their row's largest magnitude lose bits, a contribution
+ *   far under the bound).  All inside the 1e-3 row-normwise bound of this
+ *   kind.
  *   ws: mm_mul_mat_workspace_size(MM_TYPE_F16, ...) bytes (0 when that is
- *   0); at 2 <= M <= 16 it holds split-K partial sums, at M > 16 src1 as
- *   binary16 (converted once per call).
+ *   0); for the larger M it holds src1 as binary16 and the row exponents.
  */
 int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst,
                        int64_t M, int64_t N, int64_t K,
@@ -155,11 +166,12 @@ int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst,
 
 /*
  * mm_mul_mat_f32 -- dst[M][N] = src1[M][K] . src0[N][K]^T, all f32 products,
- *   fp32 accumulation (vector FMA at M = 1; from M = 2 the fp32 MFMA when
- *   src0 is 16-byte aligned and K a multiple of 4).
- *   All pointers 4-byte aligned.  Any K >= 0.
- *   ws: mm_mul_mat_workspace_size(MM_TYPE_F32, ...) bytes (0 when that is
- *   0); from M = 2 it holds split-K partial sums.
+ *   fp32 accumulation.  The F32 x F32 kind of llama.cpp PR 1632 "mulmat
+ *   tune", Introduction.  Vector FMA at M = 1; from M = 2 the fp32 MFMA when
+ *   src0 and src1 are 16-byte aligned and K is a multiple of 4 (else the
+ *   vector kernel).  All pointers 4-byte aligned.  Any K >= 0.
+ *   ws: mm_mul_mat_workspace_size(MM_TYPE_F32, ...) bytes (0 at every shape
+ *   today; pass it anyway).
  */
 int mm_mul_mat_f32(const float* src0, const float* src1, float* dst,
                    int64_t M, int64_t N, int64_t K,

@@ -21,6 +21,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqsgemm.so")
+# bench.py's read-ceiling probe: a separate library, not part of the C ABI
+BENCH_SRC = os.path.join(ROOT, "bench_read.hip")
+BENCH_LIB = os.path.join(ROOT, "bench_read.so")
 
 HIP_SOURCES = ["api.hip", "quantize.hip", "q4_narrow.hip", "q4_mma.hip", "q4_skinny.hip",
                "q4_wide_i8.hip", "q4_wide16.hip", "f_kernels.hip"]
@@ -74,6 +77,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    if os.path.exists(BENCH_SRC):
+        tmp = BENCH_LIB + ".tmp"
+        _run([hipcc, *HIPCC_FLAGS, "-shared", BENCH_SRC, "-o", tmp])
+        os.replace(tmp, BENCH_LIB)
     return LIB
 
 

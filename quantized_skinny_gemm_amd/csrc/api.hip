@@ -101,21 +101,18 @@ int run_q4_0(const Plan& p, const void* src0, const float* src1, float* dst, int
   return q4_product(p, a, nullptr, s);
 }
 
-// Skinny F16 / F32 product: the MFMA kernel (into dst, or into the split
-// partials then the fixed-order reduce); rows that are not 16-byte aligned
-// take the narrow kernel's plan for the same shape instead.
+// Skinny F16 / F32 product: the MFMA kernel, one launch; operands that it
+// cannot take (not 16-byte aligned, K off its step) take the narrow kernel's
+// plan for the same shape instead.
 int run_f_mma(const Plan& p, int type, const void* src0, const float* src1, float* dst,
-              int64_t M, int64_t N, int64_t K, void* ws, hipStream_t s) {
-  if (!f_mma_aligned(type, src0, (int)K)) {
+              int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  if (!f_mma_ok(type, src0, src1, K)) {
     Plan q;
     const int st = make_plan(type, M, N, K, 1, &q);
     if (st != MM_OK) return st;
     return hip_status(launch_f_narrow(q, type, src0, src1, dst, (int)M, (int)N, (int)K, s));
   }
-  float* out = p.split > 1 ? reinterpret_cast<float*>((uint8_t*)ws + p.off_part) : dst;
-  hipError_t e = launch_f_mma(p, type, src0, src1, out, (int)M, (int)N, (int)K, s);
-  if (e == hipSuccess && p.split > 1) e = launch_splitk_reduce(out, dst, M * N, p.split, s);
-  return hip_status(e);
+  return hip_status(launch_f_mma(p, type, src0, src1, dst, (int)M, (int)N, (int)K, s));
 }
 
 int mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* dots,
@@ -138,7 +135,7 @@ int mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* 
     case KK_Q4_WIDE: return run_q4_0(p, src0, src1, dst, dots, M, N, K, n0, n1, ws, s);
     case KK_F_NARROW:
       return hip_status(launch_f_narrow(p, type, src0, src1, dst, (int)M, (int)N, (int)K, s));
-    case KK_F_MMA: return run_f_mma(p, type, src0, src1, dst, M, N, K, ws, s);
+    case KK_F_MMA: return run_f_mma(p, type, src0, src1, dst, M, N, K, s);
     case KK_F16_WIDE:
       return hip_status(launch_f16_wide(p, (const uint16_t*)src0, src1, dst, (int)M, (int)N,
                                         (int)K, ws, s));

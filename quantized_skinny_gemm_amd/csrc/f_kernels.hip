@@ -8,20 +8,20 @@
 // (four rows per wave for F16 beyond 8192 rows).  Rows of src1 beyond 16
 // are handled by further passes (grid.y).
 //
-// Skinny MFMA kernel (F16 at 2 <= M <= 16, F32 at M >= 2; rows 16-byte
-// aligned): passes of 16 src1 rows on the 16 x 16 matrix cores.  Each wave
-// owns 16 weight rows of a K slice and loads their 16-byte pieces straight
-// into MFMA operand order (no unpacking, no per-block epilogue: the weights
-// are the B operand as stored); the workgroup's src1 slice is staged in LDS
-// per sub-slice (128-512 k) and read by its 4 or 8 waves (both chosen in the
-// plan by type and row count).  F16 uses v_mfma_f32_16x16x32_f16 with src1
-// split into two binary16 terms hi + lo (their sum carries about 22 bits of
-// the f32 value; each f16 x f16 product is exact in fp32), F32 uses
-// v_mfma_f32_16x16x4_f32 on the values as they are.  K slices beyond one
-// go to split-K partials added by the fixed-order reduce kernel.
+// Skinny MFMA kernel (F16 at 2 <= M <= 16 and, with at most 8192 weight
+// rows, up to 64; F32 from M = 2; operands 16-byte aligned): one workgroup
+// per 16 weight rows and pass of 16 src1 rows, its waves splitting K and
+// adding their partial tiles in LDS at the end, so one launch does the whole
+// product.  The weights are the MFMA's A operand as stored (16-byte loads, no
+// conversion); src1 is the B operand, loaded straight into registers.  F16
+// uses v_mfma_f32_16x16x32_f16 with src1 split into two binary16 terms
+// hi + lo after a power-of-two scale per row and sub-slice (about 22
+// significant bits at any fp32 magnitude; each f16 x f16 product is exact in
+// fp32), F32 uses v_mfma_f32_16x16x4_f32 on the values as they are.
 //
-// Wide f16 kernel (M > 16): a dense contraction on v_mfma_f32_32x32x16_f16
-// with src1 rounded to binary16 while staging into LDS and fp32 accumulation.
+// Wide f16 kernel (M beyond that): a dense contraction on
+// v_mfma_f32_32x32x16_f16; src1 is rounded to binary16 once per call after a
+// power-of-two scale per row (undone on the outputs), fp32 accumulation.
 // bf16 is avoided: the pages note that at small sizes converting operands to
 // bf16 costs more than it gains (smallbard "Generer a plusieurs"), and its
 // 8-bit mantissa would also sit too close to the 1e-3 accuracy bound.
@@ -174,141 +174,183 @@ hipError_t launch_f_typed(const Plan& p, const WT* w, const float* x, float* dst
 // ------------------------------------------------------------ skinny MFMA (F16, F32)
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <bool kF16, int SUB_>
-struct FmCfg {
-  static constexpr int kSub = SUB_;                             // k per LDS sub-slice
-  static constexpr int kStep = kF16 ? 32 : 16;                  // k per MFMA step
-  static constexpr int kSteps = kSub / kStep;
-  static constexpr int kPitch = kSub + (kF16 ? 8 : 4);          // LDS row pitch (elements)
-  static constexpr int kLds = kF16 ? 2 * 16 * kPitch * 2 : 16 * kPitch * 4;
-};
+// Buffer resources: a lane whose byte offset lies at or past the end of the
+// range reads zeros and sends no request, which is how lanes of weight rows
+// past N, of src1 rows past M, of k past K and of steps past the wave's K run
+// skip their loads without a branch.
+constexpr int kSkip = 0x7FFFFFF0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ v4i f_bload(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 
-// Lane (l16, kq) of wave w: B operand column = weight row n0 + 16 w + l16; in
-// step s of a sub-slice starting at k0 it holds k = k0 + kStep s + 8 kq ..
-// +7 (F16) or k0 + kStep s + 4 kq .. +3 (F32: one element per 16x16x4 MFMA,
-// the same k in the A operand).  Output: rows m0 + 4 kq .. +3, column n.
-template <bool kF16, bool kVecX, int W, int SUB_>
-__global__ __launch_bounds__(64 * W, 2)
-void k_f_mma(const void* __restrict__ wv_, const float* __restrict__ x, float* __restrict__ out,
-             int M, int N, int K, int krange) {
-  typedef FmCfg<kF16, SUB_> C;
-  constexpr int SUB = C::kSub, XP = C::kPitch, ST = C::kStep, NSTEP = C::kSteps, NT = 64 * W;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[C::kLds];
+// One workgroup per RT x 16 weight rows and pass of 16 src1 rows (grid.y);
+// its W waves split K into runs of `spw` steps and add their partial tiles in
+// LDS at the end, in wave order (DeepSpeed-Inference notes, III.C: partial
+// sums reduced on chip rather than by another kernel).  A step is 32 k (F16)
+// or 16 k (F32): one 16-byte weight piece per lane and row tile.  Lane
+// (l16, kq) holds weight rows n0 + 16 i + l16 (i < RT) and src1 row m0 + l16
+// at k = step * STEP + P * kq .. + P - 1 (P = 8 for F16, 4 for F32).  The
+// products run on v_mfma_f32_16x16x4_f32, element j of every lane's piece in
+// MFMA j: the weights (binary16 widened to fp32, exact) are the A operand,
+// src1 as it is the B operand, shared by the RT row tiles; every product is
+// an exact fp32 product of the given values, so no magnitude of src1 is
+// lost to a narrower format.  Output lane (l16, kq) of tile i holds
+// dst[m0 + l16][n0 + 16 i + 4 kq + r].
+template <bool kF16, int W, int S, int RT>
+__global__ __launch_bounds__(64 * W) void k_f_skinny(const void* __restrict__ w_,
+                                                     const float* __restrict__ x,
+                                                     float* __restrict__ dst, int M, int N, int K,
+                                                     int spw) {
+  constexpr int ES = kF16 ? 2 : 4;                 // bytes per weight
+  constexpr int P = kF16 ? 8 : 4;                  // k per lane and step
+  constexpr int STEP = 4 * P;                      // k per step
+  constexpr int XL = P / 4;                        // 16-byte src1 loads per lane and step
+  __shared__ v4f red[W][RT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kq = lane >> 4;
-  const int m0 = blockIdx.y * 16, z = blockIdx.z;
-  const int n = blockIdx.x * (16 * W) + 16 * wave + l16;
-  const int nr = n < N ? n : N - 1;
-  const int kbeg = z * krange;
-  const int kend = kbeg + krange < K ? kbeg + krange : K;
-  const uint8_t* wrow = reinterpret_cast<const uint8_t*>(wv_) + (int64_t)nr * K * (kF16 ? 2 : 4);
-  float* o = out + (int64_t)z * M * N;               // the slice's partial (dst when one slice)
-  const int kl = kF16 ? 8 * kq : 4 * kq;             // this lane's k offset within a step
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int n0 = blockIdx.x * (16 * RT), m0 = blockIdx.y * 16;
+  const int nrows = N - n0 < 16 * RT ? N - n0 : 16 * RT;
+  const int mrows = M - m0 < 16 ? M - m0 : 16;
+  const __amdgpu_buffer_rsrc_t rw =
+      f_rsrc(reinterpret_cast<const uint8_t*>(w_) + (int64_t)n0 * K * ES, nrows * K * ES);
+  const __amdgpu_buffer_rsrc_t rx = f_rsrc(x + (int64_t)m0 * K, mrows * K * 4);
+  const bool xok = l16 < mrows;
+  const int nsteps = (K + STEP - 1) / STEP;
+  const int s0 = wave * spw;
+  const int s1 = s0 + spw < nsteps ? s0 + spw : nsteps;
 
-  constexpr int IT = 16 * SUB / 4 / NT;               // src1 float4 items per thread
-  static_assert(IT * NT == 16 * SUB / 4, "src1 items must fill the threads");
-  for (int k0 = kbeg; k0 < kend; k0 += SUB) {
-    // src1 rows m0 .. m0+15, k0 .. k0+SUB-1 first (their wait then leaves
-    // the weights in flight), clamped into range and zeroed past M and kend
-    // (kend % 4 == 0: an item is wholly in or out)
-    float4 xv[IT];
+  auto load = [&](v4i (&wv)[S][RT], v4i (&xv)[S][XL], int s) {
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int i = tid + NT * it;
-      const int r = i / (SUB / 4), c = i % (SUB / 4);
-      const int m = m0 + r < M ? m0 + r : M - 1, k = k0 + 4 * c < kend ? k0 + 4 * c : kbeg;
-      const float* px = x + (int64_t)m * K + k;
-      if (kVecX) {
-        xv[it] = *reinterpret_cast<const float4*>(px);
-      } else {
-        xv[it] = make_float4(px[0], px[1], px[2], px[3]);
+    for (int t = 0; t < S; ++t) {
+      const int k = (s + t) * STEP + P * kq;
+      const bool in = s + t < s1 && k < K;           // K % P == 0: a piece is whole
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+        wv[t][i] = f_bload(rw, in && 16 * i + l16 < nrows ? ((16 * i + l16) * K + k) * ES : kSkip);
+#pragma unroll
+      for (int h = 0; h < XL; ++h)
+        xv[t][h] = f_bload(rx, in && xok ? (l16 * K + k + 4 * h) * 4 : kSkip);
+    }
+  };
+
+  v4f acc[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const v4i (&wv)[S][RT], const v4i (&xv)[S][XL]) {
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      float b[P];
+#pragma unroll
+      for (int h = 0; h < XL; ++h) {
+        const v4f f = __builtin_bit_cast(v4f, xv[t][h]);
+        b[4 * h] = f.x; b[4 * h + 1] = f.y; b[4 * h + 2] = f.z; b[4 * h + 3] = f.w;
+      }
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        float a[P];
+        if constexpr (kF16) {
+          const uint32_t u[4] = {(uint32_t)wv[t][i].x, (uint32_t)wv[t][i].y, (uint32_t)wv[t][i].z,
+                                 (uint32_t)wv[t][i].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            a[2 * j] = f16_bits_to_f32(u[j]);
+            a[2 * j + 1] = f16_bits_to_f32(u[j] >> 16);
+          }
+        } else {
+          const v4f f = __builtin_bit_cast(v4f, wv[t][i]);
+          a[0] = f.x; a[1] = f.y; a[2] = f.z; a[3] = f.w;
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc[i], 0, 0, 0);
       }
     }
-    // this lane's 16 weight pieces of the sub-slice (past kend: clamped,
-    // then zeroed)
-    v4i wp[NSTEP];
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      const int k = k0 + ST * s + kl;
-      const int kc = k < kend ? k : 0;
-      wp[s] = *(const __attribute__((address_space(1))) v4i*)(wrow + (int64_t)kc * (kF16 ? 2 : 4));
-    }
-    __syncthreads();                                 // the last sub-slice's LDS reads are done
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int i = tid + NT * it;
-      const int r = i / (SUB / 4), c = i % (SUB / 4);
-      const bool ok = m0 + r < M && k0 + 4 * c < kend;
-      const float v[4] = {ok ? xv[it].x : 0.0f, ok ? xv[it].y : 0.0f, ok ? xv[it].z : 0.0f,
-                          ok ? xv[it].w : 0.0f};
-      if constexpr (kF16) {
-        _Float16* xh = reinterpret_cast<_Float16*>(xs);
-        _Float16* xl = xh + 16 * XP;
-        v4h hi, lo;
-        hi.x = (_Float16)v[0]; hi.y = (_Float16)v[1]; hi.z = (_Float16)v[2]; hi.w = (_Float16)v[3];
-        lo.x = (_Float16)(v[0] - (float)hi.x); lo.y = (_Float16)(v[1] - (float)hi.y);
-        lo.z = (_Float16)(v[2] - (float)hi.z); lo.w = (_Float16)(v[3] - (float)hi.w);
-        *reinterpret_cast<v4h*>(xh + r * XP + 4 * c) = hi;
-        *reinterpret_cast<v4h*>(xl + r * XP + 4 * c) = lo;
-      } else {
-        float* xf = reinterpret_cast<float*>(xs);
-        *reinterpret_cast<float4*>(xf + r * XP + 4 * c) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      const bool in = k0 + ST * s + kl < kend;
-      v4i b = wp[s];
-      b.x = in ? b.x : 0; b.y = in ? b.y : 0; b.z = in ? b.z : 0; b.w = in ? b.w : 0;
-      if constexpr (kF16) {
-        const _Float16* xh = reinterpret_cast<const _Float16*>(xs);
-        const _Float16* xl = xh + 16 * XP;
-        const v8h bh = __builtin_bit_cast(v8h, b);
-        const v8h ah = *reinterpret_cast<const v8h*>(xh + l16 * XP + ST * s + kl);
-        const v8h al = *reinterpret_cast<const v8h*>(xl + l16 * XP + ST * s + kl);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
-      } else {
-        const float* xf = reinterpret_cast<const float*>(xs);
-        const float4 a4 = *reinterpret_cast<const float4*>(xf + l16 * XP + ST * s + kl);
-        // whole-vector bit cast (a bit cast of one element lvalue of an
-        // ext_vector reads element 0 with this compiler)
-        const v4f bf = __builtin_bit_cast(v4f, b);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, bf[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, bf[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, bf[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, bf[3], acc, 0, 0, 0);
-      }
-    }
+  };
+
+  // two register sets: the next sub-slice's loads are in flight while one
+  // is computed.  The loads are issued unconditionally (past the run they
+  // send no request): a load under a branch would make the compiler wait
+  // for it before the current sub-slice's MFMAs.  (The plan makes every run
+  // a whole number of sub-slice pairs; past K the pair computes zeros.)
+  v4i w0[S][RT], w1[S][RT], x0[S][XL], x1[S][XL];
+  load(w0, x0, s0);
+  for (int s = s0; s < s1; s += 2 * S) {
+    load(w1, x1, s + S);
+    __builtin_amdgcn_sched_barrier(0);               // keep the loads ahead of the MFMAs
+    compute(w0, x0);
+    load(w0, x0, s + 2 * S);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w1, x1);
   }
+
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = m0 + 4 * kq + r;
-    if (m < M && n < N) o[(int64_t)m * N + n] = acc[r];
+  for (int i = 0; i < RT; ++i) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  if (wave >= RT) return;
+  // wave i adds row tile i's partial tiles in wave order
+  const int i = wave;
+  v4f v = red[0][i][lane];
+#pragma unroll
+  for (int u = 1; u < W; ++u) v += red[u][i][lane];
+  const int m = m0 + l16, n = n0 + 16 * i + 4 * kq;
+  if (m >= M) return;
+  float* o = dst + (int64_t)m * N + n;
+  if (n + 3 < N && ((uintptr_t)o & 15) == 0) {
+    *reinterpret_cast<v4f*>(o) = v;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) o[r] = v[r];
   }
 }
 
 // ------------------------------------------------------------ wide f16
 
-// src1 -> binary16 (round to nearest even), [M][K] as given; the wide
-// kernel's A operand.  Four values per thread when src1 is 16-byte aligned
-// and the count a multiple of four.
+// src1 -> binary16 with one power of two per row: row m is scaled by 2^e[m]
+// so that its largest magnitude lies in [2^14, 2^15), then rounded to
+// binary16 (nearest even); the product kernel scales its outputs back by
+// 2^-e[m] (exact).  Without the scale, rows below about 1e-5 would fall on
+// binary16's subnormal grid and rows past 65504 would overflow.  One
+// workgroup per row; four values per load when the row is 16-byte aligned.
 template <bool kVec>
-__global__ __launch_bounds__(256) void k_f32_to_f16(const float* __restrict__ x,
-                                                    uint16_t* __restrict__ y, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
+__global__ __launch_bounds__(256) void k_f32_to_f16_rows(const float* __restrict__ x,
+                                                         uint16_t* __restrict__ y,
+                                                         int* __restrict__ rexp, int K) {
+  __shared__ float wmax[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float* xr = x + (int64_t)m * K;
+  uint16_t* yr = y + (int64_t)m * K;
+  float amax = 0.0f;
   if (kVec) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; 4 * i < n; i += stride) {
-      const float4 f = reinterpret_cast<const float4*>(x)[i];
-      v4h hv;
-      hv.x = (_Float16)f.x; hv.y = (_Float16)f.y; hv.z = (_Float16)f.z; hv.w = (_Float16)f.w;
-      reinterpret_cast<v4h*>(y)[i] = hv;
+    for (int i = tid; 4 * i < K; i += 256) {
+      const float4 f = reinterpret_cast<const float4*>(xr)[i];
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
     }
   } else {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
-      y[i] = (uint16_t)f32_to_f16_bits(x[i]);
+    for (int i = tid; i < K; i += 256) amax = fmaxf(amax, fabsf(xr[i]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int e = 15 - __builtin_amdgcn_frexp_expf(amax);
+  if (tid == 0) rexp[m] = e;
+  if (kVec) {
+    for (int i = tid; 4 * i < K; i += 256) {
+      const float4 f = reinterpret_cast<const float4*>(xr)[i];
+      v4h hv;
+      hv.x = (_Float16)__builtin_amdgcn_ldexpf(f.x, e);
+      hv.y = (_Float16)__builtin_amdgcn_ldexpf(f.y, e);
+      hv.z = (_Float16)__builtin_amdgcn_ldexpf(f.z, e);
+      hv.w = (_Float16)__builtin_amdgcn_ldexpf(f.w, e);
+      reinterpret_cast<v4h*>(yr)[i] = hv;
+    }
+  } else {
+    for (int i = tid; i < K; i += 256) yr[i] = (uint16_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(xr[i], e));
   }
 }
 
@@ -320,6 +362,7 @@ __global__ __launch_bounds__(256) void k_f32_to_f16(const float* __restrict__ x,
 template <int BM, int BN, bool kVec, int KS>
 __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w,
                                                   const uint16_t* __restrict__ xh,
+                                                  const int* __restrict__ rexp,
                                                   float* __restrict__ dst, int M, int N, int K,
                                                   int tiles_m, int tiles_n) {
   constexpr int HP = KS + 8;         // halves per LDS row (pad)
@@ -433,7 +476,7 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * WTM + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-        if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][j][r];
+        if (m < M && n < N) dst[(int64_t)m * N + n] = __builtin_amdgcn_ldexpf(acc[i][j][r], -rexp[m]);
       }
     }
 }
@@ -474,53 +517,51 @@ hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* 
 
 hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, float* dst, int M,
                            int N, int K, void* ws, hipStream_t s) {
-  // src1 -> binary16 into the workspace, then the tiled product
+  // src1 -> binary16 (a power of two per row) into the workspace, then the
+  // tiled product
   uint16_t* xh = reinterpret_cast<uint16_t*>((uint8_t*)ws + p.off_ah);
-  const int64_t n = (int64_t)M * K;
-  const bool cvec = (uintptr_t)x % 16 == 0 && n % 4 == 0;
-  int64_t cgrid = ((cvec ? n / 4 : n) + 255) / 256;
-  if (cgrid > 4096) cgrid = 4096;
-  if (cvec) hipLaunchKernelGGL((k_f32_to_f16<true>), dim3((unsigned)cgrid), dim3(256), 0, s, x, xh, n);
-  else hipLaunchKernelGGL((k_f32_to_f16<false>), dim3((unsigned)cgrid), dim3(256), 0, s, x, xh, n);
+  int* rexp = reinterpret_cast<int*>((uint8_t*)ws + p.off_rexp);
+  const bool cvec = (uintptr_t)x % 16 == 0 && K % 4 == 0;
+  if (cvec) hipLaunchKernelGGL((k_f32_to_f16_rows<true>), dim3((unsigned)M), dim3(256), 0, s, x, xh, rexp, K);
+  else hipLaunchKernelGGL((k_f32_to_f16_rows<false>), dim3((unsigned)M), dim3(256), 0, s, x, xh, rexp, K);
   const bool vec = (K % 8 == 0) && ((uintptr_t)w % 16 == 0);    // xh is 256-byte aligned
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
   if (p.bm == 128) {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true, 64>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<128, 128, false, 64>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true, 64>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<128, 128, false, 64>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
   } else {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true, 128>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<64, 64, false, 128>), grid, dim3(256), 0, s, w, xh, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true, 128>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<64, 64, false, 128>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
   }
   return hipGetLastError();
 }
 
-bool f_mma_aligned(int type, const void* w, int K) {
-  return (uintptr_t)w % 16 == 0 && K % (type == MM_TYPE_F16 ? 8 : 4) == 0;
+bool f_mma_ok(int type, const void* w, const float* x, int64_t K) {
+  // 16-byte pieces of both operands; 32-bit buffer offsets over 16 rows
+  return (uintptr_t)w % 16 == 0 && (uintptr_t)x % 16 == 0 &&
+         K % (type == MM_TYPE_F16 ? 8 : 4) == 0 && K <= kFMmaMaxK;
 }
 
-template <bool kF16, int W, int SUB>
-hipError_t launch_f_mma_cfg(const Plan& p, const void* w, const float* x, float* out, int M, int N,
+template <bool kF16, int W, int S, int RT>
+hipError_t launch_f_mma_cfg(const Plan& p, const void* w, const float* x, float* dst, int M, int N,
                             int K, hipStream_t s) {
-  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)p.split);
-  const int kr = (int)p.kchunk;
-  if ((uintptr_t)x % 16 == 0)
-    hipLaunchKernelGGL((k_f_mma<kF16, true, W, SUB>), grid, dim3(64 * W), 0, s, w, x, out, M, N, K, kr);
-  else
-    hipLaunchKernelGGL((k_f_mma<kF16, false, W, SUB>), grid, dim3(64 * W), 0, s, w, x, out, M, N, K, kr);
+  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m);
+  hipLaunchKernelGGL((k_f_skinny<kF16, W, S, RT>), grid, dim3(64 * W), 0, s, w, x, dst, M, N, K,
+                     (int)p.kchunk);
   return hipGetLastError();
 }
 
-hipError_t launch_f_mma(const Plan& p, int type, const void* w, const float* x, float* out, int M,
+hipError_t launch_f_mma(const Plan& p, int type, const void* w, const float* x, float* dst, int M,
                         int N, int K, hipStream_t s) {
-  // (waves, k per sub-slice) as the plan chose them
-  if (type == MM_TYPE_F16) {
-    if (p.waves == 8 && p.bn == 512) return launch_f_mma_cfg<true, 8, 512>(p, w, x, out, M, N, K, s);
-    if (p.waves == 8 && p.bn == 256) return launch_f_mma_cfg<true, 8, 256>(p, w, x, out, M, N, K, s);
-  } else {
-    if (p.waves == 4 && p.bn == 128) return launch_f_mma_cfg<false, 4, 128>(p, w, x, out, M, N, K, s);
-    if (p.waves == 8 && p.bn == 128) return launch_f_mma_cfg<false, 8, 128>(p, w, x, out, M, N, K, s);
-  }
+  // (waves, steps per sub-slice, row tiles) as the plan chose them
+  const bool f16 = type == MM_TYPE_F16;
+#define QSG_FCFG(W_, S_, RT_)                                                                \
+  if (p.waves == W_ && p.bn == S_ && p.rpw == 16 * RT_)                                      \
+    return f16 ? launch_f_mma_cfg<true, W_, S_, RT_>(p, w, x, dst, M, N, K, s)               \
+               : launch_f_mma_cfg<false, W_, S_, RT_>(p, w, x, dst, M, N, K, s);
+  QSG_FCFG(4, 2, 1) QSG_FCFG(8, 2, 1) QSG_FCFG(4, 2, 2)
+#undef QSG_FCFG
   return hipErrorInvalidValue;
 }
 

@@ -75,14 +75,15 @@ hipError_t launch_q4_mma(const Plan& p, const Q4Args& a, hipStream_t s);
 
 hipError_t launch_f_narrow(const Plan& p, int type, const void* w, const float* x, float* dst,
                            int M, int N, int K, hipStream_t s);
-// src1 is converted to binary16 into ws + p.off_ah ([M][K]) first.
+// src1 is converted to binary16 into ws + p.off_ah ([M][K]) first, with a
+// power of two per row (exponents at ws + p.off_rexp) undone on dst.
 hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, float* dst, int M,
                            int N, int K, void* ws, hipStream_t s);
-// Skinny F16 / F32 MFMA kernel; needs f_mma_aligned() (src0 16-byte aligned,
-// K a multiple of 8 (F16) or 4 (F32)).  out = dst (one K slice) or the
-// partials [split][M][N].
-bool f_mma_aligned(int type, const void* w, int K);
-hipError_t launch_f_mma(const Plan& p, int type, const void* w, const float* x, float* out, int M,
+// Skinny F16 / F32 MFMA kernel (one launch, no workspace); needs f_mma_ok():
+// src0 and src1 16-byte aligned, K a multiple of 8 (F16) or 4 (F32), K <=
+// kFMmaMaxK.
+bool f_mma_ok(int type, const void* w, const float* x, int64_t K);
+hipError_t launch_f_mma(const Plan& p, int type, const void* w, const float* x, float* dst, int M,
                         int N, int K, hipStream_t s);
 hipError_t launch_zero(float* dst, int64_t n, hipStream_t s);
 // dst[i] = sum over z = 0..split-1, in that order, of part[z * n + i].

@@ -245,48 +245,40 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   const bool f16 = type == MM_TYPE_F16;
   // F16 from 17 rows: the wide kernel, except up to 64 rows with at most
   // 8192 weight rows, where its 64 x 64 tiles give too few workgroups and
-  // passes of the skinny kernel are faster (4096 x 4096: M = 32 17.0 against
-  // 39.6 us, M = 64 23.7 against 39.9; 11008 rows tie at M = 32, 14336 rows
-  // favour the wide kernel at M = 64: 45.5 against 74.2).
+  // passes of the skinny kernel are faster (4096 x 4096: M = 32 17.8 against
+  // 39.6 us, M = 64 33.1 against 39.9; 14336 rows favour the wide kernel).
   const bool wide = f16 && (variant == 2 || (variant == 0 && M > kNarrowFMaxM && (M > 64 || N > 8192)));
-  // F16 at M = 2 with at most 8192 rows stays on the narrow kernel (us per
-  // call against the matrix cores: 4096 x 4096 11.2 / 12.4, 8192 x 4096
-  // 16.2 / 19.9, 4096 x 11008 26.2 / 30.7; 11008 x 4096 ties at 24.3).
-  const bool f16_narrow2 = f16 && M == 2 && N <= 8192;
-  const bool fmma = !wide && (variant == 3 || (variant == 0 && M >= 2 && !f16_narrow2));
+  const bool fmma = !wide && (variant == 3 || (variant == 0 && M >= 2));
   if (fmma) {
     p->kind = KK_F_MMA;
     p->variant = 3;
     p->mt = 16;
-    // Waves (16 weight rows each) per workgroup and k per LDS sub-slice
-    // (p->bn), as measured at M = 4 and 16 (us, before -> after): F16 at
-    // more than 8192 rows 256 instead of 512 (11008 x 4096: 28.2 -> 24.5);
-    // F32 128 instead of 256, with 4 waves up to 8192 rows (4096 x 4096:
-    // 23.3 -> 19.5) and 8 beyond (11008 x 4096: 49.3 -> 45.5).
-    if (f16) { p->waves = 8; p->bn = N > 8192 ? 256 : 512; }
-    else { p->waves = N > 8192 ? 8 : 4; p->bn = 128; }
+    // One workgroup per 16 weight rows (32 when src1 takes several 16-row
+    // passes, which then share each src1 load between two row tiles) and
+    // pass; its waves split K into runs of whole MFMA steps (32 k for F16,
+    // 16 k for F32) and add their partial tiles in LDS, so no K slice goes
+    // through the workspace.  8 waves of two-step sub-slices, 4 with 32-row
+    // workgroups (us per call, against the best of 4 / 8 / 16 waves and
+    // 2 / 4 steps: F32 4096 x 4096 M = 4 14.6, M = 16 18.9; 11008 x 4096
+    // M = 4 38.8, M = 16 52.3; F16 11008 x 4096 M = 4 26.2; F16 4096 x 4096
+    // M = 4 10.7 against 10.6, M = 16 14.7 against 14.0; M = 32 / 64 with
+    // 32-row workgroups: F16 17.8 / 33.1 against 24.6 / 45.6 with 16 rows).
+    const int rt = M > 16 ? 2 : 1;
+    p->rpw = 16 * rt;                                  // weight rows per workgroup
     p->tiles_m = ceil_div(M, 16);
-    p->tiles_n = ceil_div(N, 16 * p->waves);
-    // K slices of whole sub-slices until there are about two workgroups per
-    // CU (each slice adds M * N partial sums, written and read once)
-    const int64_t sub = p->bn;
-    const int64_t subs = ceil_div(K, sub);
-    int64_t split = 1;
-    if (allow_split) {
-      const int64_t wgs = p->tiles_m * p->tiles_n;
-      split = ceil_div(2 * kCUs, wgs);
-      if (split > subs) split = subs;
-      if (split > 16) split = 16;
-      if (split < 1) split = 1;
-    }
-    p->kchunk = ceil_div(subs, split) * sub;           // elements per slice
-    p->split = (int)ceil_div(K, p->kchunk);
-    size_t off = 0;
-    if (p->split > 1) {
-      p->off_part = off;
-      off = align_up(off + (size_t)p->split * (size_t)M * (size_t)N * 4, 256);
-    }
-    p->ws_bytes = off;
+    p->tiles_n = ceil_div(N, p->rpw);
+    const int64_t step = f16 ? 32 : 16;
+    const int64_t steps = ceil_div(K, step);
+    p->bn = 2;                                         // steps per sub-slice
+    int w = rt == 1 ? 8 : 4;
+    while (w > 1 && steps < 2 * p->bn * w) w /= 2;     // every wave at least one sub-slice pair
+    if (w < 4) w = 4;
+    p->waves = w;
+    // steps per wave: a whole number of sub-slice pairs (the kernel's two
+    // register sets)
+    p->kchunk = ceil_div(ceil_div(steps, w), 2 * p->bn) * 2 * p->bn;
+    p->split = 1;
+    p->ws_bytes = 0;
     return MM_OK;
   }
   if (!wide) {
@@ -314,9 +306,11 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       p->tiles_n = ceil_div(N, p->bn);
     }
     p->kchunk = K;
-    // src1 as binary16 [M][K], converted once (not per tile and stage)
+    // src1 as binary16 [M][K], converted once (not per tile and stage), and
+    // its power-of-two exponent per row
     p->off_ah = 0;
-    p->ws_bytes = align_up((size_t)M * (size_t)K * 2, 256);
+    p->off_rexp = align_up((size_t)M * (size_t)K * 2, 256);
+    p->ws_bytes = align_up(p->off_rexp + (size_t)M * 4, 256);
     return MM_OK;
   }
   p->ws_bytes = 0;

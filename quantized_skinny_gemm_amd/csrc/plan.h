@@ -31,6 +31,7 @@ constexpr int kNarrowMaxLds = 65536; // LDS bytes the narrow kernel may stage ac
 constexpr int kNarrowMaxGrid = 768;  // narrow workgroups along N (3 per CU)
 constexpr int kMmaMaxM = 32;       // largest M the skinny MFMA kernel takes by default
 constexpr int kSkinnyPairs = 4;    // skinny kernel: block pairs per wave phase
+constexpr int64_t kFMmaMaxK = 1 << 23;  // skinny F kernel: 32-bit buffer offsets over 32 rows
 constexpr int kMmaWaves = 8;       // waves per workgroup of the skinny kernel for unaligned
                                    // weights or K % 64 != 0 (32 rows per workgroup)
 
@@ -43,7 +44,8 @@ enum KernelKind {
   KK_F16_WIDE = 5,
   KK_Q4_MMA = 6,    // skinny Q4_0 on int8 MFMA (16 weight rows per workgroup)
   KK_Q4_WIDE16 = 7, // wide Q4_0 on fp16 MFMA with exact block dots
-  KK_F_MMA = 8,     // skinny F16 / F32 on the 16x16 MFMA (passes of 16 src1 rows)
+  KK_F_MMA = 8,     // skinny F16 / F32 on the 16x16 MFMA (16 weight rows per workgroup,
+                    // passes of 16 src1 rows, waves split K)
 };
 
 struct Plan {
@@ -55,7 +57,7 @@ struct Plan {
   int rpw = 1;              // src0 rows per wave (skinny MFMA: per workgroup)
   int waves = 4;            // waves per workgroup (skinny MFMA: they split K)
   // wide kernels
-  int bm = 0, bn = 0, waves_m = 0, waves_n = 0;   // (skinny F MFMA kernel: bn = k per LDS sub-slice)
+  int bm = 0, bn = 0, waves_m = 0, waves_n = 0;   // (skinny F MFMA kernel: bn = steps per sub-slice)
   // grid
   int64_t tiles_m = 1;      // wide: output tile rows; narrow: passes over M
   int64_t tiles_n = 1;      // output tile columns (narrow: row groups of waves*rpw src0 rows)
@@ -64,10 +66,13 @@ struct Plan {
   bool fuse = false;        // narrow Q4_0: quantize src1 inside the product kernel
   int fuse_rpw = 2, fuse_waves = 8;  // fused kernel: rows per wave and waves per workgroup
   int64_t fuse_grid = 0;    // fused kernel: workgroups along N
-  int64_t kchunk = 0;       // K per split (Q4 narrow: units; Q4 wide / skinny: blocks; F: elements)
+  int64_t kchunk = 0;       // K per split (Q4 narrow: units; Q4 wide / skinny: blocks;
+                            // skinny F: MFMA steps per wave)
   // workspace layout (bytes)
   size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0;
   size_t off_ah = 0;        // wide kernel: Q8_0 codes as binary16 [M][K] (0: not written)
+                            // (wide F16 kernel: src1 as binary16 [M][K])
+  size_t off_rexp = 0;      // wide F16 kernel: int32 [M] power-of-two exponent per src1 row
   size_t off_sq = 0, off_ss = 0;   // skinny MFMA kernel: its operand-order codes and scales
                                    // (0: not written)
   int64_t sk_rows = 0;      // skinny layout: src1 rows padded to 16-row tiles

@@ -1,22 +1,22 @@
 """Summaries of rocprofv3 output (CSV format) for the kernels of this library.
 
-    python -m quantized_skinny_gemm_amd.rocprof_summary stats DIR
+    python rocprof_summary.py stats DIR
         Per-kernel table from DIR's *_kernel_stats.csv (calls, average and
         total duration), as markdown.
 
-    python -m quantized_skinny_gemm_amd.rocprof_summary shapes DIR [--only SUBSTR]
+    python rocprof_summary.py shapes DIR [--only SUBSTR]
         Per (kernel, grid) table from DIR's *_kernel_trace.csv: the same
         kernel launched at different shapes gets one row per grid, with the
         number of dispatches and their median and minimum duration.
 
-    python -m quantized_skinny_gemm_amd.rocprof_summary counters DIR [DIR ...] [--only SUBSTR]
+    python rocprof_summary.py counters DIR [DIR ...] [--only SUBSTR]
         Per (kernel, grid) averages per dispatch of every counter in the
         DIRs' *_counter_collection.csv (one --pmc pass per DIR), with the
         ratios that read directly: VALU and LDS instructions and MFMAs per
         wave, share of wave cycles waiting on a dependency, share of LDS
         cycles lost to bank conflicts.
 
-    python -m quantized_skinny_gemm_amd.rocprof_summary traffic \\
+    python rocprof_summary.py traffic \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --kernel SUBSTR --copy-bytes B --source FILE --algo-bytes A --out JSON
         HBM bytes per dispatch of the kernels whose name contains SUBSTR, from

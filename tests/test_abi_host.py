@@ -154,22 +154,23 @@ def test_dispatch_threshold_and_workspace(m):
         # MFMA), 16 or 32 src1 rows
         assert rows == (8 if m <= 8 else 16 if m <= 16 else 32) and cols in (4, 8, 16)
         assert split == 1
-    # F16: M = 1 narrow (and M = 2 up to 8192 rows), up to 16 rows the
-    # skinny MFMA kernel (K slices through the workspace), beyond the wide
-    # kernel; F32: narrow at M = 1, skinny MFMA from 2 rows
+    # F16: M = 1 narrow, up to 16 rows the skinny MFMA kernel, beyond the
+    # wide kernel; F32: narrow at M = 1, skinny MFMA from 2 rows
     for t in (F16, F32):
         fv, fsplit, frows, fcols, flaunch = qs.dispatch(t, m, 4096, 4096)
         # (F16 up to 64 rows at this N = 4096 also takes the skinny kernel)
-        fwant = 1 if (m == 1 or (m == 2 and t == F16)) else 3 if (m <= 64 or t == F32) else 2
+        fwant = 1 if m == 1 else 3 if (m <= 64 or t == F32) else 2
         assert fv == fwant
         if fv == 3:
-            # 16-row passes; workgroups of 8 waves (F32 up to 8192 rows: 4)
-            assert frows == 16 and fcols == (4 if t == F32 else 8)
-            assert flaunch == 1 + (1 if fsplit > 1 else 0)
-            assert qs.workspace_size(t, m, 4096, 4096) >= (fsplit * m * 4096 * 4 if fsplit > 1 else 0)
+            # 16-row passes, workgroups of 4 to 16 waves that split K among
+            # themselves: one launch, no workspace
+            assert frows == 16 and fcols in (4, 8, 16)
+            assert fsplit == 1 and flaunch == 1
+            assert qs.workspace_size(t, m, 4096, 4096) == 0
         elif fv == 2:
-            # the wide F16 kernel converts src1 to binary16 in the workspace
-            assert fsplit == 1 and qs.workspace_size(t, m, 4096, 4096) >= m * 4096 * 2
+            # the wide F16 kernel converts src1 to binary16 in the workspace,
+            # with one power-of-two exponent per row
+            assert fsplit == 1 and qs.workspace_size(t, m, 4096, 4096) >= m * 4096 * 2 + 4 * m
         else:
             assert fsplit == 1 and qs.workspace_size(t, m, 4096, 4096) == 0
 
@@ -250,6 +251,9 @@ def test_measured_tile_and_wave_choices():
     assert qs.dispatch(F32, 1, 11008, 4096)[3] == 1
     assert qs.dispatch(F16, 1, 4096, 4096)[3] == 1
     assert qs.dispatch(F16, 1, 11008, 4096)[3] == 4
-    # skinny F MFMA: waves per workgroup (F32 beyond 8192 rows: 8)
+    # skinny F MFMA: 8 waves per 16-row workgroup in one pass, 4 per 32-row
+    # workgroup when src1 takes several passes; fewer only for short K
     assert qs.dispatch(F32, 4, 11008, 4096)[3] == 8
     assert qs.dispatch(F16, 16, 11008, 4096)[3] == 8
+    assert qs.dispatch(F16, 40, 4096, 4096)[3] == 4
+    assert qs.dispatch(F16, 4, 100, 64)[3] == 4

@@ -428,3 +428,74 @@ def test_grouped_products(m):
         if n >= 4096:                       # same plan (no split): the same bits
             assert bool(torch.equal(out, single))
         assert_close(to_host(out), mul_mat.mul_mat_q4_0_f32_dequant(wq, x), TOL_Q4_0, f"group n={n}")
+
+
+# ------------------------------------------------------- F16 src1 range
+# Row scales from far below binary16's normal range to far above its largest
+# value, in one batch; an all-zero row among them.  Every F16 path (narrow,
+# skinny MFMA in one or several 16-row passes, wide MFMA) must stay within
+# the F16 bound on every row, as F32 does.
+ROW_SCALES = [1e-30, 1e-7, 1e-5, 1e-3, 1.0, 1e3, 1e5, 0.0, 1e30]
+
+
+def _scaled_rows(m, k, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    scales = np.array([ROW_SCALES[i % len(ROW_SCALES)] for i in range(m)], dtype=np.float32)
+    return (x * scales[:, None]).astype(np.float32)
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (2, 8200, 4096), (2, 4096, 4096), (4, 4096, 4096), (16, 4096, 4096), (17, 4096, 4096),
+    (17, 9000, 1024), (64, 4096, 1024), (64, 8500, 512), (512, 640, 512), (5, 300, 1000),
+])
+def test_f16_src1_row_scales(m, n, k):
+    qs = _qs()
+    rng = np.random.default_rng(m * 31 + n + k)
+    wh = (rng.standard_normal((n, k)) * 0.02).astype(np.float16)
+    x = _scaled_rows(m, k, 1000 + m)
+    kind = qs.dispatch(qs.MM_TYPE_F16, m, n, k)[0]
+    say("f16 row scales", m, n, k, "variant", kind)
+    y = to_host(qs.mul_mat_f16_f32(to_dev(wh), to_dev(x)))
+    assert_close(y, mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 scaled rows {m}x{n}x{k}")
+    for v in (1, 2, 3):
+        yv, _ = qs.debug_mul_mat(qs.MM_TYPE_F16, to_dev(wh), to_dev(x), v)
+        assert_close(to_host(yv), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 scaled rows variant {v}")
+    w = wh.astype(np.float32)
+    y32 = to_host(qs.mul_mat_f32(to_dev(w), to_dev(x)))
+    assert_close(y32, mul_mat.mul_mat_f32(w, x), TOL_F, f"f32 scaled rows {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n", [(16, 4096), (40, 4096), (100, 11008)])
+def test_f16_batch_vs_alone(m, n):
+    """Row i of a batched F16 product equals the M = 1 product of that row
+    (smallbard 'La courbe': a sequence gives in a batch what it gives alone),
+    for rows of very different magnitudes."""
+    qs = _qs()
+    k = 4096
+    rng = np.random.default_rng(m + n)
+    wh = (rng.standard_normal((n, k)) * 0.02).astype(np.float16)
+    x = _scaled_rows(m, k, 77 + m)
+    say("f16 batch vs alone", m, n)
+    full = to_host(qs.mul_mat_f16_f32(to_dev(wh), to_dev(x)))
+    for i in range(0, m, max(1, m // 12)):
+        if not np.any(x[i]):
+            continue
+        alone = to_host(qs.mul_mat_f16_f32(to_dev(wh), to_dev(x[i:i + 1])))
+        assert_close(full[i:i + 1], alone.astype(np.float64), TOL_F, f"row {i}")
+
+
+@pytest.mark.parametrize("n", [4096, 8192, 8191])
+def test_f16_m2_aligned(n):
+    """F16 at M = 2 with aligned operands and K % 8 == 0: the dispatched
+    (skinny MFMA) kernel and the vectorised narrow kernel (variant 1)."""
+    qs = _qs()
+    k = 4096
+    rng = np.random.default_rng(n)
+    wh = (rng.standard_normal((n, k)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((2, k)).astype(np.float32)
+    say("f16 M=2", n, k, qs.dispatch(qs.MM_TYPE_F16, 2, n, k))
+    y = to_host(qs.mul_mat_f16_f32(to_dev(wh), to_dev(x)))
+    assert_close(y, mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 M=2 N={n}")
+    y1, _ = qs.debug_mul_mat(qs.MM_TYPE_F16, to_dev(wh), to_dev(x), 1)
+    assert_close(to_host(y1), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 M=2 N={n} narrow")
