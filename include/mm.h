@@ -103,6 +103,24 @@ int mm_mul_mat_q4_0_f32(const void* src0, const float* src1, float* dst,
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mm_mul_mat_q4_0_f32_noalloc -- mm_mul_mat_q4_0_f32 without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *   Same operands, layouts, alignment rules, result and determinism as
+ *   mm_mul_mat_q4_0_f32 (same kernels; the output is bit-identical).  The
+ *   workspace is a fixed array of 64 MiB (67108864 bytes) in device memory
+ *   that the library holds on each GPU it runs on until the process ends;
+ *   the call itself allocates nothing.  A shape whose
+ *   mm_mul_mat_workspace_size(MM_TYPE_Q4_0, M, N, K) exceeds 64 MiB returns
+ *   MM_ERR_WORKSPACE before any HIP call (e.g. M = 512 fits for every N up
+ *   to 128256 at K = 4096).  Every call on one GPU shares that GPU's array:
+ *   calls that may overlap in time on one GPU (different streams, or
+ *   different host threads) race and must be serialised by the caller.
+ */
+int mm_mul_mat_q4_0_f32_noalloc(const void* src0, const float* src1, float* dst,
+                                int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * The two stages of mm_mul_mat_q4_0_f32, exposed separately (llama.cpp PR
  * 1632 "mulmat tune", Introduction: the quantized kind runs an INIT stage
  * that converts src1, then the COMPUTE stage).  mm_mul_mat_q4_0_f32 is

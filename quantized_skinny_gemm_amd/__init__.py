@@ -43,6 +43,7 @@ for _name, _args, _res in [
     ("mm_quantize_q4_0", [_vp, _vp, _i64, _i64, _vp], _int),
     ("mm_quantize_q8_0", [_vp, _vp, _i64, _i64, _vp], _int),
     ("mm_mul_mat_q4_0_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    ("mm_mul_mat_q4_0_f32_noalloc", [_vp, _vp, _vp, _i64, _i64, _i64, _vp], _int),
     ("mm_mul_mat_f16_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     ("mm_mul_mat_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     ("mm_q4_0_init", [_vp, _vp, _i64, _i64, _i64, _sz, _vp], _int),

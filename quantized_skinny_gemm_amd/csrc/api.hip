@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/mm.h"
 #include "kernels.h"
@@ -34,6 +35,35 @@ int check_device() {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MM_OK : MM_ERR_HIP; }
+
+// Workspace of mm_mul_mat_q4_0_f32_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address on the current
+// GPU comes from hipGetSymbolAddress, looked up once per device (with that
+// device current) and kept in g_scratch_ptr; only that pointer is ever
+// passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device), or NULL with *st set on failure.
+void* scratch_ptr(int* st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) { *st = MM_ERR_HIP; return nullptr; }
+  if (dev < 0 || dev >= kMaxDevices) { *st = MM_ERR_DEVICE; return nullptr; }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *st = MM_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *st = MM_OK;
+  return g_scratch_ptr[dev];
+}
 
 Q4Args q4_args(const Plan& p, const void* src0, float* dst, int32_t* dots, int64_t M,
                int64_t N, int64_t K, int64_t n0, int64_t n1, void* ws) {
@@ -170,6 +200,26 @@ int mm_quantize_q8_0(const float* x, void* y, int64_t nrows, int64_t k, void* st
 int mm_mul_mat_q4_0_f32(const void* src0, const float* src1, float* dst, int64_t M, int64_t N,
                         int64_t K, void* ws, size_t ws_bytes, void* stream) {
   return mul_mat(MM_TYPE_Q4_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+}
+
+int mm_mul_mat_q4_0_f32_noalloc(const void* src0, const float* src1, float* dst, int64_t M,
+                                int64_t N, int64_t K, void* stream) {
+  // the plan first: a shape whose workspace does not fit the array is
+  // rejected before any HIP call
+  Plan p;
+  int st = make_plan(MM_TYPE_Q4_0, M, N, K, 0, &p);
+  if (st != MM_OK) return st;
+  if (p.ws_bytes > kNoAllocScratchBytes) return MM_ERR_WORKSPACE;
+  if (p.kind == KK_NONE) return MM_OK;
+  st = validate_mul_mat(MM_TYPE_Q4_0, src0, src1, dst, M, N, K, nullptr, 0, p, STAGE_ALL,
+                        /*check_ws=*/false);
+  if (st != MM_OK) return st;
+  st = check_device();
+  if (st != MM_OK) return st;
+  void* ws = scratch_ptr(&st);
+  if (!ws) return st;
+  return mul_mat(MM_TYPE_Q4_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws,
+                 kNoAllocScratchBytes, stream);
 }
 
 int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst, int64_t M,
@@ -374,7 +424,9 @@ const char* mm_status_string(int status) {
     case MM_ERR_NULL: return "a required pointer is NULL";
     case MM_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 32 for a block type, or too large)";
     case MM_ERR_ALIGN: return "pointer not aligned as required";
-    case MM_ERR_WORKSPACE: return "workspace missing or smaller than mm_mul_mat_workspace_size()";
+    case MM_ERR_WORKSPACE:
+      return "workspace missing or smaller than mm_mul_mat_workspace_size() (for "
+             "mm_mul_mat_q4_0_f32_noalloc: the shape needs more than its fixed 64 MiB array)";
     case MM_ERR_ALIAS: return "output or workspace overlaps another operand";
     case MM_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
     case MM_ERR_HIP: return "HIP runtime error";

@@ -319,7 +319,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
 
 int validate_mul_mat(int type, const void* src0, const void* src1, const void* dst,
                      int64_t M, int64_t N, int64_t K, const void* ws, size_t ws_bytes,
-                     const Plan& p, int stage) {
+                     const Plan& p, int stage, bool check_ws) {
   if (p.kind == KK_NONE) return MM_OK;
   const bool need_src0 = stage != STAGE_INIT && K > 0;
   const bool need_src1 = stage != STAGE_COMPUTE && K > 0;
@@ -338,7 +338,8 @@ int validate_mul_mat(int type, const void* src0, const void* src1, const void* d
   } else {
     if (s0 % 4 || s1 % 4) return MM_ERR_ALIGN;
   }
-  if (p.ws_bytes > 0) {
+  if (!check_ws) ws = nullptr;
+  if (check_ws && p.ws_bytes > 0) {
     if (!ws || ws_bytes < p.ws_bytes) return MM_ERR_WORKSPACE;
     if ((uintptr_t)ws % 256) return MM_ERR_ALIGN;
   }
@@ -347,7 +348,7 @@ int validate_mul_mat(int type, const void* src0, const void* src1, const void* d
   const size_t s1_bytes = src1 ? (size_t)M * (size_t)K * 4 : 0;
   if (overlaps(dst, dst_bytes, src0, s0_bytes) || overlaps(dst, dst_bytes, src1, s1_bytes))
     return MM_ERR_ALIAS;
-  if (p.ws_bytes > 0 &&
+  if (ws && p.ws_bytes > 0 &&
       (overlaps(ws, p.ws_bytes, dst, dst_bytes) || overlaps(ws, p.ws_bytes, src0, s0_bytes) ||
        overlaps(ws, p.ws_bytes, src1, s1_bytes)))
     return MM_ERR_ALIAS;

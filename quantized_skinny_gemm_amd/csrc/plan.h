@@ -32,6 +32,7 @@ constexpr int kNarrowMaxGrid = 768;  // narrow workgroups along N (3 per CU)
 constexpr int kMmaMaxM = 32;       // largest M the skinny MFMA kernel takes by default
 constexpr int kSkinnyPairs = 4;    // skinny kernel: block pairs per wave phase
 constexpr int64_t kFMmaMaxK = 1 << 23;  // skinny F kernel: 32-bit buffer offsets over 32 rows
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;  // mm_mul_mat_q4_0_f32_noalloc's array
 constexpr int kMmaWaves = 8;       // waves per workgroup of the skinny kernel for unaligned
                                    // weights or K % 64 != 0 (32 rows per workgroup)
 
@@ -92,9 +93,11 @@ enum Stage { STAGE_ALL = 0, STAGE_INIT = 1, STAGE_COMPUTE = 2 };
 
 // Argument checks of mm_mul_mat_* / mm_q4_0_init / mm_q4_0_compute /
 // mm_debug_mul_mat; no HIP calls.
+// check_ws = false skips the workspace checks (the no-allocation entry
+// point supplies its own array).
 int validate_mul_mat(int type, const void* src0, const void* src1, const void* dst,
                      int64_t M, int64_t N, int64_t K, const void* ws, size_t ws_bytes,
-                     const Plan& p, int stage = STAGE_ALL);
+                     const Plan& p, int stage = STAGE_ALL, bool check_ws = true);
 
 // Argument checks of mm_quantize_q4_0 / mm_quantize_q8_0; no HIP calls.
 int validate_quantize(int out_type, const void* x, const void* y, int64_t nrows, int64_t k);

@@ -257,3 +257,17 @@ def test_measured_tile_and_wave_choices():
     assert qs.dispatch(F16, 16, 11008, 4096)[3] == 8
     assert qs.dispatch(F16, 40, 4096, 4096)[3] == 4
     assert qs.dispatch(F16, 4, 100, 64)[3] == 4
+
+
+def test_noalloc_entry_point_host_checks():
+    # shapes whose workspace exceeds the fixed 64 MiB array are rejected
+    # before any pointer is looked at or any HIP call is made
+    assert qs.workspace_size(Q4, 4096, 64, 16384) > 64 << 20
+    assert qs.lib.mm_mul_mat_q4_0_f32_noalloc(None, None, None, 4096, 64, 16384, None) == WS
+    # the usual shape checks and empty problems
+    assert qs.lib.mm_mul_mat_q4_0_f32_noalloc(FAKE, FAKE, FAKE, 1, 16, 48, None) == SHAPE
+    assert qs.lib.mm_mul_mat_q4_0_f32_noalloc(None, None, None, 0, 16, 64, None) == OK
+    # pointer checks come before the device is touched
+    assert qs.lib.mm_mul_mat_q4_0_f32_noalloc(FAKE, FAKE + 2**30, None, 1, 64, 64, None) == NULL
+    assert qs.lib.mm_mul_mat_q4_0_f32_noalloc(FAKE, FAKE + 2**30 + 4, FAKE + 2**31, 1, 64, 64,
+                                              None) == ALIGN
