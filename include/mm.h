@@ -209,8 +209,7 @@ const char* mm_status_string(int status);
  * mm_dispatch -- the kernel choice mm_mul_mat_* makes at this shape (pure
  * host function).  Writes 5 ints to out (may be NULL):
  *   out[0] variant: 1 = narrow-M kernel, 2 = wide-M (MFMA) kernel (Q4_0,
- *          F16), 3 = skinny MFMA kernel (a few src1 rows; F32 from 2),
- *          4 = wide-M fp16-MFMA kernel (Q4_0, batches of tens of rows)
+ *          F16), 3 = skinny MFMA kernel (a few src1 rows; F32 from 2)
  *   out[1] split-K factor (1 = none)
  *   out[2] rows of src1 per pass (narrow, skinny) or output tile rows (wide)
  *   out[3] output tile columns (wide), src0 rows per wave (narrow) or
@@ -224,7 +223,7 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);
 /*
  * mm_debug_mul_mat -- test entry: the same product as mm_mul_mat_<type>,
  * with the kernel forced (variant 0 = as dispatched, 1 = narrow, 2 = wide
- * (Q4_0 and F16 only), 3 = skinny MFMA, 4 = wide fp16 MFMA (Q4_0 only);
+ * (Q4_0 and F16 only), 3 = skinny MFMA;
  * MM_ERR_ARG for a variant the type does not have)
  * and, for Q4_0, the int32 block dots S_b[m][n][b] of output columns
  * n0 <= n < n1 also written to `dots` ([M][n1-n0][K/32] int32, may be NULL)

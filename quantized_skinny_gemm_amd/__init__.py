@@ -240,9 +240,9 @@ _W_DTYPE = {MM_TYPE_Q4_0: torch.uint8, MM_TYPE_F16: torch.float16, MM_TYPE_F32: 
 
 def debug_mul_mat(mm_type: int, w: torch.Tensor, x: torch.Tensor, variant: int = 0,
                   n0: int = 0, n1: int = 0):
-    """Product with the kernel forced (0 auto, 1 narrow, 2 wide, 3 skinny MFMA, 4 wide fp16
-    MFMA for Q4_0); for Q4_0 also the int32 block dots [M, n1-n0, K/32] of columns n0..n1-1
-    as written by the production kernel."""
+    """Product with the kernel forced (0 auto, 1 narrow, 2 wide, 3 skinny MFMA); for Q4_0
+    also the int32 block dots [M, n1-n0, K/32] of columns n0..n1-1 as written by the
+    production kernel."""
     w = _dev(w, "w", _W_DTYPE[mm_type])
     x = _dev(x, "x", torch.float32)
     m, k = x.shape

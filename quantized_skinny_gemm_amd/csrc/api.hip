@@ -73,7 +73,6 @@ Q4Args q4_args(const Plan& p, const void* src0, float* dst, int32_t* dots, int64
   a.aq = (const int8_t*)(base + p.off_aq);
   a.ad = (const float*)(base + p.off_ad);
   a.ab = (const int32_t*)(base + p.off_ab);
-  a.ah = p.off_ah ? (const uint16_t*)(base + p.off_ah) : nullptr;
   a.sq = p.off_sq ? (const uint8_t*)(base + p.off_sq) : nullptr;
   a.ss = p.off_ss ? (const float*)(base + p.off_ss) : nullptr;
   a.sk_phases = (int)p.sk_phases;
@@ -95,8 +94,7 @@ int q4_init(const Plan& p, const float* src1, int64_t M, int64_t K, void* ws, hi
         (int32_t*)(base + p.off_ab), base + p.off_sq, (float*)(base + p.off_ss), p.sk_rows,
         p.sk_phases, p.mt == 8, s));
   return hip_status(launch_quantize_q8_0(src1, M, K, nullptr, (int8_t*)(base + p.off_aq),
-                                         (float*)(base + p.off_ad), (int32_t*)(base + p.off_ab),
-                                         p.off_ah ? (uint16_t*)(base + p.off_ah) : nullptr, s));
+                                         (float*)(base + p.off_ad), (int32_t*)(base + p.off_ab), s));
 }
 
 Q4Mats single_mat(const void* src0, float* dst, int64_t N) {
@@ -115,7 +113,6 @@ int q4_product(const Plan& p, const Q4Args& a, const float* x, hipStream_t s) {
   hipError_t e = p.kind == KK_Q4_NARROW   ? launch_q4_narrow(p, a, single_mat(a.w, a.dst, a.N), x, s)
                  : p.kind == KK_Q4_MMA    ? (a.sq && q4_skinny_ok(a.K, a.w) ? launch_q4_skinny(p, a, s)
                                                                       : launch_q4_mma(p, a, s))
-                 : p.kind == KK_Q4_WIDE16 ? launch_q4_wide16(p, a, s)
                                           : launch_q4_wide_i8(p, a, s);
   if (e == hipSuccess && p.split > 1)
     e = launch_splitk_reduce(a.part, a.dst, (int64_t)a.M * a.N, p.split, s);
@@ -161,7 +158,6 @@ int mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* 
     case KK_ZERO: return hip_status(launch_zero(dst, M * N, s));
     case KK_Q4_NARROW:
     case KK_Q4_MMA:
-    case KK_Q4_WIDE16:
     case KK_Q4_WIDE: return run_q4_0(p, src0, src1, dst, dots, M, N, K, n0, n1, ws, s);
     case KK_F_NARROW:
       return hip_status(launch_f_narrow(p, type, src0, src1, dst, (int)M, (int)N, (int)K, s));
@@ -181,8 +177,7 @@ int quantize(int out_type, const float* x, void* y, int64_t nrows, int64_t k, vo
   if (st != MM_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (out_type == MM_TYPE_Q4_0) return hip_status(launch_quantize_q4_0(x, nrows, k, (uint8_t*)y, s));
-  return hip_status(launch_quantize_q8_0(x, nrows, k, (uint8_t*)y, nullptr, nullptr, nullptr,
-                                         nullptr, s));
+  return hip_status(launch_quantize_q8_0(x, nrows, k, (uint8_t*)y, nullptr, nullptr, nullptr, s));
 }
 
 }  // namespace
@@ -285,7 +280,7 @@ int group_plan(int count, const int64_t* Ns, int64_t M, int64_t K, Plan* whole, 
   int st = make_plan(MM_TYPE_Q4_0, M, tot, K, 0, whole, /*allow_split=*/false);
   if (st != MM_OK) return st;
   size_t need = whole->ws_bytes;
-  if (whole->kind == KK_Q4_WIDE || whole->kind == KK_Q4_WIDE16 || whole->kind == KK_Q4_MMA) {
+  if (whole->kind == KK_Q4_WIDE || whole->kind == KK_Q4_MMA) {
     for (int i = 0; i < count; ++i) {
       Plan pi;
       st = make_plan(MM_TYPE_Q4_0, M, Ns[i], K, 0, &pi);
@@ -399,7 +394,7 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
   if (out) {
     out[0] = p.variant;
     out[1] = p.split;
-    const bool tiled = p.variant == 2 || p.variant == 4;
+    const bool tiled = p.variant == 2;
     out[2] = tiled ? p.bm : p.mt;
     out[3] = tiled ? p.bn : p.variant == 3 ? p.waves : p.kind == KK_Q4_NARROW && p.fuse ? p.fuse_rpw : p.rpw;
     const int init = (p.type == MM_TYPE_Q4_0 && !(p.kind == KK_Q4_NARROW && p.fuse)) ? 1 : 0;
@@ -411,7 +406,7 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
 int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* dots,
                      int64_t M, int64_t N, int64_t K, int64_t n0, int64_t n1, int variant,
                      void* ws, size_t ws_bytes, void* stream) {
-  if (variant < 0 || variant > 4) return MM_ERR_ARG;
+  if (variant < 0 || variant > 3) return MM_ERR_ARG;
   if (n0 < 0 || n1 < n0 || n1 > N) return MM_ERR_SHAPE;
   if (type != MM_TYPE_Q4_0 || n1 == n0) dots = nullptr;
   else if (!dots) return MM_ERR_NULL;

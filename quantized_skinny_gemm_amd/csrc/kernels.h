@@ -11,11 +11,9 @@ namespace qsg {
 // Q8_0 activation quantisation.  Writes the canonical 34-byte blocks to
 // `canon` (may be NULL) and/or the library's internal wdata layout
 // (codes int8 [rows][k], scales f32 [rows][k/32], bias -8*sum(q) int32
-// [rows][k/32]; all NULL to skip), and optionally the codes again as
-// binary16 [rows][k] (`wh`, exact: |q| <= 127).
+// [rows][k/32]; all NULL to skip).
 hipError_t launch_quantize_q8_0(const float* x, int64_t nrows, int64_t k, uint8_t* canon,
-                                int8_t* wq, float* wd, int32_t* wb, uint16_t* wh,
-                                hipStream_t s);
+                                int8_t* wq, float* wd, int32_t* wb, hipStream_t s);
 
 hipError_t launch_quantize_q4_0(const float* x, int64_t nrows, int64_t k, uint8_t* y,
                                 hipStream_t s);
@@ -33,7 +31,6 @@ struct Q4Args {
   const int8_t* aq;      // wdata codes
   const float* ad;       // wdata scales
   const int32_t* ab;     // wdata -8*sum(q)
-  const uint16_t* ah;    // wdata codes as binary16 (wide kernel; NULL otherwise)
   const uint8_t* sq;     // skinny kernel: codes in operand order (NULL otherwise)
   const float* ss;       // skinny kernel: scales in operand order
   int sk_phases;         // skinny kernel: phases of 8 blocks per row
@@ -62,10 +59,8 @@ struct Q4Mats {
 // a.N is the total row count of mats; a.w / a.dst are unused here.
 hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, const float* x,
                             hipStream_t s);
-// Wide kernels (INIT must have run): int8 MFMA, and fp16 MFMA with exact
-// block dots (reads a.ah).
+// Wide kernel (INIT must have run): int8 MFMA.
 hipError_t launch_q4_wide_i8(const Plan& p, const Q4Args& a, hipStream_t s);
-hipError_t launch_q4_wide16(const Plan& p, const Q4Args& a, hipStream_t s);
 // Skinny MFMA kernel: reads the wdata in a (INIT must have run), writes
 // a.dst.  16-row workgroups when K % 64 == 0 and src0 is 4-byte aligned
 // (q4_skinny_ok); otherwise the 32-row kernel with LDS-staged chunks.

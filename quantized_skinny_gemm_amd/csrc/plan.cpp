@@ -44,7 +44,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   *p = Plan();
   p->type = type;
   if (type != MM_TYPE_F32 && type != MM_TYPE_F16 && type != MM_TYPE_Q4_0) return MM_ERR_ARG;
-  if (variant < 0 || variant > 4) return MM_ERR_ARG;
+  if (variant < 0 || variant > 3) return MM_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MM_ERR_SHAPE;
   if (type == MM_TYPE_Q4_0 && (K % kQK)) return MM_ERR_SHAPE;
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
@@ -56,7 +56,6 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     // kernel; beyond: the tiled wide kernel.
     const bool mma = variant == 3 || (variant == 0 && M > kFuseMaxM && M <= kMmaMaxM);
     const bool narrow = !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
-    const bool wide16 = variant == 4 || (variant == 0 && M > kMmaMaxM && M <= kWide16MaxM);
     // wdata: codes, scales, bias; the codes and scales are followed by 256
     // spare bytes (the skinny kernel's last phase may read up to 7 blocks past
     // the end, and drops them)
@@ -160,34 +159,6 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
         const int64_t groups = ceil_div(N, (int64_t)p->fuse_rpw * p->fuse_waves);
         p->fuse_grid = groups < kNarrowMaxGrid ? groups : kNarrowMaxGrid;
       }
-    } else if (wide16) {
-      p->kind = KK_Q4_WIDE16;
-      p->variant = 4;
-      // its MFMA operands are binary16: INIT also writes the codes in that form
-      p->off_ah = off; off = align_up(off + (size_t)M * (size_t)K * 2, 256);
-      if (M <= 32) { p->bm = 32; p->bn = 64; p->waves_m = 1; p->waves_n = 2; }
-      else { p->bm = 64; p->bn = 64; p->waves_m = 2; p->waves_n = 2; }
-      p->tiles_m = ceil_div(M, p->bm);
-      p->tiles_n = ceil_div(N, p->bn);
-      const int64_t tiles = p->tiles_m * p->tiles_n;
-      const int64_t stages = ceil_div(nb, kWide16KB);
-      // Fewer tiles than CUs: split K for about two workgroups per CU, at
-      // least 4 stages per split (us per call, against one workgroup per CU
-      // and 2 stages: M = 512, 4096 x 4096 58.7 -> 49.5; M = 128, 4096 x 14336
-      // 54.2 -> 47.3-48.8; M = 256, 4096 x 4096 39.2 -> 34.5; M = 40,
-      // 11008 x 4096 33.9 -> 31.8; M = 64, 14336 x 4096 35.4 -> 36.3).  With
-      // enough tiles it does not pay (M = 512, 14336 x 4096, split 2: 127 ->
-      // 142).
-      int64_t split = 1;
-      if (allow_split && tiles < kCUs) {
-        split = ceil_div(2 * kCUs, tiles);
-        const int64_t max_split = stages / 4;          // >= 4 stages per split
-        if (split > max_split) split = max_split;
-        if (split > 16) split = 16;
-        if (split < 1) split = 1;
-      }
-      p->kchunk = ceil_div(stages, split) * kWide16KB;   // blocks per split
-      p->split = (int)ceil_div(nb, p->kchunk);
     } else {
       p->kind = KK_Q4_WIDE;
       p->variant = 2;
@@ -241,7 +212,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   // F16 / F32: M = 1 the narrow kernel; from 2 rows the skinny MFMA kernel
   // (passes of 16 rows), for F16 only up to the limit below, beyond which
   // the wide kernel takes it.
-  if (variant == 4 || (variant == 2 && type != MM_TYPE_F16)) return MM_ERR_ARG;
+  if (variant == 2 && type != MM_TYPE_F16) return MM_ERR_ARG;
   const bool f16 = type == MM_TYPE_F16;
   // F16 from 17 rows: the wide kernel, except up to 64 rows with at most
   // 8192 weight rows, where its 64 x 64 tiles give too few workgroups and

@@ -21,9 +21,6 @@ constexpr int kQ4Bytes = 18;       // bytes per Q4_0 block
 constexpr int kQ8Bytes = 34;       // bytes per Q8_0 block
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kWideI8KB = 4;       // Q4_0 blocks per LDS stage, int8 wide kernel
-constexpr int kWide16KB = 8;       // Q4_0 blocks per LDS stage, fp16 wide kernel
-constexpr int kWide16MaxM = 0;     // largest M the fp16 wide kernel takes by default (none: the
-                                   // int8 wide kernel with register prefetch is faster at every M)
 constexpr int kNarrowQ4MaxM = 8;   // largest M the Q4_0 narrow kernel takes in one pass
 constexpr int kNarrowFMaxM = 16;   // largest M the f16/f32 narrow kernel takes in one pass
 constexpr int kFuseMaxM = 2;       // narrow Q4_0 passes of at most this many rows fuse INIT
@@ -44,7 +41,6 @@ enum KernelKind {
   KK_F_NARROW = 4,  // f16 or f32 src0
   KK_F16_WIDE = 5,
   KK_Q4_MMA = 6,    // skinny Q4_0 on int8 MFMA (16 weight rows per workgroup)
-  KK_Q4_WIDE16 = 7, // wide Q4_0 on fp16 MFMA with exact block dots
   KK_F_MMA = 8,     // skinny F16 / F32 on the 16x16 MFMA (16 weight rows per workgroup,
                     // passes of 16 src1 rows, waves split K)
 };
@@ -52,7 +48,7 @@ enum KernelKind {
 struct Plan {
   int type = 0;
   int kind = KK_NONE;
-  int variant = 0;          // 1 narrow, 2 wide (Q4_0: int8; F16: fp16), 3 skinny MFMA, 4 wide (Q4_0, fp16)
+  int variant = 0;          // 1 narrow, 2 wide (Q4_0: int8; F16: fp16), 3 skinny MFMA
   // narrow kernels
   int mt = 1;               // src1 rows per pass (compile-time tile)
   int rpw = 1;              // src0 rows per wave (skinny MFMA: per workgroup)
@@ -71,8 +67,7 @@ struct Plan {
                             // skinny F: MFMA steps per wave)
   // workspace layout (bytes)
   size_t off_aq = 0, off_ad = 0, off_ab = 0, off_part = 0;
-  size_t off_ah = 0;        // wide kernel: Q8_0 codes as binary16 [M][K] (0: not written)
-                            // (wide F16 kernel: src1 as binary16 [M][K])
+  size_t off_ah = 0;        // wide F16 kernel: src1 as binary16 [M][K]
   size_t off_rexp = 0;      // wide F16 kernel: int32 [M] power-of-two exponent per src1 row
   size_t off_sq = 0, off_ss = 0;   // skinny MFMA kernel: its operand-order codes and scales
                                    // (0: not written)

@@ -33,8 +33,7 @@ __device__ __forceinline__ void store_u16(uint8_t* p, uint32_t v) {
 
 __global__ __launch_bounds__(kThreads) void k_quantize_q8_0(
     const float* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ canon,
-    int8_t* __restrict__ wq, float* __restrict__ wd, int32_t* __restrict__ wb,
-    uint16_t* __restrict__ wh) {
+    int8_t* __restrict__ wq, float* __restrict__ wd, int32_t* __restrict__ wb) {
   // two lanes per block, 16 values (64 bytes) each
   const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t blk = gtid >> 1;
@@ -67,19 +66,6 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q8_0(
       wd[blk] = f16_bits_to_f32(dbits);
       wb[blk] = -8 * sum;
     }
-  }
-  if (wh) {
-    // the 16 codes as binary16 (integers of magnitude <= 127: exact)
-    uint32_t hv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q0 = (int)(int8_t)((packed[j >> 1] >> (16 * (j & 1))) & 0xff);
-      const int q1 = (int)(int8_t)((packed[j >> 1] >> (16 * (j & 1) + 8)) & 0xff);
-      hv[j] = f32_to_f16_bits((float)q0) | (f32_to_f16_bits((float)q1) << 16);
-    }
-    uint4* o = reinterpret_cast<uint4*>(wh + blk * 32 + 16 * h);
-    o[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-    o[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
   }
 }
 
@@ -203,13 +189,12 @@ int64_t grid_for(int64_t nblocks, int lanes) { return (nblocks * lanes + kThread
 }  // namespace
 
 hipError_t launch_quantize_q8_0(const float* x, int64_t nrows, int64_t k, uint8_t* canon,
-                                int8_t* wq, float* wd, int32_t* wb, uint16_t* wh,
-                                hipStream_t s) {
+                                int8_t* wq, float* wd, int32_t* wb, hipStream_t s) {
   const int64_t nblocks = nrows * (k / 32);
   const int64_t grid = grid_for(nblocks, 2);
   if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL(k_quantize_q8_0, dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks,
-                     canon, wq, wd, wb, wh);
+                     canon, wq, wd, wb);
   return hipGetLastError();
 }
 

@@ -120,9 +120,9 @@ def test_aliasing():
 
 def test_debug_entry_argument_checks():
     assert qs.lib.mm_debug_mul_mat(Q4, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 7, None, 0, None) == ARG
-    # the fp16 wide Q4_0 variant is for Q4_0 only, the wide F kernel for F16 only
-    assert qs.lib.mm_debug_mul_mat(F16, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 4, None, 0, None) == ARG
-    assert qs.lib.mm_debug_mul_mat(F32, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 4, None, 0, None) == ARG
+    # variants 1-3 only; the wide F kernel is for F16 only
+    for t in (F16, F32, Q4):
+        assert qs.lib.mm_debug_mul_mat(t, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 4, None, 0, None) == ARG
     assert qs.lib.mm_debug_mul_mat(F32, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 2, None, 0, None) == ARG
     # the skinny MFMA variant exists for every type
     for t in (F16, F32, Q4):
