@@ -63,7 +63,8 @@ typedef enum mm_type {
     MM_TYPE_F32 = 0,
     MM_TYPE_F16 = 1,
     MM_TYPE_Q4_0 = 2,
-    MM_TYPE_Q8_0 = 3
+    MM_TYPE_Q8_0 = 3,
+    MM_TYPE_Q4_0R = 4      /* Q4_0 weights in the repacked layout (mm_repack_q4_0) */
 } mm_type;
 
 /*
@@ -156,6 +157,43 @@ int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const*
                               const int64_t* Ns, const float* src1, int64_t M, int64_t K,
                               void* ws, size_t ws_bytes, void* stream);
 size_t mm_mul_mat_q4_0_group_workspace_size(int count, const int64_t* Ns, int64_t M, int64_t K);
+
+/*
+ * Weight repack at load time (DeepSpeed-Inference reading notes, III.C
+ * SBI-GeMM, item 3: the weights are laid out once, at initialisation, so
+ * that every thread of the product reads whole cache lines of what it
+ * consumes).  The repacked layout ("Q4_0R") holds the same 18 bytes per
+ * block, grouped per tile of 16 weight rows and phase of 8 blocks (256
+ * values of K) into 2304-byte chunks, tile-major ([ceil(N/16)][ceil(K/256)]):
+ *   bytes    0..2047: codes, [half hh][lane l][4 dwords]: lane l = i + 16 g
+ *                     holds code bytes 4g..4g+3 of row i of the tile for
+ *                     blocks 4 hh + 0..3 (low nibbles: elements 4g..4g+3,
+ *                     high nibbles: elements 16+4g..19+4g);
+ *   bytes 2048..2303: scales, [row i][block b] binary16 d.
+ * Rows past N and blocks past K/32 are padding (codes 0x88, scale 0).
+ *
+ * mm_repacked_q4_0_bytes -- size of the repacked form of N x K Q4_0 weights
+ *   (ceil(N/16) * ceil(K/256) * 2304); -1 if K % 32 != 0 or a size is
+ *   negative.  Pure host function.
+ * mm_repack_q4_0 -- src0 (Q4_0 [N][K/32] blocks, 2-byte aligned) -> dst
+ *   (repacked, 16-byte aligned, mm_repacked_q4_0_bytes(N, K) bytes, all
+ *   written including padding).  Buffers must not overlap.
+ * mm_unpack_q4_0 -- the inverse: repacked src (16-byte aligned) -> Q4_0
+ *   [N][K/32] blocks in dst (2-byte aligned); unpack(repack(w)) == w byte
+ *   for byte.
+ * mm_mul_mat_q4_0r_f32 -- mm_mul_mat_q4_0_f32 with src0 in the repacked
+ *   layout (16-byte aligned): the same result (block dots bit-exact,
+ *   dst within the same bound; the kernels differ, so dst may differ from
+ *   the plain call in the last bits).  ws:
+ *   mm_mul_mat_workspace_size(MM_TYPE_Q4_0R, M, N, K) bytes.
+ * Errors as for the other entry points (MM_ERR_SHAPE for K % 32 != 0).
+ */
+int64_t mm_repacked_q4_0_bytes(int64_t N, int64_t K);
+int mm_repack_q4_0(const void* src0, void* dst, int64_t N, int64_t K, void* stream);
+int mm_unpack_q4_0(const void* src0r, void* dst, int64_t N, int64_t K, void* stream);
+int mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst,
+                         int64_t M, int64_t N, int64_t K,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mm_mul_mat_f16_f32 -- dst[M][N] = src1[M][K] . f32(src0[N][K])^T, fp32 accumulation.

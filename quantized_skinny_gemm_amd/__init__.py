@@ -20,7 +20,8 @@ import os
 import torch
 
 __all__ = [
-    "LIB_PATH", "lib", "MM_TYPE_F32", "MM_TYPE_F16", "MM_TYPE_Q4_0", "MM_TYPE_Q8_0",
+    "LIB_PATH", "lib", "MM_TYPE_F32", "MM_TYPE_F16", "MM_TYPE_Q4_0", "MM_TYPE_Q8_0", "MM_TYPE_Q4_0R",
+    "repacked_bytes", "repack_q4_0", "unpack_q4_0", "mul_mat_q4_0r_f32",
     "MMError", "quantize_q4_0", "quantize_q8_0", "mul_mat_q4_0_f32", "mul_mat_f16_f32",
     "mul_mat_f32", "workspace_size", "debug_workspace_size", "row_bytes", "dispatch",
     "debug_mul_mat", "status_string", "q4_0_init", "q4_0_compute", "mul_mat_q4_0_f32_group",
@@ -29,7 +30,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsgemm.so")
 
-MM_TYPE_F32, MM_TYPE_F16, MM_TYPE_Q4_0, MM_TYPE_Q8_0 = 0, 1, 2, 3
+MM_TYPE_F32, MM_TYPE_F16, MM_TYPE_Q4_0, MM_TYPE_Q8_0, MM_TYPE_Q4_0R = 0, 1, 2, 3, 4
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -44,6 +45,10 @@ for _name, _args, _res in [
     ("mm_quantize_q8_0", [_vp, _vp, _i64, _i64, _vp], _int),
     ("mm_mul_mat_q4_0_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     ("mm_mul_mat_q4_0_f32_noalloc", [_vp, _vp, _vp, _i64, _i64, _i64, _vp], _int),
+    ("mm_mul_mat_q4_0r_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    ("mm_repack_q4_0", [_vp, _vp, _i64, _i64, _vp], _int),
+    ("mm_unpack_q4_0", [_vp, _vp, _i64, _i64, _vp], _int),
+    ("mm_repacked_q4_0_bytes", [_i64, _i64], _i64),
     ("mm_mul_mat_f16_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     ("mm_mul_mat_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     ("mm_q4_0_init", [_vp, _vp, _i64, _i64, _i64, _sz, _vp], _int),
@@ -164,6 +169,47 @@ def mul_mat_q4_0_f32(w: torch.Tensor, x: torch.Tensor, out=None, ws=None) -> tor
     if w.shape[1] != row_bytes(MM_TYPE_Q4_0, x.shape[1]):
         raise ValueError("w row bytes do not match K")
     return _mul_mat(lib.mm_mul_mat_q4_0_f32, MM_TYPE_Q4_0, w, x, out, ws, "mm_mul_mat_q4_0_f32")
+
+
+def repacked_bytes(n: int, k: int) -> int:
+    return int(lib.mm_repacked_q4_0_bytes(int(n), int(k)))
+
+
+def repack_q4_0(w: torch.Tensor, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """uint8 [N, K/32*18] Q4_0 -> uint8 [repacked_bytes(N, K)] repacked weights."""
+    w = _dev(w, "w", torch.uint8)
+    n = w.shape[0]
+    if out is None:
+        out = torch.empty(max(repacked_bytes(n, k), 0), dtype=torch.uint8, device=w.device)
+    _check(lib.mm_repack_q4_0(_ptr(w), _ptr(out), n, k, _stream(w)), "mm_repack_q4_0")
+    return out
+
+
+def unpack_q4_0(wr: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Repacked weights -> uint8 [N, K/32*18] Q4_0."""
+    wr = _dev(wr, "wr", torch.uint8)
+    if out is None:
+        out = torch.empty((n, max(row_bytes(MM_TYPE_Q4_0, k), 0)), dtype=torch.uint8, device=wr.device)
+    _check(lib.mm_unpack_q4_0(_ptr(wr), _ptr(out), n, k, _stream(wr)), "mm_unpack_q4_0")
+    return out
+
+
+def mul_mat_q4_0r_f32(wr: torch.Tensor, n: int, x: torch.Tensor, out=None, ws=None) -> torch.Tensor:
+    """dst[M, N] = Q8_0(x) . W^T with W (N x K) given in the repacked layout."""
+    wr = _dev(wr, "wr", torch.uint8)
+    x = _dev(x, "x", torch.float32)
+    m, k = x.shape
+    if wr.numel() < repacked_bytes(n, k):
+        raise ValueError("repacked weights smaller than repacked_bytes(N, K)")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    else:
+        _dev(out, "out", torch.float32)
+    ws = _workspace(workspace_size(MM_TYPE_Q4_0R, m, n, k), x.device, ws)
+    nbytes = 0 if ws is None else ws.numel()
+    _check(lib.mm_mul_mat_q4_0r_f32(_ptr(wr), _ptr(x), _ptr(out), m, n, k, _ptr(ws), nbytes,
+                                    _stream(x)), "mm_mul_mat_q4_0r_f32")
+    return out
 
 
 def group_workspace_size(ns, m: int, k: int) -> int:

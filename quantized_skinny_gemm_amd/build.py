@@ -26,7 +26,7 @@ BENCH_SRC = os.path.join(ROOT, "bench_read.hip")
 BENCH_LIB = os.path.join(ROOT, "bench_read.so")
 
 HIP_SOURCES = ["api.hip", "quantize.hip", "q4_narrow.hip", "q4_mma.hip", "q4_skinny.hip",
-               "q4_wide_i8.hip", "f_kernels.hip"]
+               "q4_wide_i8.hip", "f_kernels.hip", "repack.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 ARCH = "gfx950"

@@ -110,10 +110,11 @@ Q4Mats single_mat(const void* src0, float* dst, int64_t N) {
 
 // The product kernel (x != NULL: INIT fused), then the split-K reduction.
 int q4_product(const Plan& p, const Q4Args& a, const float* x, hipStream_t s) {
-  hipError_t e = p.kind == KK_Q4_NARROW   ? launch_q4_narrow(p, a, single_mat(a.w, a.dst, a.N), x, s)
-                 : p.kind == KK_Q4_MMA    ? (a.sq && q4_skinny_ok(a.K, a.w) ? launch_q4_skinny(p, a, s)
-                                                                      : launch_q4_mma(p, a, s))
-                                          : launch_q4_wide_i8(p, a, s);
+  hipError_t e = p.kind == KK_Q4_NARROW    ? launch_q4_narrow(p, a, single_mat(a.w, a.dst, a.N), x, s)
+                 : p.kind == KK_Q4_MMA     ? (a.sq && q4_skinny_ok(a.K, a.w) ? launch_q4_skinny(p, a, s)
+                                                                       : launch_q4_mma(p, a, s))
+                 : p.kind == KK_Q4R_SKINNY ? launch_q4r_skinny(p, a, s)
+                                           : launch_q4_wide_i8(p, a, s);
   if (e == hipSuccess && p.split > 1)
     e = launch_splitk_reduce(a.part, a.dst, (int64_t)a.M * a.N, p.split, s);
   return hip_status(e);
@@ -158,6 +159,7 @@ int mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* 
     case KK_ZERO: return hip_status(launch_zero(dst, M * N, s));
     case KK_Q4_NARROW:
     case KK_Q4_MMA:
+    case KK_Q4R_SKINNY:
     case KK_Q4_WIDE: return run_q4_0(p, src0, src1, dst, dots, M, N, K, n0, n1, ws, s);
     case KK_F_NARROW:
       return hip_status(launch_f_narrow(p, type, src0, src1, dst, (int)M, (int)N, (int)K, s));
@@ -178,6 +180,27 @@ int quantize(int out_type, const float* x, void* y, int64_t nrows, int64_t k, vo
   hipStream_t s = (hipStream_t)stream;
   if (out_type == MM_TYPE_Q4_0) return hip_status(launch_quantize_q4_0(x, nrows, k, (uint8_t*)y, s));
   return hip_status(launch_quantize_q8_0(x, nrows, k, (uint8_t*)y, nullptr, nullptr, nullptr, s));
+}
+
+// Q4_0 <-> repacked Q4_0: plain rows are 2-byte aligned, the repacked
+// buffer 16-byte aligned; the two must not overlap.
+int repack(const void* src, void* dst, int64_t N, int64_t K, bool to_repacked, void* stream) {
+  const int64_t rb = repacked_bytes(N, K);
+  if (rb < 0) return MM_ERR_SHAPE;
+  if (N == 0 || K == 0) return MM_OK;
+  if (!src || !dst) return MM_ERR_NULL;
+  const void* plain = to_repacked ? src : dst;
+  const void* packed = to_repacked ? dst : src;
+  if ((uintptr_t)plain % 2 || (uintptr_t)packed % 16) return MM_ERR_ALIGN;
+  const uintptr_t p0 = (uintptr_t)plain, p1 = (uintptr_t)packed;
+  const size_t pb = (size_t)N * (size_t)row_bytes(MM_TYPE_Q4_0, K);
+  if (p0 < p1 + (size_t)rb && p1 < p0 + pb) return MM_ERR_ALIAS;
+  const int st = check_device();
+  if (st != MM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(to_repacked
+                        ? launch_repack_q4_0((const uint8_t*)src, (uint8_t*)dst, N, K, s)
+                        : launch_unpack_q4_0((const uint8_t*)src, (uint8_t*)dst, N, K, s));
 }
 
 }  // namespace
@@ -215,6 +238,21 @@ int mm_mul_mat_q4_0_f32_noalloc(const void* src0, const float* src1, float* dst,
   if (!ws) return st;
   return mul_mat(MM_TYPE_Q4_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws,
                  kNoAllocScratchBytes, stream);
+}
+
+int mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst, int64_t M, int64_t N,
+                         int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  return mul_mat(MM_TYPE_Q4_0R, src0r, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+}
+
+int64_t mm_repacked_q4_0_bytes(int64_t N, int64_t K) { return repacked_bytes(N, K); }
+
+int mm_repack_q4_0(const void* src0, void* dst, int64_t N, int64_t K, void* stream) {
+  return repack(src0, dst, N, K, /*to_repacked=*/true, stream);
+}
+
+int mm_unpack_q4_0(const void* src0r, void* dst, int64_t N, int64_t K, void* stream) {
+  return repack(src0r, dst, N, K, /*to_repacked=*/false, stream);
 }
 
 int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst, int64_t M,
@@ -397,7 +435,8 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
     const bool tiled = p.variant == 2;
     out[2] = tiled ? p.bm : p.mt;
     out[3] = tiled ? p.bn : p.variant == 3 ? p.waves : p.kind == KK_Q4_NARROW && p.fuse ? p.fuse_rpw : p.rpw;
-    const int init = (p.type == MM_TYPE_Q4_0 && !(p.kind == KK_Q4_NARROW && p.fuse)) ? 1 : 0;
+    const bool q4 = p.type == MM_TYPE_Q4_0 || p.type == MM_TYPE_Q4_0R;
+    const int init = (q4 && !(p.kind == KK_Q4_NARROW && p.fuse)) ? 1 : 0;
     out[4] = init + 1 + (p.split > 1 ? 1 : 0);
   }
   return MM_OK;
@@ -408,7 +447,7 @@ int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst, 
                      void* ws, size_t ws_bytes, void* stream) {
   if (variant < 0 || variant > 3) return MM_ERR_ARG;
   if (n0 < 0 || n1 < n0 || n1 > N) return MM_ERR_SHAPE;
-  if (type != MM_TYPE_Q4_0 || n1 == n0) dots = nullptr;
+  if ((type != MM_TYPE_Q4_0 && type != MM_TYPE_Q4_0R) || n1 == n0) dots = nullptr;
   else if (!dots) return MM_ERR_NULL;
   return mul_mat(type, src0, src1, dst, dots, M, N, K, n0, n1, variant, ws, ws_bytes, stream);
 }

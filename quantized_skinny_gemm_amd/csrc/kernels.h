@@ -59,7 +59,16 @@ struct Q4Mats {
 // a.N is the total row count of mats; a.w / a.dst are unused here.
 hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, const float* x,
                             hipStream_t s);
-// Wide kernel (INIT must have run): int8 MFMA.
+// Skinny MFMA kernel on repacked weights (repack.hip); reads the operand-
+// order wdata of 16-row tiles (INIT must have run).
+hipError_t launch_q4r_skinny(const Plan& p, const Q4Args& a, hipStream_t s);
+// Weight repack: Q4_0 [N][K/32] blocks <-> the repacked layout.
+hipError_t launch_repack_q4_0(const uint8_t* src, uint8_t* dst, int64_t N, int64_t K,
+                              hipStream_t s);
+hipError_t launch_unpack_q4_0(const uint8_t* src, uint8_t* dst, int64_t N, int64_t K,
+                              hipStream_t s);
+// Wide kernel (INIT must have run): int8 MFMA; plain or repacked weights
+// (p.type).
 hipError_t launch_q4_wide_i8(const Plan& p, const Q4Args& a, hipStream_t s);
 // Skinny MFMA kernel: reads the wdata in a (INIT must have run), writes
 // a.dst.  16-row workgroups when K % 64 == 0 and src0 is 4-byte aligned

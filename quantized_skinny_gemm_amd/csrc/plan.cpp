@@ -36,25 +36,36 @@ int64_t row_bytes(int type, int64_t K) {
     case MM_TYPE_F16: return 2 * K;
     case MM_TYPE_Q4_0: return (K % kQK) ? -1 : K / kQK * kQ4Bytes;
     case MM_TYPE_Q8_0: return (K % kQK) ? -1 : K / kQK * kQ8Bytes;
+    case MM_TYPE_Q4_0R: return -1;                 // tiled, not row-major (repacked_bytes)
     default: return -1;
   }
+}
+
+int64_t repacked_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K < 0 || K % kQK || N > kMaxDim || K > kMaxDim) return -1;
+  return ceil_div(N, 16) * ceil_div(K / kQK, 8) * kQ4RChunk;
 }
 
 int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, bool allow_split) {
   *p = Plan();
   p->type = type;
-  if (type != MM_TYPE_F32 && type != MM_TYPE_F16 && type != MM_TYPE_Q4_0) return MM_ERR_ARG;
+  if (type != MM_TYPE_F32 && type != MM_TYPE_F16 && type != MM_TYPE_Q4_0 &&
+      type != MM_TYPE_Q4_0R)
+    return MM_ERR_ARG;
   if (variant < 0 || variant > 3) return MM_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MM_ERR_SHAPE;
-  if (type == MM_TYPE_Q4_0 && (K % kQK)) return MM_ERR_SHAPE;
+  if ((type == MM_TYPE_Q4_0 || type == MM_TYPE_Q4_0R) && (K % kQK)) return MM_ERR_SHAPE;
+  if (type == MM_TYPE_Q4_0R && variant == 1) return MM_ERR_ARG;   // no narrow kernel for it
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
   if (K == 0) { p->kind = KK_ZERO; return MM_OK; }
 
-  if (type == MM_TYPE_Q4_0) {
+  if (type == MM_TYPE_Q4_0 || type == MM_TYPE_Q4_0R) {
+    const bool rep = type == MM_TYPE_Q4_0R;
     const int64_t nb = K / kQK;
     // M <= 2: the fused narrow kernel; up to kMmaMaxM: the skinny MFMA
-    // kernel; beyond: the tiled wide kernel.
-    const bool mma = variant == 3 || (variant == 0 && M > kFuseMaxM && M <= kMmaMaxM);
+    // kernel; beyond: the tiled wide kernel.  Repacked weights: the skinny
+    // kernel from M = 1.
+    const bool mma = variant == 3 || (variant == 0 && (rep || M > kFuseMaxM) && M <= kMmaMaxM);
     const bool narrow = !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
     // wdata: codes, scales, bias; the codes and scales are followed by 256
     // spare bytes (the skinny kernel's last phase may read up to 7 blocks past
@@ -63,7 +74,32 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     p->off_aq = off; off = align_up(off + (size_t)M * (size_t)K + 256, 256);
     p->off_ad = off; off = align_up(off + (size_t)M * (size_t)nb * 4 + 256, 256);
     p->off_ab = off; off = align_up(off + (size_t)M * (size_t)nb * 4, 256);
-    if (mma) {
+    if (mma && rep) {
+      // one 16-row tile per workgroup; its waves split the phases of 8 blocks
+      // among themselves (whole phases: the weights and the operand-order
+      // wdata are zero past K); passes of 16 or 32 src1 rows.
+      p->kind = KK_Q4R_SKINNY;
+      p->variant = 3;
+      p->mt = M <= 16 ? 16 : 32;
+      p->rpw = 16;
+      p->tiles_m = ceil_div(M, p->mt);
+      p->tiles_n = ceil_div(N, p->rpw);
+      p->split = 1;
+      const int64_t phases = ceil_div(nb, 2 * kSkinnyPairs);
+      const int wmax = p->mt == 16 ? 16 : 8;
+      const int64_t wtarget = (p->mt == 32 ? 8 : 16) * (int64_t)kCUs;
+      const int64_t tiles = p->tiles_m * p->tiles_n;
+      int w = 4;
+      while (w < wmax && tiles * w < wtarget && phases >= 2 * w) w *= 2;
+      p->waves = w;
+      p->kchunk = ceil_div(phases, w);                 // phases per wave
+      const int64_t sk_rows = p->tiles_m * p->mt;
+      if (sk_rows * phases * 256 > ((int64_t)1 << 30)) return MM_ERR_SHAPE;
+      p->sk_rows = sk_rows;
+      p->sk_phases = phases;
+      p->off_sq = off; off = align_up(off + (size_t)sk_rows * phases * 256, 256);
+      p->off_ss = off; off = align_up(off + (size_t)sk_rows * phases * 32, 256);
+    } else if (mma) {
       // 16-row workgroups whose waves split K among themselves (no split
       // across workgroups, so no partial sums in the workspace); passes of
       // 8 src1 rows (two blocks per MFMA), 16 or 32.
@@ -304,6 +340,8 @@ int validate_mul_mat(int type, const void* src0, const void* src1, const void* d
   if (d % 4) return MM_ERR_ALIGN;
   if (type == MM_TYPE_Q4_0) {
     if (s0 % 2 || s1 % 16) return MM_ERR_ALIGN;
+  } else if (type == MM_TYPE_Q4_0R) {
+    if (s0 % 16 || s1 % 16) return MM_ERR_ALIGN;
   } else if (type == MM_TYPE_F16) {
     if (s0 % 2 || s1 % 4) return MM_ERR_ALIGN;
   } else {
@@ -315,7 +353,9 @@ int validate_mul_mat(int type, const void* src0, const void* src1, const void* d
     if ((uintptr_t)ws % 256) return MM_ERR_ALIGN;
   }
   const size_t dst_bytes = dst ? (size_t)M * (size_t)N * 4 : 0;
-  const size_t s0_bytes = src0 ? (size_t)N * (size_t)row_bytes(type, K) : 0;
+  const size_t s0_bytes = !src0 ? 0
+                          : type == MM_TYPE_Q4_0R ? (size_t)repacked_bytes(N, K)
+                                                  : (size_t)N * (size_t)row_bytes(type, K);
   const size_t s1_bytes = src1 ? (size_t)M * (size_t)K * 4 : 0;
   if (overlaps(dst, dst_bytes, src0, s0_bytes) || overlaps(dst, dst_bytes, src1, s1_bytes))
     return MM_ERR_ALIAS;

@@ -19,6 +19,7 @@ namespace qsg {
 constexpr int kQK = 32;            // values per Q4_0 / Q8_0 block
 constexpr int kQ4Bytes = 18;       // bytes per Q4_0 block
 constexpr int kQ8Bytes = 34;       // bytes per Q8_0 block
+constexpr int kQ4RChunk = 2304;    // repacked Q4_0: bytes per 16-row tile and phase of 8 blocks
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kWideI8KB = 4;       // Q4_0 blocks per LDS stage, int8 wide kernel
 constexpr int kNarrowQ4MaxM = 8;   // largest M the Q4_0 narrow kernel takes in one pass
@@ -41,6 +42,7 @@ enum KernelKind {
   KK_F_NARROW = 4,  // f16 or f32 src0
   KK_F16_WIDE = 5,
   KK_Q4_MMA = 6,    // skinny Q4_0 on int8 MFMA (16 weight rows per workgroup)
+  KK_Q4R_SKINNY = 9, // skinny Q4_0 on repacked weights (int8 MFMA, operands loaded as stored)
   KK_F_MMA = 8,     // skinny F16 / F32 on the 16x16 MFMA (16 weight rows per workgroup,
                     // passes of 16 src1 rows, waves split K)
 };
@@ -98,5 +100,9 @@ int validate_mul_mat(int type, const void* src0, const void* src1, const void* d
 int validate_quantize(int out_type, const void* x, const void* y, int64_t nrows, int64_t k);
 
 int64_t row_bytes(int type, int64_t K);
+
+// Bytes of N x K Q4_0 weights in the repacked layout (repack.hip): tiles of
+// 16 rows x phases of 8 blocks, padded; -1 for an invalid shape.
+int64_t repacked_bytes(int64_t N, int64_t K);
 
 }  // namespace qsg

@@ -463,6 +463,183 @@ hipError_t launch_8(const Plan& p, const Q4Args& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// ---- Repacked weights (Q4_0R, repack.hip): per 16-row tile and phase of 8
+// blocks one 2304-byte chunk whose 16-byte lane pieces are already this
+// kernel's A operands (lane i + 16 g: code bytes 4 g .. 4 g + 3 of row i, for
+// 4 blocks per piece) followed by the rows' scales.  A phase is two 16-byte
+// loads of codes and one of scales per lane and row tile: no LDS patch, no
+// funnel shifts.  Blocks past K are zero padding in both the weights and the
+// operand-order wdata, so every wave runs whole phases.
+template <int MP, int RT>
+struct PhaseR {
+  v4i w[RT][2];               // code dwords of blocks 0..3 and 4..7 of this lane's row
+  v4i sc[RT];                 // the row's 8 scales (binary16)
+  v4i act[MP][kPH];
+  float da[MP][2 * kPH];
+};
+
+template <int MP, int RT>
+__device__ __forceinline__ void load_phase_r(PhaseR<MP, RT>& P, const Q4Args& a,
+                                             const uint8_t* const (&tbase)[RT], int f, int ty) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const uint8_t* c = tbase[rt] + (int64_t)f * kQ4RChunk;
+    P.w[rt][0] = *(const __attribute__((address_space(1))) v4i*)(c + 16 * lane);
+    P.w[rt][1] = *(const __attribute__((address_space(1))) v4i*)(c + 1024 + 16 * lane);
+    P.sc[rt] = *(const __attribute__((address_space(1))) v4i*)(c + 2048 + 16 * (lane & 15));
+  }
+  const __amdgpu_buffer_rsrc_t rq = wdata_rsrc(a.sq, a.sq_bytes);
+  const __amdgpu_buffer_rsrc_t rs = wdata_rsrc(a.ss, a.ss_bytes);
+#pragma unroll
+  for (int t = 0; t < MP; ++t) {
+    const int tp = (ty * MP + t) * a.sk_phases + f;
+    const bool rv = (lane & 15) < a.M - (ty * MP + t) * 16;
+    const int qo = rv ? tp * 4096 + 16 * lane : kSkip;
+#pragma unroll
+    for (int j = 0; j < kPH; ++j) P.act[t][j] = bload128(rq, rv ? qo + 1024 * j : kSkip);
+    const bool sv = rv && lane < 16;
+    const v4i s0 = bload128(rs, sv ? (tp * 16 + lane) * 32 : kSkip);
+    const v4i s1 = bload128(rs, sv ? (tp * 16 + lane) * 32 + 16 : kSkip);
+    P.da[t][0] = __int_as_float(s0[0]); P.da[t][1] = __int_as_float(s0[1]);
+    P.da[t][2] = __int_as_float(s0[2]); P.da[t][3] = __int_as_float(s0[3]);
+    P.da[t][4] = __int_as_float(s1[0]); P.da[t][5] = __int_as_float(s1[1]);
+    P.da[t][6] = __int_as_float(s1[2]); P.da[t][7] = __int_as_float(s1[3]);
+  }
+}
+
+template <int MP, int RT, bool kDump>
+__device__ __forceinline__ void compute_phase_r(const PhaseR<MP, RT>& P, float (&acc)[RT][MP][4],
+                                                int f, int n0, int m0, const Q4Args& a) {
+  const int lane = threadIdx.x & 63;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int nb = a.K / 32;
+#pragma unroll
+  for (int kb = 0; kb < 2 * kPH; ++kb) {
+    const int b = 8 * f + kb;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const long A = nibbles_x16((uint32_t)P.w[rt][kb >> 2][kb & 3]);
+      const uint32_t sw = (uint32_t)P.sc[rt][kb >> 1];
+      const float dw = f16_bits_to_f32((kb & 1) ? sw >> 16 : sw);
+#pragma unroll
+      for (int t = 0; t < MP; ++t) {
+        const v4i& ac = P.act[t][kb >> 1];
+        const long B = (kb & 1) ? (long)(((uint64_t)(uint32_t)ac.w << 32) | (uint32_t)ac.z)
+                                : (long)(((uint64_t)(uint32_t)ac.y << 32) | (uint32_t)ac.x);
+        const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const v4f sc = scale_tile(dw, P.da[t][kb]);
+        acc[rt][t][0] = fmaf((float)D.x, sc.x, acc[rt][t][0]);
+        acc[rt][t][1] = fmaf((float)D.y, sc.y, acc[rt][t][1]);
+        acc[rt][t][2] = fmaf((float)D.z, sc.z, acc[rt][t][2]);
+        acc[rt][t][3] = fmaf((float)D.w, sc.w, acc[rt][t][3]);
+        if (kDump && b < nb) {
+          const int m = m0 + 16 * t + i16;
+          const int Dv[4] = {D.x, D.y, D.z, D.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = n0 + 16 * rt + 4 * g + r;
+            if (m < a.M && n >= a.n0 && n < a.n1)
+              a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + b] = Dv[r] / 16;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Workgroup: RT x 16 weight rows; its W waves split the phases into runs of
+// pp phases and add their partial tiles in LDS at the end in a fixed order.
+template <int MP, int RT, int W, bool kDump>
+__global__ __launch_bounds__(64 * W)
+void k_q4r_skinny(Q4Args a, int pp) {
+  __shared__ float red[W * RT * MP * 4 * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nb = a.K / 32, phases = (nb + 7) / 8, tiles = (a.N + 15) / 16;
+  const int n0 = blockIdx.x * 16 * RT, ty = blockIdx.y, m0 = ty * 16 * MP;
+  const int f0 = wave * pp < phases ? wave * pp : phases;
+  const int f1 = f0 + pp < phases ? f0 + pp : phases;
+  const uint8_t* tbase[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int tt = blockIdx.x * RT + rt;
+    tt = tt < tiles ? tt : tiles - 1;                // a missing tile's outputs are dropped
+    tbase[rt] = a.w + (int64_t)tt * phases * kQ4RChunk;
+  }
+
+  float acc[RT][MP][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < MP; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[rt][t][r] = 0.0f;
+
+  // Two register sets, the next phase's loads in flight while one is
+  // computed.
+  PhaseR<MP, RT> P0, P1;
+  const int nph = f1 - f0;
+  if (nph > 0) load_phase_r<MP, RT>(P0, a, tbase, f0, ty);
+  int f = 0;
+  for (; f + 2 < nph; f += 2) {
+    load_phase_r<MP, RT>(P1, a, tbase, f0 + f + 1, ty);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase_r<MP, RT, kDump>(P0, acc, f0 + f, n0, m0, a);
+    __builtin_amdgcn_sched_barrier(0);
+    load_phase_r<MP, RT>(P0, a, tbase, f0 + f + 2, ty);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase_r<MP, RT, kDump>(P1, acc, f0 + f + 1, n0, m0, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (f + 1 < nph) {
+    load_phase_r<MP, RT>(P1, a, tbase, f0 + f + 1, ty);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase_r<MP, RT, kDump>(P0, acc, f0 + f, n0, m0, a);
+    compute_phase_r<MP, RT, kDump>(P1, acc, f0 + f + 1, n0, m0, a);
+  } else if (f < nph) {
+    compute_phase_r<MP, RT, kDump>(P0, acc, f0 + f, n0, m0, a);
+  }
+
+  constexpr int NT = RT * MP;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < MP; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[((wave * NT + rt * MP + t) * 4 + r) * 64 + lane] = acc[rt][t][r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < NT * 256; idx += 64 * W) {
+    const int tt = idx >> 8, r = (idx >> 6) & 3, l = idx & 63;
+    const int rt = tt / MP, t = tt - rt * MP;
+    float s = 0.0f;
+    for (int w2 = 0; w2 < W; ++w2) s += red[((w2 * NT + tt) * 4 + r) * 64 + l];
+    const int m = m0 + 16 * t + (l & 15);
+    const int n = n0 + 16 * rt + 4 * (l >> 4) + r;
+    if (m < a.M && n < a.N) a.dst[(int64_t)m * a.N + n] = s;
+  }
+}
+
+template <int MP, int RT, int W>
+hipError_t launch_r(const Plan& p, const Q4Args& a, hipStream_t s) {
+  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1u);
+  const int pp = (int)p.kchunk;                     // phases per wave
+  if (a.dots) hipLaunchKernelGGL((k_q4r_skinny<MP, RT, W, true>), grid, dim3(64 * W), 0, s, a, pp);
+  else hipLaunchKernelGGL((k_q4r_skinny<MP, RT, W, false>), grid, dim3(64 * W), 0, s, a, pp);
+  return hipGetLastError();
+}
+
+template <int MP, int RT>
+hipError_t launch_r_mp(const Plan& p, const Q4Args& a, hipStream_t s) {
+  if (p.waves == 4) return launch_r<MP, RT, 4>(p, a, s);
+  if (p.waves == 8) return launch_r<MP, RT, 8>(p, a, s);
+  if constexpr (MP == 1 && RT == 1) {
+    if (p.waves == 16) return launch_r<MP, RT, 16>(p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 bool q4_skinny_ok(int K, const void* w) {
@@ -475,6 +652,14 @@ hipError_t launch_q4_skinny(const Plan& p, const Q4Args& a, hipStream_t s) {
   if (p.mt == 16 && p.rpw == 16) return launch_mp<1, 1>(p, a, s);
   if (p.mt == 32 && p.rpw == 16) return launch_mp<2, 1>(p, a, s);
   if (p.mt == 16 && p.rpw == 32) return launch_mp<1, 2>(p, a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_q4r_skinny(const Plan& p, const Q4Args& a, hipStream_t s) {
+  if (p.split != 1 || !a.sq) return hipErrorInvalidValue;
+  if (p.mt == 16 && p.rpw == 16) return launch_r_mp<1, 1>(p, a, s);
+  if (p.mt == 32 && p.rpw == 16) return launch_r_mp<2, 1>(p, a, s);
+  if (p.mt == 16 && p.rpw == 32) return launch_r_mp<1, 2>(p, a, s);
   return hipErrorInvalidValue;
 }
 

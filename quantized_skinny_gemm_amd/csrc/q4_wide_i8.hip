@@ -25,6 +25,7 @@
 // notes, III.C SBI-GeMM: a second kernel reduces across the input-dim tiles).
 #include "device.h"
 #include "kernels.h"
+#include "../../include/mm.h"
 
 namespace qsg {
 
@@ -75,7 +76,11 @@ __device__ __forceinline__ v8h scale_operand(float d, int h) {
   return v;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool kPairs, bool kDump>
+// kRep: the weights are in the repacked layout (repack.hip): a stage of
+// KB = 4 blocks is half a phase of each 16-row tile, 1 KB of codes (each
+// lane piece: code bytes 4 g .. 4 g + 3 of one row for the 4 blocks) and the
+// rows' scales, staged with one 16-byte load per piece.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool kPairs, bool kDump, bool kRep = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, int tiles_m,
                                                                    int tiles_n, int kchunk,
                                                                    int split) {
@@ -117,17 +122,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
   // clamped into the matrices; what lies outside the tile or the K range is
   // masked when the registers are written to LDS (codes 8 and zero scales for
   // weights, zero codes and scales for activations).
-  constexpr int WI = kPairs ? (BN * (KB / 2) + NT - 1) / NT : (BN * KB + NT - 1) / NT;
+  static_assert(!kRep || (KB == 4 && BN % 16 == 0), "repacked stages are half a phase of whole tiles");
+  constexpr int WI = kRep ? (BN * 4 + NT - 1) / NT
+                   : kPairs ? (BN * (KB / 2) + NT - 1) / NT : (BN * KB + NT - 1) / NT;
   constexpr int AI = (BM * KB * 2 + NT - 1) / NT;
   constexpr int SI = (BM * KB + NT - 1) / NT;
-  uint32_t wreg[WI][9];
+  uint32_t wreg[WI][kRep ? 6 : 9];
+  const int rtiles = (N + 15) / 16, rphases = (nb + 7) / 8;
   v4i areg[AI];
   float sreg[SI];
   auto load_stage = [&](int kb) {
 #pragma unroll
     for (int u = 0; u < WI; ++u) {
       const int i = tid + u * NT;
-      if (kPairs) {
+      if (kRep) {
+        // piece (tile tq, lane l) of this half phase, and lane l's row scales
+        const int ii = i < BN * 4 ? i : 0;
+        const int tq = ii >> 6, l = ii & 63;
+        int tile = n0 / 16 + tq;
+        tile = tile < rtiles ? tile : rtiles - 1;
+        const __attribute__((address_space(1))) uint8_t* c =
+            (const __attribute__((address_space(1))) uint8_t*)(a.w + ((int64_t)tile * rphases + kb / 8) * kQ4RChunk);
+        const v4i q = *(const __attribute__((address_space(1))) v4i*)(c + ((kb / 4) & 1) * 1024 + 16 * l);
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const v2i d = *(const __attribute__((address_space(1))) v2i*)(c + 2048 + 16 * (l & 15) + ((kb / 4) & 1) * 8);
+        wreg[u][0] = (uint32_t)q.x; wreg[u][1] = (uint32_t)q.y;
+        wreg[u][2] = (uint32_t)q.z; wreg[u][3] = (uint32_t)q.w;
+        wreg[u][4] = (uint32_t)d.x; wreg[u][5] = (uint32_t)d.y;
+      } else if (kPairs) {
         const int r = (i / (KB / 2)) % BN, pp = i % (KB / 2);
         const int n = n0 + r < N ? n0 + r : N - 1;
         const int b = kb + 2 * pp < kb1 ? kb + 2 * pp : kb0;
@@ -167,7 +189,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
 #pragma unroll
     for (int u = 0; u < WI; ++u) {
       const int i = tid + u * NT;
-      if (kPairs) {
+      if (kRep) {
+        if (i >= BN * 4) continue;
+        const int tq = i >> 6, l = i & 63;
+        const int r = 16 * tq + (l & 15), g = l >> 4;
+        const bool okr = n0 + r < N;
+        // codes: finite for every row and block (padding is q = 8); a
+        // block outside the tile or the K range gets a zero scale
+#pragma unroll
+        for (int bb = 0; bb < KB; ++bb) {
+          *reinterpret_cast<uint32_t*>(sB + r * PITCH + bb * 32 + 4 * g) = nib_lo_signed(wreg[u][bb]);
+          *reinterpret_cast<uint32_t*>(sB + r * PITCH + bb * 32 + 16 + 4 * g) = nib_hi_signed(wreg[u][bb]);
+        }
+        if (g == 0) {
+#pragma unroll
+          for (int bb = 0; bb < KB; ++bb) {
+            const uint32_t dw = wreg[u][4 + (bb >> 1)];
+            sBd[bb * BN + r] = (okr && kb + bb < kb1) ? f16_bits_to_f32((bb & 1) ? dw >> 16 : dw) : 0.0f;
+          }
+        }
+      } else if (kPairs) {
         if (i >= BN * (KB / 2)) continue;
         const int r = i / (KB / 2), pp = i % (KB / 2);
         const int b = kb + 2 * pp;
@@ -278,7 +319,10 @@ hipError_t launch_cfg(const Plan& p, const Q4Args& a, bool pairs, hipStream_t s)
   const dim3 block(64 * WMS * WNS);
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n, kc = (int)p.kchunk, sp = p.split;
   const bool dump = a.dots != nullptr;
-  if (pairs) {
+  if (p.type == MM_TYPE_Q4_0R) {
+    if (dump) hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, false, true, true>), grid, block, 0, s, a, tm, tn, kc, sp);
+    else hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, false, false, true>), grid, block, 0, s, a, tm, tn, kc, sp);
+  } else if (pairs) {
     if (dump) hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, true, true>), grid, block, 0, s, a, tm, tn, kc, sp);
     else hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, true, false>), grid, block, 0, s, a, tm, tn, kc, sp);
   } else {

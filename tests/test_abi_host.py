@@ -271,3 +271,32 @@ def test_noalloc_entry_point_host_checks():
     assert qs.lib.mm_mul_mat_q4_0_f32_noalloc(FAKE, FAKE + 2**30, None, 1, 64, 64, None) == NULL
     assert qs.lib.mm_mul_mat_q4_0_f32_noalloc(FAKE, FAKE + 2**30 + 4, FAKE + 2**31, 1, 64, 64,
                                               None) == ALIGN
+
+
+def test_repack_host_checks():
+    R = qs.MM_TYPE_Q4_0R
+    assert qs.repacked_bytes(16, 256) == 2304
+    assert qs.repacked_bytes(17, 256) == 2 * 2304
+    assert qs.repacked_bytes(4096, 4096) == 256 * 16 * 2304 == 4096 * 4096 // 32 * 18
+    assert qs.repacked_bytes(16, 288) == 2 * 2304       # 9 blocks: a padded second phase
+    assert qs.repacked_bytes(16, 48) == -1
+    assert qs.row_bytes(R, 4096) == -1
+    # argument checks before any HIP call
+    assert qs.lib.mm_repack_q4_0(FAKE, FAKE + 2**30, 16, 48, None) == SHAPE
+    assert qs.lib.mm_repack_q4_0(None, FAKE, 16, 64, None) == NULL
+    assert qs.lib.mm_repack_q4_0(FAKE + 1, FAKE + 2**30, 16, 64, None) == ALIGN
+    assert qs.lib.mm_repack_q4_0(FAKE, FAKE + 2**30 + 8, 16, 64, None) == ALIGN
+    assert qs.lib.mm_unpack_q4_0(FAKE + 8, FAKE + 2**30, 16, 64, None) == ALIGN
+    assert qs.lib.mm_repack_q4_0(FAKE, FAKE + 16, 16, 64, None) == ALIAS
+    assert qs.lib.mm_repack_q4_0(None, None, 0, 64, None) == OK
+    # products on repacked weights: the skinny kernel from M = 1, the wide one past 32
+    for m, want in ((1, 3), (2, 3), (8, 3), (32, 3), (33, 2), (512, 2)):
+        v, split, rows, cols, launches = qs.dispatch(R, m, 4096, 4096)
+        assert v == want, (m, v)
+        assert launches == 2 + (1 if split > 1 else 0)
+    assert qs.lib.mm_debug_mul_mat(R, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 1, None, 0, None) == ARG
+    need = qs.workspace_size(R, 4, 256, 512)
+    assert need > 0
+    st = qs.lib.mm_mul_mat_q4_0r_f32(FAKE + 8, FAKE + 2**30, FAKE + 2**31, 4, 256, 512,
+                                     FAKE + 2**32, need, None)
+    assert st == ALIGN
