@@ -345,6 +345,93 @@ def run_sweep(reps: int, out_path: str | None):
     return results
 
 
+# ------------------------------------------------------------ dispatch table
+TABLE_TYPES = {   # type -> (shapes N x K, kernel variants it has)
+    "q4_0": ([(256, 512), (4096, 4096), (11008, 4096), (4096, 11008), (14336, 4096),
+              (4096, 14336), (128256, 4096)], (1, 2, 3)),
+    "q4_0r": ([(4096, 4096), (11008, 4096), (4096, 11008), (14336, 4096), (4096, 14336),
+               (128256, 4096)], (2, 3)),
+    "f16": ([(4096, 4096), (11008, 4096), (14336, 4096), (128256, 4096)], (1, 2, 3)),
+    "f32": ([(4096, 4096), (11008, 4096)], (1, 3)),
+}
+TABLE_MS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]
+TABLE_MAX_M = 0x7FFFFFFF
+
+
+def table_ranges(best):
+    """[(M_lo, M_hi, variant)] from {measured M: fastest variant}: each
+    crossover at the geometric mean of the measured M on either side, the
+    last measured choice kept beyond; adjacent equal choices merged."""
+    ms = sorted(best)
+    out = []
+    for i, m in enumerate(ms):
+        lo = 1 if i == 0 else out[-1][1] + 1
+        hi = TABLE_MAX_M if i + 1 == len(ms) else int((m * ms[i + 1]) ** 0.5)
+        if out and out[-1][2] == best[m]:
+            out[-1] = (out[-1][0], hi, best[m])
+        else:
+            out.append((lo, hi, best[m]))
+    return out
+
+
+def tune_table(path: str, reps: int = 5):
+    """Times every kernel variant of every type on the workload shapes at M =
+    2^n (graph replays over distinct weight copies, as run_sweep) and writes
+    the dispatch table the library reads (one line per M range)."""
+    import torch
+    import quantized_skinny_gemm_amd as qs
+
+    dev = torch.device("cuda:0")
+    s = torch.cuda.Stream()
+    gen = torch.Generator(device=dev)
+    mm_types = {"q4_0": qs.MM_TYPE_Q4_0, "q4_0r": qs.MM_TYPE_Q4_0R, "f16": qs.MM_TYPE_F16,
+                "f32": qs.MM_TYPE_F32}
+    lines = ["# Kernel choice per shape, measured on one MI355X by", "#   python bench.py --tune-table <file>",
+             "# type N K M_lo M_hi variant   (1 narrow, 2 wide, 3 skinny MFMA)"]
+    for t, (shapes, variants) in TABLE_TYPES.items():
+        mm_type = mm_types[t]
+        for n, k in shapes:
+            gen.manual_seed(n + 3 * k)
+            wf = torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02
+            if t == "q4_0":
+                base = qs.quantize_q4_0(wf)
+            elif t == "q4_0r":
+                base = qs.repack_q4_0(qs.quantize_q4_0(wf), k)
+            elif t == "f16":
+                base = wf.to(torch.float16)
+            else:
+                base = wf
+            del wf
+            nbytes = base.numel() * base.element_size()
+            copies = max(1, min(32, int(-(-MALL_DEFEAT_BYTES // nbytes))))
+            wcopies = [base] + [base.clone() for _ in range(copies - 1)]
+            best = {}
+            for m in TABLE_MS:
+                x = torch.randn((m, k), generator=gen, device=dev, dtype=torch.float32)
+                dst = torch.empty((m, n), dtype=torch.float32, device=dev)
+                times = {}
+                for v in variants:
+                    wsb = qs.debug_workspace_size(mm_type, m, n, k, v)
+                    wsp = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+                    torch.cuda.synchronize()
+                    calls = [(t, qs.lib.mm_debug_mul_mat,
+                              (mm_type, wc.data_ptr(), x.data_ptr(), dst.data_ptr(), None, m, n, k,
+                               0, 0, v, wsp.data_ptr(), wsb, s.cuda_stream), 0.0) for wc in wcopies]
+                    times[v] = time_graph(torch, s, calls, reps) * 1e3 / len(calls)
+                    del wsp
+                best[m] = min(times, key=times.get)
+                log(f"table {t:5s} {n:6d}x{k:<6d} M={m:4d} " +
+                    " ".join(f"v{v} {us:9.2f}us" for v, us in times.items()) + f" -> v{best[m]}")
+                del x, dst
+            for lo, hi, v in table_ranges(best):
+                lines.append(f"{t} {n} {k} {lo} {hi} {v}")
+            del wcopies, base
+            torch.cuda.empty_cache()
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    log(f"wrote {path}")
+
+
 # ------------------------------------------------------------ cpu leg
 def _oracle_layers(budget_s: float):
     """One worker's leg: the CPU oracle (as it stands) on one Llama-7B layer's 7
@@ -466,6 +553,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--only-step", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--tune-table", metavar="FILE",
+                    help="time every kernel variant at M = 2^n on the workload shapes and write "
+                         "the dispatch table the library reads")
     ap.add_argument("--sweep", metavar="JSON", nargs="?", const="",
                     help="time every product of the five workloads instead (table on "
                          "stderr, optional JSON file)")
@@ -482,6 +572,9 @@ def main():
         return
     if args.sweep is not None:
         run_sweep(max(2, args.kernel_reps // 4), args.sweep or None)
+        return
+    if args.tune_table:
+        tune_table(args.tune_table)
         return
 
     # the CPU leg first, before this process touches the GPU (its workers are

@@ -27,7 +27,7 @@ BENCH_LIB = os.path.join(ROOT, "bench_read.so")
 
 HIP_SOURCES = ["api.hip", "quantize.hip", "q4_narrow.hip", "q4_mma.hip", "q4_skinny.hip",
                "q4_wide_i8.hip", "f_kernels.hip", "repack.hip"]
-CXX_SOURCES = ["plan.cpp"]
+CXX_SOURCES = ["plan.cpp", "dispatch_table.cpp"]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [
@@ -75,7 +75,7 @@ def build(verbose: bool = False) -> str:
             if verbose and (r.stdout or r.stderr):
                 print(r.stdout + r.stderr)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-ldl", "-o", tmp])
     os.replace(tmp, LIB)
     if os.path.exists(BENCH_SRC):
         tmp = BENCH_LIB + ".tmp"

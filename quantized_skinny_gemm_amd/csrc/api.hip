@@ -319,9 +319,11 @@ int group_plan(int count, const int64_t* Ns, int64_t M, int64_t K, Plan* whole, 
   if (st != MM_OK) return st;
   size_t need = whole->ws_bytes;
   if (whole->kind == KK_Q4_WIDE || whole->kind == KK_Q4_MMA) {
+    // every member takes the group's kernel (one INIT writes the wdata
+    // layout of that kernel for all of them)
     for (int i = 0; i < count; ++i) {
       Plan pi;
-      st = make_plan(MM_TYPE_Q4_0, M, Ns[i], K, 0, &pi);
+      st = make_plan(MM_TYPE_Q4_0, M, Ns[i], K, whole->variant, &pi);
       if (st != MM_OK) return st;
       if (pi.ws_bytes > need) need = pi.ws_bytes;
     }
@@ -404,7 +406,7 @@ int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const*
   for (int i = 0; i < count; ++i) {
     if (Ns[i] == 0) continue;
     Plan pi;
-    make_plan(MM_TYPE_Q4_0, M, Ns[i], K, 0, &pi);
+    make_plan(MM_TYPE_Q4_0, M, Ns[i], K, whole.variant, &pi);
     st = q4_product(pi, q4_args(pi, src0s[i], dsts[i], nullptr, M, Ns[i], K, 0, 0, ws), nullptr, s);
     if (st != MM_OK) return st;
   }

@@ -58,6 +58,11 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   if (type == MM_TYPE_Q4_0R && variant == 1) return MM_ERR_ARG;   // no narrow kernel for it
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
   if (K == 0) { p->kind = KK_ZERO; return MM_OK; }
+  if (variant == 0) {
+    const int tv = dispatch_table_variant(type, M, N, K);
+    dispatch_log(type, M, N, K, tv, tv != 0);
+    variant = tv;
+  }
 
   if (type == MM_TYPE_Q4_0 || type == MM_TYPE_Q4_0R) {
     const bool rep = type == MM_TYPE_Q4_0R;

@@ -78,7 +78,16 @@ struct Plan {
   size_t ws_bytes = 0;
 };
 
-// Builds the plan; returns 0 (MM_OK) or a negative mm_status.
+// The measured dispatch table (dispatch_table.cpp): the variant listed for
+// (type, N, K) at this M, or 0 when the table has none (or no table was
+// found).  The file is read once per process.
+int dispatch_table_variant(int type, int64_t M, int64_t N, int64_t K);
+// Logs a dispatch decision on stderr when MM_VERBOSE is set.
+void dispatch_log(int type, int64_t M, int64_t N, int64_t K, int variant, bool from_table);
+
+// Builds the plan; returns 0 (MM_OK) or a negative mm_status.  variant 0
+// takes the table's choice for the shape if it lists one, else the built-in
+// rules.
 // allow_split = false keeps K whole (used when several matrices share one
 // launch: their outputs are written directly, never as split partials).
 int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p,

@@ -134,9 +134,11 @@ def test_debug_entry_argument_checks():
     assert qs.lib.mm_debug_mul_mat(9, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 0, None, 0, None) == ARG
 
 
+# The built-in rules, at shapes the measured dispatch table does not list
+# (4100 rows); the table itself is tested in test_dispatch_table.py.
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64, 100, 128, 512])
 def test_dispatch_threshold_and_workspace(m):
-    variant, split, rows, cols, launches = qs.dispatch(Q4, m, 4096, 4096)
+    variant, split, rows, cols, launches = qs.dispatch(Q4, m, 4100, 4096)
     # M <= 2: narrow kernel with INIT fused (one launch); up to 32 src1 rows:
     # the skinny MFMA kernel; beyond: the wide kernel.  Both of the latter
     # run INIT first, and a split adds the reduce kernel.
@@ -144,7 +146,7 @@ def test_dispatch_threshold_and_workspace(m):
     assert variant == want
     assert launches == (0 if m <= 2 else 1) + 1 + (1 if split > 1 else 0)
     assert split >= 1
-    ws = qs.workspace_size(Q4, m, 4096, 4096)
+    ws = qs.workspace_size(Q4, m, 4100, 4096)
     # at least the wdata: codes + scale + bias per block
     assert ws >= m * 4096 + 2 * 4 * m * 128
     if variant == 1:
@@ -157,7 +159,7 @@ def test_dispatch_threshold_and_workspace(m):
     # F16: M = 1 narrow, up to 16 rows the skinny MFMA kernel, beyond the
     # wide kernel; F32: narrow at M = 1, skinny MFMA from 2 rows
     for t in (F16, F32):
-        fv, fsplit, frows, fcols, flaunch = qs.dispatch(t, m, 4096, 4096)
+        fv, fsplit, frows, fcols, flaunch = qs.dispatch(t, m, 4100, 4096)
         # (F16 up to 64 rows at this N = 4096 also takes the skinny kernel)
         fwant = 1 if m == 1 else 3 if (m <= 64 or t == F32) else 2
         assert fv == fwant
@@ -166,13 +168,13 @@ def test_dispatch_threshold_and_workspace(m):
             # themselves: one launch, no workspace
             assert frows == 16 and fcols in (4, 8, 16)
             assert fsplit == 1 and flaunch == 1
-            assert qs.workspace_size(t, m, 4096, 4096) == 0
+            assert qs.workspace_size(t, m, 4100, 4096) == 0
         elif fv == 2:
             # the wide F16 kernel converts src1 to binary16 in the workspace,
             # with one power-of-two exponent per row
-            assert fsplit == 1 and qs.workspace_size(t, m, 4096, 4096) >= m * 4096 * 2 + 4 * m
+            assert fsplit == 1 and qs.workspace_size(t, m, 4100, 4096) >= m * 4096 * 2 + 4 * m
         else:
-            assert fsplit == 1 and qs.workspace_size(t, m, 4096, 4096) == 0
+            assert fsplit == 1 and qs.workspace_size(t, m, 4100, 4096) == 0
 
 
 def test_split_k_when_grid_is_small():
@@ -237,9 +239,10 @@ def test_group_argument_checks():
 def test_measured_tile_and_wave_choices():
     # Q4_0 wide int8 tiles (rows, cols): 64 x 128 up to M = 64 with few weight
     # rows and from M = 65 to 128 with many, 64 x 64 / 128 x 128 otherwise
+    # (built-in rules: shapes off the measured table, 16 rows more)
     for m, n, want in ((64, 4096, (64, 128)), (64, 14336, (64, 64)), (128, 14336, (64, 128)),
                        (100, 11008, (64, 128)), (128, 4096, (128, 128)), (512, 14336, (128, 128))):
-        v, _, rows, cols, _ = qs.dispatch(Q4, m, n, 4096 if n > 4096 else 14336)
+        v, _, rows, cols, _ = qs.dispatch(Q4, m, n + 16, 4096 if n > 4096 else 14336)
         assert v == 2 and (rows, cols) == want, (m, n, rows, cols)
     # Q4_0 at M = 1 (the fused kernel): one weight row per wave at every size
     for n, k in ((256, 512), (4096, 4096), (4096, 11008), (11008, 4096), (12288, 4096)):
@@ -289,9 +292,10 @@ def test_repack_host_checks():
     assert qs.lib.mm_unpack_q4_0(FAKE + 8, FAKE + 2**30, 16, 64, None) == ALIGN
     assert qs.lib.mm_repack_q4_0(FAKE, FAKE + 16, 16, 64, None) == ALIAS
     assert qs.lib.mm_repack_q4_0(None, None, 0, 64, None) == OK
-    # products on repacked weights: the skinny kernel from M = 1, the wide one past 32
+    # products on repacked weights (built-in rules, a shape off the measured
+    # table): the skinny kernel from M = 1, the wide one past 32
     for m, want in ((1, 3), (2, 3), (8, 3), (32, 3), (33, 2), (512, 2)):
-        v, split, rows, cols, launches = qs.dispatch(R, m, 4096, 4096)
+        v, split, rows, cols, launches = qs.dispatch(R, m, 4112, 4096)
         assert v == want, (m, v)
         assert launches == 2 + (1 if split > 1 else 0)
     assert qs.lib.mm_debug_mul_mat(R, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 1, None, 0, None) == ARG
