@@ -38,6 +38,10 @@ import os
 import sys
 
 
+XCDS = 8          # MI355X: accelerator complex dies
+SIMDS = 1024      # 256 compute units x 4 SIMDs
+
+
 def _csv_rows(directory: str, suffix: str):
     files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
     if not files:
@@ -132,6 +136,12 @@ def counters_markdown(directories, only: str = "") -> str:
         if "SQ_WAIT_INST_ANY" in avg and avg.get("SQ_WAVE_CYCLES"):
             derived.append(("wave cycles waiting on a dependency",
                             f"{avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.2f}"))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and avg.get("GRBM_GUI_ACTIVE"):
+            # GRBM_GUI_ACTIVE sums the elapsed cycles of the 8 XCDs; the MFMA
+            # busy cycles are summed over all 1024 SIMDs (256 CUs x 4)
+            elapsed = avg["GRBM_GUI_ACTIVE"] / XCDS
+            derived.append(("matrix cores busy (share of SIMD cycles)",
+                            f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (elapsed * SIMDS):.3f}"))
         if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
             derived.append(("LDS cycles lost to bank conflicts",
                             f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.2f}"))
