@@ -37,6 +37,10 @@ HIPCC_FLAGS = [
     # MFMA results in ordinary VGPRs: the scale epilogues read every output
     # register, and an accumulation-register result costs one extra move each
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # the leading kernel arguments (up to 14 dwords) arrive in scalar
+    # registers at wave launch instead of through a load from the kernel
+    # argument segment: a wave can address its first loads at once
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
     "-Wno-unused-command-line-argument",
 ]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]

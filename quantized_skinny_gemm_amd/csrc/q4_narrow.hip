@@ -495,14 +495,41 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
 // Fused small-M kernel (MT <= 2 rows of src1, K/32 even, 4-byte aligned
 // weights, no K split): the common decode case, kept as lean as possible.
 // Each workgroup quantizes src1 into LDS once, then walks row groups
-// g = blockIdx.x, blockIdx.x + gridDim.x, ...; wave w of the group owns R
-// rows (R = 2, or 1 for M = 1 with many rows: twice the row groups), rows
-// 8R g + R w .. 8R g + R w + R - 1, and lane l the K units (block pairs) l, l + 64,
-// ...  The steps (group, K unit range) of a wave form one flat sequence
-// whose next step's weights are loaded before the current one is computed.
-template <int MT, int NR, int R, int WAVES>
+// g = blockIdx.x, blockIdx.x + G, ...; wave w of the group owns R rows
+// rows RPG g + R w .. RPG g + R w + R - 1, and lane l the K units (block
+// pairs) l, l + 64, ...  The steps (group, K unit range) of a wave form one
+// flat sequence whose next step's weights are loaded before the current one
+// is computed.
+//
+// Arguments: everything a wave needs before its first weight load (src1,
+// up to three weight matrices with their first rows, N, K, M and the grid
+// size G) comes first, in 14 dwords that the launch preloads into scalar
+// registers, so no wave waits on a memory round trip for its kernel
+// arguments before it can issue a load.  A row n belongs to matrix 0 below
+// r1, to matrix 1 below r2 and to matrix 2 beyond (r1 = r2 = N for a single
+// matrix).  Groups of more than three matrices (kMany) look their rows up
+// in the descriptor instead; the outputs always come from it (their
+// addresses are needed only at the end).
+struct FusedOut {
+  const uint8_t* w[kMaxGroup];
+  float* dst[kMaxGroup];
+  int row0[kMaxGroup + 1];
+  int count;
+};
+
+// Matrix of row n in a group of more than three (descriptor lookup).
+__device__ __forceinline__ int fused_mat(const FusedOut& fo, int n) {
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxGroup; ++j)
+    if (j < fo.count && n >= fo.row0[j]) i = j;
+  return i;
+}
+
+template <int MT, int NR, int R, int WAVES, bool kMany>
 __global__ __launch_bounds__(64 * WAVES)
-void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
+void k_q4_fused(const float* __restrict__ x, const uint8_t* w0, const uint8_t* w1,
+                const uint8_t* w2, int N, int K, int r1, int r2, int M, int G, FusedOut fo) {
   constexpr int NT = 64 * WAVES, RPG = WAVES * R;
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -514,20 +541,29 @@ void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
   const int m0 = blockIdx.y * MT;
   const int rows = M - m0 < MT ? M - m0 : MT;
   const int ngroups = (N + RPG - 1) / RPG;
-  const int G = (int)gridDim.x;
   const int mygroups = (int)blockIdx.x < ngroups ? (ngroups - 1 - (int)blockIdx.x) / G + 1 : 0;
   const int S = mygroups * SU;
   if (S == 0) return;                                // uniform over the workgroup
   int8_t* sq = smem;
   float* sd = reinterpret_cast<float*>(smem + (int64_t)MT * nb * 32);
   int32_t* sb = reinterpret_cast<int32_t*>(sd + MT * nb);
+  // output bases, read from the descriptor now (constant offsets) so that
+  // their loads are long complete when the first result is stored
+  float* const d0 = fo.dst[0];
+  float* const d1 = fo.dst[1];
+  float* const d2 = fo.dst[2];
 
-  // weight row pointer of the wave's row r at step s (rows past N clamped)
+  // weight row pointer of the wave's row r in group g (rows past N clamped)
   auto rowptr = [&](int g, int r) -> const uint8_t* {
     int n = g * RPG + wave * R + r;
     n = n < N ? n : N - 1;
-    const int i = mat_of(mats, n);
-    return mats.w[i] + (int64_t)(n - mats.row0[i]) * rb;
+    if (kMany) {
+      const int i = fused_mat(fo, n);
+      return fo.w[i] + (int64_t)(n - fo.row0[i]) * rb;
+    }
+    if (n < r1) return w0 + (int64_t)n * rb;
+    if (n < r2) return w1 + (int64_t)(n - r1) * rb;
+    return w2 + (int64_t)(n - r2) * rb;
   };
 
   // activation loads first (vmcnt retires in order), then the first weights
@@ -547,11 +583,14 @@ void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
     const int u = lane < units ? lane : 0;
     load_unit<R, true>(wv, rp, u);
   }
+  // the first weights are in flight before src1 is waited for
+  __builtin_amdgcn_sched_barrier(0);
   quant_store<NT, NR, MT>(sl, 0, rounds, v, ok, sq, sd, sb);
   for (int it0 = NR; it0 < rounds; it0 += NR) {
     quant_load<NT, NR, MT>(sl, x, it0, rounds, v, ok);
     quant_store<NT, NR, MT>(sl, it0, rounds, v, ok, sq, sd, sb);
   }
+  if (!kMany) asm volatile("" ::"s"(d0), "s"(d1), "s"(d2));
   lds_barrier();
 
   ActView av;
@@ -594,15 +633,26 @@ void k_q4_fused(Q4Mats mats, const float* __restrict__ x, int M, int N, int K) {
           if (lane == r * MT + m) mine = t;
           acc[r][m] = 0.0f;
         }
-      // output pointers of the two rows (wave-uniform lookups)
+      // output pointers of the wave's rows (wave-uniform lookups)
       float* out[R];
       int ldo[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int nr = nw + r < N ? nw + r : N - 1;
-        const int mi = mat_of(mats, nr);
-        out[r] = mats.dst[mi] + (nr - mats.row0[mi]);
-        ldo[r] = mats.row0[mi + 1] - mats.row0[mi];
+        if (kMany) {
+          const int mi = fused_mat(fo, nr);
+          out[r] = fo.dst[mi] + (nr - fo.row0[mi]);
+          ldo[r] = fo.row0[mi + 1] - fo.row0[mi];
+        } else if (nr < r1) {
+          out[r] = d0 + nr;
+          ldo[r] = r1;
+        } else if (nr < r2) {
+          out[r] = d1 + (nr - r1);
+          ldo[r] = r2 - r1;
+        } else {
+          out[r] = d2 + (nr - r2);
+          ldo[r] = N - r2;
+        }
       }
       const int r = lane / MT, m = lane % MT;
       float* o = out[0];
@@ -683,12 +733,32 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
     const size_t lds = (size_t)p.mt * nb * 40;
     const int nt = 64 * p.fuse_waves;
     const int rounds = (int)(((int64_t)p.mt * nb * 2 + nt - 1) / nt);
+    FusedOut fo;
+    for (int i = 0; i < kMaxGroup; ++i) {
+      fo.w[i] = i < mats.count ? mats.w[i] : nullptr;
+      fo.dst[i] = i < mats.count ? mats.dst[i] : nullptr;
+    }
+    for (int i = 0; i <= kMaxGroup; ++i) fo.row0[i] = mats.row0[i < mats.count ? i : mats.count];
+    fo.count = mats.count;
+    const bool many = mats.count > 3;
+    const uint8_t* w1 = mats.count > 1 ? mats.w[1] : mats.w[0];
+    const uint8_t* w2 = mats.count > 2 ? mats.w[2] : w1;
+    const int r1 = mats.count > 1 ? mats.row0[1] : a.N;
+    const int r2 = mats.count > 2 ? mats.row0[2] : a.N;
+    const int G = p.fuse_grid;
+#define QSG_FUSED_GO(MT_, NR_, R_, W_)                                                             \
+    do {                                                                                           \
+      if (many)                                                                                    \
+        hipLaunchKernelGGL((k_q4_fused<MT_, NR_, R_, W_, true>), grid, dim3(nt), lds, s, x,        \
+                           mats.w[0], w1, w2, a.N, a.K, r1, r2, a.M, G, fo);                       \
+      else                                                                                         \
+        hipLaunchKernelGGL((k_q4_fused<MT_, NR_, R_, W_, false>), grid, dim3(nt), lds, s, x,       \
+                           mats.w[0], w1, w2, a.N, a.K, r1, r2, a.M, G, fo);                       \
+    } while (0)
 #define QSG_FUSED(MT_, R_, W_)                                                                     \
     if (p.mt == MT_ && p.fuse_rpw == R_ && p.fuse_waves == W_) {                                   \
-      if (rounds <= 1)                                                                             \
-        hipLaunchKernelGGL((k_q4_fused<MT_, 1, R_, W_>), grid, dim3(nt), lds, s, mats, x, a.M, a.N, a.K); \
-      else                                                                                         \
-        hipLaunchKernelGGL((k_q4_fused<MT_, 2, R_, W_>), grid, dim3(nt), lds, s, mats, x, a.M, a.N, a.K); \
+      if (rounds <= 1) QSG_FUSED_GO(MT_, 1, R_, W_);                                               \
+      else QSG_FUSED_GO(MT_, 2, R_, W_);                                                           \
       return hipGetLastError();                                                                    \
     }
     QSG_FUSED(1, 2, 8)
@@ -697,6 +767,7 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
     QSG_FUSED(2, 2, 8)
     QSG_FUSED(2, 1, 16)
 #undef QSG_FUSED
+#undef QSG_FUSED_GO
     return hipErrorInvalidValue;
   }
   // rows per wave and waves per workgroup must match make_plan()
