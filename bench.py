@@ -551,7 +551,9 @@ def main():
                     help="skip the per-config table (every product of the five workloads)")
     ap.add_argument("--config-reps", type=int, default=5)
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--only-step", action="store_true")
+    ap.add_argument("--only-step", action="store_true",
+                    help="only the decode step and its per-launch times (for profiler runs: "
+                         "no per-matrix variant, read ceiling or config table)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--tune-table", metavar="FILE",
                     help="time every kernel variant at M = 2^n on the workload shapes and write "
@@ -678,14 +680,14 @@ def main():
             "per_kind_us": {r["kind"]: round(r["avg_us"], 4) for r in kern},
         },
     }
-    ceiling = read_ceiling(st, args.kernel_reps, s)
+    ceiling = None if args.only_step else read_ceiling(st, args.kernel_reps, s)
     if ceiling is not None:
         out["read_ceiling"] = ceiling
         log(f"plain read of the step's weights, same launch pattern: {ceiling['GBs']} GB/s "
             f"({ceiling['per_kind_us']} us per launch)")
     if cpu is not None:
         out["cpu_baseline"] = cpu
-    if not args.no_configs:
+    if not args.no_configs and not args.only_step:
         del st, grouped, single, step_calls, graph
         torch.cuda.empty_cache()
         log("timing every product of the five workloads")

@@ -205,8 +205,8 @@ def traffic(args) -> dict:
         "algorithmic_bytes_per_launch": args.algo_bytes,
         "traffic_over_algorithmic": round((read_b + write_b) / args.algo_bytes, 4)
         if args.algo_bytes else None,
-        "kernel_source": os.path.relpath(args.source, os.path.dirname(os.path.dirname(
-            os.path.abspath(__file__)))),
+        "kernel_source": os.path.relpath(os.path.abspath(args.source),
+                                         os.path.dirname(os.path.abspath(__file__))),
         "kernel_source_sha256": sha,
     }
 
