@@ -42,15 +42,15 @@ __device__ __forceinline__ uint32_t nib_hi_signed(uint32_t q) {
   return (((q >> 4) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
 }
 
-// Writes one decoded block (scale + 32 signed codes) into LDS.
-__device__ __forceinline__ void put_block(int8_t* sB, float* sBd, int bn, int r, int bb, float d,
-                                          const uint32_t (&q)[4]) {
+// Writes one decoded block (binary16 scale bits + 32 signed codes) into LDS.
+__device__ __forceinline__ void put_block(int8_t* sB, uint16_t* sBd, int bn, int r, int bb,
+                                          uint32_t d, const uint32_t (&q)[4]) {
   uint2* p = reinterpret_cast<uint2*>(sB + r * PITCH + bb * 32);
   p[0] = make_uint2(nib_lo_signed(q[0]), nib_lo_signed(q[1]));   // elements 0..7
   p[1] = make_uint2(nib_lo_signed(q[2]), nib_lo_signed(q[3]));   // elements 8..15
   p[2] = make_uint2(nib_hi_signed(q[0]), nib_hi_signed(q[1]));   // elements 16..23
   p[3] = make_uint2(nib_hi_signed(q[2]), nib_hi_signed(q[3]));   // elements 24..31
-  sBd[bb * bn + r] = d;
+  sBd[bb * bn + r] = (uint16_t)d;
 }
 
 __device__ __forceinline__ v4i lds_operand(const int8_t* row, int bb, int h) {
@@ -64,16 +64,17 @@ __device__ __forceinline__ v4i lds_operand(const int8_t* row, int bb, int h) {
   return v;
 }
 
-// Operand of the 32 x 32 x 16 fp16 MFMA that forms the outer product of
-// two scale vectors: element k = 0 of lane l < 32 is the scale of row (or
+// Operand of the 32 x 32 x 8 fp16 MFMA that forms the outer product of two
+// scale vectors: element k = 0 of lane l < 32 is the scale of row (or
 // column) l, every other element zero, so the MFMA's result is
-// d_a[row] * d_w[col] in the layout of the int32 block dots.  The scales
-// are binary16 values (widened to fp32 when staged), so the conversion back
-// and their product are exact.
-__device__ __forceinline__ v8h scale_operand(float d, int h) {
-  v8h v = {};
-  v[0] = h == 0 ? (_Float16)d : (_Float16)0.0f;
-  return v;
+// d_a[row] * d_w[col] in the layout of the int32 block dots.  The scales are
+// staged as their binary16 bits; their product is exact in fp32.  (K = 8
+// takes two registers per operand where K = 16 takes four, at the same
+// issue cost: fewer zero registers to refill per block.)
+__device__ __forceinline__ v4h scale_operand(uint32_t bits, int h) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i v = {h == 0 ? (int)bits : 0, 0};
+  return __builtin_bit_cast(v4h, v);
 }
 
 // kRep: the weights are in the repacked layout (repack.hip): a stage of
@@ -90,8 +91,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
   static_assert(WM >= 1 && WN >= 1, "wave tile must be a multiple of 32x32");
   __shared__ __attribute__((aligned(16))) int8_t sA[BM * PITCH];
   __shared__ __attribute__((aligned(16))) int8_t sB[BN * PITCH];
-  __shared__ __attribute__((aligned(16))) float sAd[KB * BM];
-  __shared__ __attribute__((aligned(16))) float sBd[KB * BN];
+  __shared__ __attribute__((aligned(16))) uint16_t sAd[KB * BM];
+  __shared__ __attribute__((aligned(16))) uint16_t sBd[KB * BN];
 
   const int M = a.M, N = a.N, K = a.K;
   const int nb = K / 32;
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
 #pragma unroll
           for (int bb = 0; bb < KB; ++bb) {
             const uint32_t dw = wreg[u][4 + (bb >> 1)];
-            sBd[bb * BN + r] = (okr && kb + bb < kb1) ? f16_bits_to_f32((bb & 1) ? dw >> 16 : dw) : 0.0f;
+            sBd[bb * BN + r] = (okr && kb + bb < kb1) ? (uint16_t)((bb & 1) ? dw >> 16 : dw) : (uint16_t)0;
           }
         }
       } else if (kPairs) {
@@ -219,8 +220,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
           q0[j] = ok0 ? __builtin_amdgcn_alignbit(wreg[u][j + 1], wreg[u][j], 16) : 0x88888888u;
           q1[j] = ok1 ? wreg[u][5 + j] : 0x88888888u;
         }
-        const float d0 = ok0 ? f16_bits_to_f32(wreg[u][0]) : 0.0f;
-        const float d1 = ok1 ? f16_bits_to_f32(wreg[u][4] >> 16) : 0.0f;
+        const uint32_t d0 = ok0 ? wreg[u][0] & 0xFFFFu : 0u;
+        const uint32_t d1 = ok1 ? wreg[u][4] >> 16 : 0u;
         put_block(sB, sBd, BN, r, 2 * pp, d0, q0);
         put_block(sB, sBd, BN, r, 2 * pp + 1, d1, q1);
       } else {
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
         uint32_t q[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) q[j] = ok ? (wreg[u][1 + 2 * j] | (wreg[u][2 + 2 * j] << 16)) : 0x88888888u;
-        put_block(sB, sBd, BN, r, bb, ok ? f16_bits_to_f32(wreg[u][0]) : 0.0f, q);
+        put_block(sB, sBd, BN, r, bb, ok ? wreg[u][0] & 0xFFFFu : 0u, q);
       }
     }
 #pragma unroll
@@ -248,7 +249,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
       const int i = tid + u * NT;
       if (i >= BM * KB) continue;
       const int r = i % BM, bb = i / BM;
-      sAd[bb * BM + r] = (m0 + r < M && kb + bb < kb1) ? sreg[u] : 0.0f;
+      // the wdata keeps d_a widened to fp32: back to its binary16 bits (exact)
+      sAd[bb * BM + r] = (m0 + r < M && kb + bb < kb1) ? (uint16_t)f32_to_f16_bits(sreg[u]) : (uint16_t)0;
     }
   };
 
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
     const int nblk = (kb1 - kb < KB) ? kb1 - kb : KB;
     for (int bb = 0; bb < nblk; ++bb) {
       v4i A[WM], B[WN];
-      v8h Ad[WM], Bd[WN];
+      v4h Ad[WM], Bd[WN];
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         A[i] = lds_operand(sA + (wm * WTM + 32 * i + l32) * PITCH, bb, h);
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
           const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[i], B[j], zero, 0, 0, 0);
           // d_a[row] * d_w[col] for every output of the tile, in the MFMA
           // result layout (output row of register r: 8*(r/4) + 4*h + (r%4))
-          const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ad[i], Bd[j], v16f{}, 0, 0, 0);
+          const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(Ad[i], Bd[j], v16f{}, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf((float)c[r], sc[r], acc[i][j][r]);
           if (kDump) {
