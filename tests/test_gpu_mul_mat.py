@@ -433,6 +433,37 @@ def test_grouped_products(m):
         assert_close(to_host(out), mul_mat.mul_mat_q4_0_f32_dequant(wq, x), TOL_Q4_0, f"group n={n}")
 
 
+# Groups of one to three matrices: the fused M <= 2 kernel takes their
+# weight pointers and first rows as kernel arguments (row boundaries off the
+# workgroup's row groups, a ragged member, the decode step's q,k,v and
+# gate,up shapes); larger groups read a descriptor (test_grouped_products).
+@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("ns", [[4096, 4096, 4096], [1000, 37, 2048], [11008, 11008], [300]])
+def test_grouped_products_up_to_three(m, ns):
+    import torch
+    qs = _qs()
+    k = 4096
+    rng = np.random.default_rng(90 + m + len(ns) + ns[0])
+    ws, wqs = [], []
+    for n in ns:
+        wq = codec.quantize_q4_0((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+        wqs.append(wq)
+        ws.append(to_dev(wq))
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    say("grouped<=3", m, ns, qs.dispatch(qs.MM_TYPE_Q4_0, m, sum(ns), k))
+    outs = qs.mul_mat_q4_0_f32_group(ws, to_dev(x))
+    for n, wq, w, out in zip(ns, wqs, ws, outs):
+        assert out.shape == (m, n)
+        ref = mul_mat.mul_mat_q4_0_f32_dequant(wq, x)
+        assert_close(to_host(out), ref, TOL_Q4_0, f"group n={n}")
+        # every output of the member equals the matrix computed alone (each
+        # wave reduces one weight row in the same order either way)
+        single = qs.mul_mat_q4_0_f32(w, to_dev(x))
+        same = qs.dispatch(qs.MM_TYPE_Q4_0, m, n, k)[:2] == (qs.dispatch(qs.MM_TYPE_Q4_0, m, sum(ns), k)[0], 1)
+        if same:
+            assert bool(torch.equal(out, single)), f"group n={n} differs from the single call"
+
+
 # ------------------------------------------------------- F16 src1 range
 # Row scales from far below binary16's normal range to far above its largest
 # value, in one batch; an all-zero row among them.  Every F16 path (narrow,
