@@ -12,8 +12,8 @@ What it computes (plain NumPy, float64 unless a step is fixed to fp32):
 * ``codec``   -- Q4_0 and Q8_0 quantize / dequantize / decode, as the exact
   sequence of IEEE fp32 operations the readings below fix, plus the per-block
   integer dot products.
-* ``mul_mat`` -- ``dst[M, N] = src1[M, K] . src0[N, K]^T`` for Q4_0, F16 and
-  F32 ``src0``, in float64.
+* ``mul_mat`` -- ``dst[M, N] = src1[M, K] . src0[N, K]^T`` for Q4_0, Q8_0, F16
+  and F32 ``src0``, in float64.
 
 Sources (page title, section):
 
@@ -47,6 +47,10 @@ R6  Q4_0: ``t = fl32(fl32(x * id) + 8.5)`` then ``floor`` and clamp to
 R7  Q8_0: ``round`` is round-half-away-from-zero applied to ``fl32(x * id)``.
 R8  fp32 -> fp16 is IEEE round-to-nearest-even with subnormals kept.
 R9  ``dst`` is overwritten (not accumulated into).
+R10 Q8_0 weights (src0): the Q8_0 block of R1, quantized from f32 weights
+    by the same routine as src1 (R5, R7, R8); each block dot is the sum of
+    the products of the two signed 8-bit code sets (no offset), scaled by
+    both fp16 scales.
 """
 
 from . import codec, mul_mat  # noqa: F401

@@ -172,3 +172,13 @@ def block_dots(w_q4: np.ndarray, a_q8: np.ndarray, k: int) -> np.ndarray:
     w = q4.astype(np.int64) - 8
     a = q8.astype(np.int64)
     return np.einsum("mbj,nbj->mnb", a, w)
+
+
+def block_dots_q8(w_q8: np.ndarray, a_q8: np.ndarray, k: int) -> np.ndarray:
+    """S[m, n, b] = sum_j q8w[n,b,j] * q8a[m,b,j] in int64, for Q8_0 weights.
+
+    |S| <= 32 * 127 * 127 = 516128, so every value fits int32 (and fp32).
+    """
+    _, qw = decode_q8_0(w_q8, k)
+    _, qa = decode_q8_0(a_q8, k)
+    return np.einsum("mbj,nbj->mnb", qa.astype(np.int64), qw.astype(np.int64))
