@@ -196,6 +196,27 @@ int mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mm_mul_mat_q8_0_f32 -- dst[M][N] (f32) = Q8_0(src1)[M][K] . Q8_0 src0[N][K]^T.
+ * The quantized kind with Q8_0 weights: llama.cpp PR 1632 "mulmat tune"
+ * names Q8_0 among the quantized src0 types it measures (Results section);
+ * its blocks are the Q8_0 blocks above, the same ones the INIT stage writes
+ * for src1 (mm_quantize_q8_0 makes them from f32 weights).
+ *   src0: N rows of K/32 Q8_0 blocks (row pitch 34*K/32 bytes), 4-byte
+ *         aligned.  src1: f32 [M][K], 16-byte aligned.  dst: f32 [M][N],
+ *         4-byte aligned.  K % 32 == 0.
+ *   ws:   mm_mul_mat_workspace_size(MM_TYPE_Q8_0, M, N, K) bytes, 256-byte
+ *         aligned (the Q8_0 copy of src1 and any split-K partial sums).
+ * dst[m][n] = sum_b f32(d_w[n][b]) * f32(d_a[m][b]) * S_b[m][n], with the
+ * int32 block dot S_b = sum_j qw * qa of the two signed code sets (|S_b| <=
+ * 32 * 128 * 128), accumulated in fp32.  M <= 2 with K a multiple of 64:
+ * one kernel that quantizes src1 itself; otherwise INIT, then the tiled
+ * int8 MFMA kernel.
+ */
+int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
+                        int64_t M, int64_t N, int64_t K,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
  * mm_mul_mat_f16_f32 -- dst[M][N] = src1[M][K] . f32(src0[N][K])^T, fp32 accumulation.
  * The F16 x F32 kind of llama.cpp PR 1632 "mulmat tune", Introduction
  * (src0 F16, src1 and dst F32; no INIT stage).
@@ -233,8 +254,8 @@ int mm_mul_mat_f32(const float* src0, const float* src1, float* dst,
                    int64_t M, int64_t N, int64_t K,
                    void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of workspace the product of `type` (F32, F16 or Q4_0) needs at this
- * shape; 0 for an invalid shape or type.  Pure host function. */
+/* Bytes of workspace the product of `type` (F32, F16, Q4_0, Q8_0 or Q4_0R)
+ * needs at this shape; 0 for an invalid shape or type.  Pure host function. */
 size_t mm_mul_mat_workspace_size(int type, int64_t M, int64_t N, int64_t K);
 
 /* Bytes of one row of K values of `type`; -1 if K is invalid for it. */
@@ -261,11 +282,13 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);
 /*
  * mm_debug_mul_mat -- test entry: the same product as mm_mul_mat_<type>,
  * with the kernel forced (variant 0 = as dispatched, 1 = narrow, 2 = wide
- * (Q4_0 and F16 only), 3 = skinny MFMA;
+ * (Q4_0, Q4_0R, Q8_0 and F16), 3 = skinny MFMA (not Q8_0);
  * MM_ERR_ARG for a variant the type does not have)
- * and, for Q4_0, the int32 block dots S_b[m][n][b] of output columns
- * n0 <= n < n1 also written to `dots` ([M][n1-n0][K/32] int32, may be NULL)
- * by the production kernel itself.  Workspace: mm_debug_workspace_size().
+ * and, for Q4_0 and Q4_0R, the int32 block dots S_b[m][n][b] of output
+ * columns n0 <= n < n1 also written to `dots` ([M][n1-n0][K/32] int32, may
+ * be NULL) by the production kernel itself; for Q8_0 by the wide kernel
+ * only (MM_ERR_ARG when the call would take the fused narrow kernel).
+ * Workspace: mm_debug_workspace_size().
  */
 int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst,
                      int32_t* dots, int64_t M, int64_t N, int64_t K,

@@ -22,7 +22,8 @@ import torch
 __all__ = [
     "LIB_PATH", "lib", "MM_TYPE_F32", "MM_TYPE_F16", "MM_TYPE_Q4_0", "MM_TYPE_Q8_0", "MM_TYPE_Q4_0R",
     "repacked_bytes", "repack_q4_0", "unpack_q4_0", "mul_mat_q4_0r_f32",
-    "MMError", "quantize_q4_0", "quantize_q8_0", "mul_mat_q4_0_f32", "mul_mat_f16_f32",
+    "MMError", "quantize_q4_0", "quantize_q8_0", "mul_mat_q4_0_f32", "mul_mat_q8_0_f32",
+    "mul_mat_f16_f32",
     "mul_mat_f32", "workspace_size", "debug_workspace_size", "row_bytes", "dispatch",
     "debug_mul_mat", "status_string", "q4_0_init", "q4_0_compute", "mul_mat_q4_0_f32_group",
     "group_workspace_size",
@@ -46,6 +47,7 @@ for _name, _args, _res in [
     ("mm_mul_mat_q4_0_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     ("mm_mul_mat_q4_0_f32_noalloc", [_vp, _vp, _vp, _i64, _i64, _i64, _vp], _int),
     ("mm_mul_mat_q4_0r_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
+    ("mm_mul_mat_q8_0_f32", [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp], _int),
     ("mm_repack_q4_0", [_vp, _vp, _i64, _i64, _vp], _int),
     ("mm_unpack_q4_0", [_vp, _vp, _i64, _i64, _vp], _int),
     ("mm_repacked_q4_0_bytes", [_i64, _i64], _i64),
@@ -169,6 +171,15 @@ def mul_mat_q4_0_f32(w: torch.Tensor, x: torch.Tensor, out=None, ws=None) -> tor
     if w.shape[1] != row_bytes(MM_TYPE_Q4_0, x.shape[1]):
         raise ValueError("w row bytes do not match K")
     return _mul_mat(lib.mm_mul_mat_q4_0_f32, MM_TYPE_Q4_0, w, x, out, ws, "mm_mul_mat_q4_0_f32")
+
+
+def mul_mat_q8_0_f32(w: torch.Tensor, x: torch.Tensor, out=None, ws=None) -> torch.Tensor:
+    """dst[M, N] = Q8_0(x)[M, K] . Q8_0(w)[N, K]^T; w uint8 [N, K/32*34], x float32 [M, K]."""
+    w = _dev(w, "w", torch.uint8)
+    x = _dev(x, "x", torch.float32)
+    if w.shape[1] != row_bytes(MM_TYPE_Q8_0, x.shape[1]):
+        raise ValueError("w row bytes do not match K")
+    return _mul_mat(lib.mm_mul_mat_q8_0_f32, MM_TYPE_Q8_0, w, x, out, ws, "mm_mul_mat_q8_0_f32")
 
 
 def repacked_bytes(n: int, k: int) -> int:

@@ -240,6 +240,11 @@ int mm_mul_mat_q4_0_f32_noalloc(const void* src0, const float* src1, float* dst,
                  kNoAllocScratchBytes, stream);
 }
 
+int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst, int64_t M, int64_t N,
+                        int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  return mul_mat(MM_TYPE_Q8_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+}
+
 int mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst, int64_t M, int64_t N,
                          int64_t K, void* ws, size_t ws_bytes, void* stream) {
   return mul_mat(MM_TYPE_Q4_0R, src0r, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
@@ -437,7 +442,7 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
     const bool tiled = p.variant == 2;
     out[2] = tiled ? p.bm : p.mt;
     out[3] = tiled ? p.bn : p.variant == 3 ? p.waves : p.kind == KK_Q4_NARROW && p.fuse ? p.fuse_rpw : p.rpw;
-    const bool q4 = p.type == MM_TYPE_Q4_0 || p.type == MM_TYPE_Q4_0R;
+    const bool q4 = p.type == MM_TYPE_Q4_0 || p.type == MM_TYPE_Q4_0R || p.type == MM_TYPE_Q8_0;
     const int init = (q4 && !(p.kind == KK_Q4_NARROW && p.fuse)) ? 1 : 0;
     out[4] = init + 1 + (p.split > 1 ? 1 : 0);
   }
@@ -449,8 +454,16 @@ int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst, 
                      void* ws, size_t ws_bytes, void* stream) {
   if (variant < 0 || variant > 3) return MM_ERR_ARG;
   if (n0 < 0 || n1 < n0 || n1 > N) return MM_ERR_SHAPE;
-  if ((type != MM_TYPE_Q4_0 && type != MM_TYPE_Q4_0R) || n1 == n0) dots = nullptr;
+  if ((type != MM_TYPE_Q4_0 && type != MM_TYPE_Q4_0R && type != MM_TYPE_Q8_0) || n1 == n0)
+    dots = nullptr;
   else if (!dots) return MM_ERR_NULL;
+  if (type == MM_TYPE_Q8_0 && dots) {
+    // Q8_0 weights: only the wide kernel writes block dots
+    Plan p;
+    const int st = make_plan(type, M, N, K, variant, &p);
+    if (st != MM_OK) return st;
+    if (p.kind == KK_Q4_NARROW) return MM_ERR_ARG;
+  }
   return mul_mat(type, src0, src1, dst, dots, M, N, K, n0, n1, variant, ws, ws_bytes, stream);
 }
 

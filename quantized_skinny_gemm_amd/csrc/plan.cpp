@@ -50,12 +50,14 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   *p = Plan();
   p->type = type;
   if (type != MM_TYPE_F32 && type != MM_TYPE_F16 && type != MM_TYPE_Q4_0 &&
-      type != MM_TYPE_Q4_0R)
+      type != MM_TYPE_Q4_0R && type != MM_TYPE_Q8_0)
     return MM_ERR_ARG;
   if (variant < 0 || variant > 3) return MM_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MM_ERR_SHAPE;
-  if ((type == MM_TYPE_Q4_0 || type == MM_TYPE_Q4_0R) && (K % kQK)) return MM_ERR_SHAPE;
+  const bool q8 = type == MM_TYPE_Q8_0;
+  if ((type == MM_TYPE_Q4_0 || type == MM_TYPE_Q4_0R || q8) && (K % kQK)) return MM_ERR_SHAPE;
   if (type == MM_TYPE_Q4_0R && variant == 1) return MM_ERR_ARG;   // no narrow kernel for it
+  if (q8 && variant == 3) return MM_ERR_ARG;                      // no skinny kernel for Q8_0
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
   if (K == 0) { p->kind = KK_ZERO; return MM_OK; }
   if (variant == 0) {
@@ -64,14 +66,19 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     variant = tv;
   }
 
-  if (type == MM_TYPE_Q4_0 || type == MM_TYPE_Q4_0R) {
+  if (type == MM_TYPE_Q4_0 || type == MM_TYPE_Q4_0R || q8) {
     const bool rep = type == MM_TYPE_Q4_0R;
     const int64_t nb = K / kQK;
     // M <= 2: the fused narrow kernel; up to kMmaMaxM: the skinny MFMA
     // kernel; beyond: the tiled wide kernel.  Repacked weights: the skinny
-    // kernel from M = 1.
-    const bool mma = variant == 3 || (variant == 0 && (rep || M > kFuseMaxM) && M <= kMmaMaxM);
-    const bool narrow = !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
+    // kernel from M = 1.  Q8_0 weights: the fused kernel (block pairs, so K
+    // a multiple of 64, and src1 staged whole in LDS) for M <= 2 or when
+    // forced (passes of two src1 rows), the wide kernel otherwise.
+    const bool q8_fusable = q8 && nb % 2 == 0 && 2 * nb * 40 <= kNarrowMaxLds;
+    const bool mma = !q8 && (variant == 3 || (variant == 0 && (rep || M > kFuseMaxM) && M <= kMmaMaxM));
+    const bool narrow = q8 ? q8_fusable && (variant == 1 || (variant == 0 && M <= kFuseMaxM))
+                           : !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
+    if (q8 && variant == 1 && !narrow) return MM_ERR_ARG;
     // wdata: codes, scales, bias; the codes and scales are followed by 256
     // spare bytes (the skinny kernel's last phase may read up to 7 blocks past
     // the end, and drops them)
@@ -196,6 +203,18 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       // M = 2: only the long-K case pays (4096 x 11008: 11.0 -> 9.8 us; one
       // row per wave elsewhere is slower, 4096 x 4096 5.2 -> 5.4)
       if (p->fuse && p->mt == 2 && N <= 8192 && K > 8192) { p->fuse_rpw = 1; p->fuse_waves = 16; }
+      if (q8) {
+        // Q8_0 weights: the fused kernel only, in passes of at most two src1
+        // rows, K whole (every workgroup stages all of src1)
+        p->mt = narrow_mt(M, kFuseMaxM);
+        p->tiles_m = ceil_div(M, p->mt);
+        p->kchunk = units;
+        p->split = 1;
+        p->fuse = true;
+        p->fuse_rpw = p->mt == 1 ? 1 : 2;
+        p->fuse_waves = K > 8192 ? 16 : 8;
+        if (p->mt == 2 && K > 8192) p->fuse_rpw = 1;
+      }
       {
         const int64_t groups = ceil_div(N, (int64_t)p->fuse_rpw * p->fuse_waves);
         p->fuse_grid = groups < kNarrowMaxGrid ? groups : kNarrowMaxGrid;
@@ -221,6 +240,9 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       else if (M <= 64) { p->bm = 64; p->bn = 64; p->waves_m = 2; p->waves_n = 2; }
       else if (M <= 128 && many_rows) { p->bm = 64; p->bn = 128; p->waves_m = 2; p->waves_n = 2; }
       else { p->bm = 128; p->bn = 128; p->waves_m = 2; p->waves_n = 2; }
+      // Q8_0 weights stage twice the bytes per pair: the 128 x 128 tile
+      // would hold more than 256 VGPRs (one wave per SIMD); 128 x 64 keeps two
+      if (q8 && p->bm == 128 && p->bn == 128) p->bn = 64;
       p->tiles_m = ceil_div(M, p->bm);
       p->tiles_n = ceil_div(N, p->bn);
       const int64_t tiles = p->tiles_m * p->tiles_n;
@@ -345,6 +367,8 @@ int validate_mul_mat(int type, const void* src0, const void* src1, const void* d
   if (d % 4) return MM_ERR_ALIGN;
   if (type == MM_TYPE_Q4_0) {
     if (s0 % 2 || s1 % 16) return MM_ERR_ALIGN;
+  } else if (type == MM_TYPE_Q8_0) {
+    if (s0 % 4 || s1 % 16) return MM_ERR_ALIGN;
   } else if (type == MM_TYPE_Q4_0R) {
     if (s0 % 16 || s1 % 16) return MM_ERR_ALIGN;
   } else if (type == MM_TYPE_F16) {

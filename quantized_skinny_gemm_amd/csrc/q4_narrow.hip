@@ -31,6 +31,7 @@
 //     and add the partial sums afterwards).
 #include "device.h"
 #include "kernels.h"
+#include "../../include/mm.h"
 
 namespace qsg {
 
@@ -150,6 +151,61 @@ __device__ __forceinline__ void unit_mac(const uint32_t (&wv)[R][9], int64_t u, 
       for (int j = 0; j < 4; ++j) q[r][j] = wv[r][1 + 2 * j] | (wv[r][2 + 2 * j] << 16);
     }
     block_mac<MT, R, kDump, kMask>(q, dw, (int)u, valid, av, acc, nw, m0, nb, a);
+  }
+}
+
+// Q8_0 weights (the fused kernel only): a K unit is a pair of 34-byte
+// blocks, 68 bytes, 4-byte aligned when K/32 is even; block 0's scale is
+// bytes 0-1 and its codes start at byte 2 (dwords shifted by 16 bits),
+// block 1's scale is the high half of dword 8 and its codes are dwords 9-16.
+// The codes are signed bytes, so each block dot is 8 v_dot4 from zero.
+template <int R>
+__device__ __forceinline__ void load_unit8(uint32_t (&wv)[R][17], const uint8_t* const (&rowp)[R],
+                                           int64_t u) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const __attribute__((address_space(1))) uint32_t* p =
+        (const __attribute__((address_space(1))) uint32_t*)(rowp[r] + 68 * u);
+#pragma unroll
+    for (int i = 0; i < 17; ++i) wv[r][i] = p[i];
+  }
+}
+
+template <int MT, int R>
+__device__ __forceinline__ void unit_mac8(const uint32_t (&wv)[R][17], int64_t u,
+                                          const ActView& av, float (&acc)[R][MT]) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint32_t q[R][8];
+    float dw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      dw[r] = f16_bits_to_f32(half == 0 ? wv[r][0] : wv[r][8] >> 16);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        q[r][j] = half == 0 ? __builtin_amdgcn_alignbit(wv[r][j + 1], wv[r][j], 16) : wv[r][9 + j];
+    }
+    const int bl = (int)(2 * u + half) - av.boff;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int mm = m < av.rows ? m : av.rows - 1;
+      const v4i* ap = reinterpret_cast<const v4i*>(av.q + mm * av.qpitch + (int64_t)bl * 32);
+      const v4i a0 = ap[0], a1 = ap[1];
+      const float da = av.d[mm * av.dpitch + bl];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        int s = 0;
+        s = __builtin_amdgcn_sdot4((int)q[r][0], a0.x, s, false);
+        s = __builtin_amdgcn_sdot4((int)q[r][1], a0.y, s, false);
+        s = __builtin_amdgcn_sdot4((int)q[r][2], a0.z, s, false);
+        s = __builtin_amdgcn_sdot4((int)q[r][3], a0.w, s, false);
+        s = __builtin_amdgcn_sdot4((int)q[r][4], a1.x, s, false);
+        s = __builtin_amdgcn_sdot4((int)q[r][5], a1.y, s, false);
+        s = __builtin_amdgcn_sdot4((int)q[r][6], a1.z, s, false);
+        s = __builtin_amdgcn_sdot4((int)q[r][7], a1.w, s, false);
+        acc[r][m] = fmaf((float)s, dw[r] * da, acc[r][m]);
+      }
+    }
   }
 }
 
@@ -526,7 +582,7 @@ __device__ __forceinline__ int fused_mat(const FusedOut& fo, int n) {
   return i;
 }
 
-template <int MT, int NR, int R, int WAVES, bool kMany>
+template <int MT, int NR, int R, int WAVES, bool kMany, bool kQ8>
 __global__ __launch_bounds__(64 * WAVES)
 void k_q4_fused(const float* __restrict__ x, const uint8_t* w0, const uint8_t* w1,
                 const uint8_t* w2, int N, int K, int r1, int r2, int M, int G, FusedOut fo) {
@@ -536,7 +592,8 @@ void k_q4_fused(const float* __restrict__ x, const uint8_t* w0, const uint8_t* w
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nb = K / 32;
   const int units = nb / 2;
-  const int64_t rb = (int64_t)nb * 18;
+  const int64_t rb = (int64_t)nb * (kQ8 ? 34 : 18);
+  constexpr int UW = kQ8 ? 17 : 9;                   // dwords per K unit (block pair)
   const int SU = (units + 63) / 64;                  // steps per row group
   const int m0 = blockIdx.y * MT;
   const int rows = M - m0 < MT ? M - m0 : MT;
@@ -575,13 +632,14 @@ void k_q4_fused(const float* __restrict__ x, const uint8_t* w0, const uint8_t* w
   bool ok[NR];
   quant_load<NT, NR, MT>(sl, x, 0, rounds, v, ok);
   int g = blockIdx.x, i = 0;                         // current step: group g, K step i
-  uint32_t wv[R][9];
+  uint32_t wv[R][UW];
   {
     const uint8_t* rp[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) rp[r] = rowptr(g, r);
     const int u = lane < units ? lane : 0;
-    load_unit<R, true>(wv, rp, u);
+    if constexpr (kQ8) load_unit8<R>(wv, rp, u);
+    else load_unit<R, true>(wv, rp, u);
   }
   // the first weights are in flight before src1 is waited for
   __builtin_amdgcn_sched_barrier(0);
@@ -607,22 +665,26 @@ void k_q4_fused(const float* __restrict__ x, const uint8_t* w0, const uint8_t* w
     int in = i + 1, gn = g;
     if (in == SU) { in = 0; gn = g + G; }
     if (s + 1 == S) { in = i; gn = g; }
-    uint32_t cur[R][9];
+    uint32_t cur[R][UW];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int j = 0; j < 9; ++j) cur[r][j] = wv[r][j];
+      for (int j = 0; j < UW; ++j) cur[r][j] = wv[r][j];
     {
       const uint8_t* rp[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) rp[r] = rowptr(gn, r);
       int un = lane + 64 * in;
       un = un < units ? un : 0;
-      load_unit<R, true>(wv, rp, un);
+      if constexpr (kQ8) load_unit8<R>(wv, rp, un);
+      else load_unit<R, true>(wv, rp, un);
     }
     const int u = lane + 64 * i;
     const int nw = g * RPG + wave * R;
-    if (u < units) unit_mac<MT, R, true, false, false>(cur, u, true, av, acc, nw, m0, nb, Q4Args{});
+    if (u < units) {
+      if constexpr (kQ8) unit_mac8<MT, R>(cur, u, av, acc);
+      else unit_mac<MT, R, true, false, false>(cur, u, true, av, acc, nw, m0, nb, Q4Args{});
+    }
     if (i == SU - 1) {
       float mine = 0.0f;
 #pragma unroll
@@ -728,6 +790,10 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
   // (in units) doubles and the split count is unchanged.
   Plan q = p;
   if (!pairs && nb % 2 == 0) q.kchunk = p.kchunk * 2;
+  // Q8_0 weights have the fused kernel only (the plan and the validation
+  // guarantee its conditions; a dump of block dots takes the wide kernel)
+  if (p.type == MM_TYPE_Q8_0 && !(x && pairs && p.split == 1 && a.dots == nullptr && p.fuse))
+    return hipErrorInvalidValue;
   if (x && pairs && p.split == 1 && a.dots == nullptr && p.fuse) {
     const dim3 grid((unsigned)p.fuse_grid, (unsigned)p.tiles_m, 1u);
     const size_t lds = (size_t)p.mt * nb * 40;
@@ -746,14 +812,20 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
     const int r1 = mats.count > 1 ? mats.row0[1] : a.N;
     const int r2 = mats.count > 2 ? mats.row0[2] : a.N;
     const int G = p.fuse_grid;
-#define QSG_FUSED_GO(MT_, NR_, R_, W_)                                                             \
+    const bool q8 = p.type == MM_TYPE_Q8_0;
+#define QSG_FUSED_K(MT_, NR_, R_, W_, MANY_)                                                       \
     do {                                                                                           \
-      if (many)                                                                                    \
-        hipLaunchKernelGGL((k_q4_fused<MT_, NR_, R_, W_, true>), grid, dim3(nt), lds, s, x,        \
+      if (q8)                                                                                      \
+        hipLaunchKernelGGL((k_q4_fused<MT_, NR_, R_, W_, MANY_, true>), grid, dim3(nt), lds, s, x, \
                            mats.w[0], w1, w2, a.N, a.K, r1, r2, a.M, G, fo);                       \
       else                                                                                         \
-        hipLaunchKernelGGL((k_q4_fused<MT_, NR_, R_, W_, false>), grid, dim3(nt), lds, s, x,       \
-                           mats.w[0], w1, w2, a.N, a.K, r1, r2, a.M, G, fo);                       \
+        hipLaunchKernelGGL((k_q4_fused<MT_, NR_, R_, W_, MANY_, false>), grid, dim3(nt), lds, s,   \
+                           x, mats.w[0], w1, w2, a.N, a.K, r1, r2, a.M, G, fo);                    \
+    } while (0)
+#define QSG_FUSED_GO(MT_, NR_, R_, W_)                                                             \
+    do {                                                                                           \
+      if (many) QSG_FUSED_K(MT_, NR_, R_, W_, true);                                               \
+      else QSG_FUSED_K(MT_, NR_, R_, W_, false);                                                   \
     } while (0)
 #define QSG_FUSED(MT_, R_, W_)                                                                     \
     if (p.mt == MT_ && p.fuse_rpw == R_ && p.fuse_waves == W_) {                                   \
@@ -768,6 +840,7 @@ hipError_t launch_q4_narrow(const Plan& p, const Q4Args& a, const Q4Mats& mats, 
     QSG_FUSED(2, 1, 16)
 #undef QSG_FUSED
 #undef QSG_FUSED_GO
+#undef QSG_FUSED_K
     return hipErrorInvalidValue;
   }
   // rows per wave and waves per workgroup must match make_plan()

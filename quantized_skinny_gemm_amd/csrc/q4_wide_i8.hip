@@ -53,6 +53,15 @@ __device__ __forceinline__ void put_block(int8_t* sB, uint16_t* sBd, int bn, int
   sBd[bb * bn + r] = (uint16_t)d;
 }
 
+// Writes one Q8_0 block (binary16 scale bits + its 32 int8 codes as stored).
+__device__ __forceinline__ void put_block8(int8_t* sB, uint16_t* sBd, int bn, int r, int bb,
+                                           uint32_t d, const uint32_t (&q)[8]) {
+  uint2* p = reinterpret_cast<uint2*>(sB + r * PITCH + bb * 32);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = make_uint2(q[2 * j], q[2 * j + 1]);
+  sBd[bb * bn + r] = (uint16_t)d;
+}
+
 __device__ __forceinline__ v4i lds_operand(const int8_t* row, int bb, int h) {
   // lane half h supplies elements 8h..8h+7 and 16+8h..16+8h+7 of the block;
   // the A and B operands use the same assignment, so the MFMA's k-sum runs
@@ -81,7 +90,8 @@ __device__ __forceinline__ v4h scale_operand(uint32_t bits, int h) {
 // KB = 4 blocks is half a phase of each 16-row tile, 1 KB of codes (each
 // lane piece: code bytes 4 g .. 4 g + 3 of one row for the 4 blocks) and the
 // rows' scales, staged with one 16-byte load per piece.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool kPairs, bool kDump, bool kRep = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool kPairs, bool kDump, bool kRep = false,
+          bool kQ8 = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, int tiles_m,
                                                                    int tiles_n, int kchunk,
                                                                    int split) {
@@ -96,7 +106,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
 
   const int M = a.M, N = a.N, K = a.K;
   const int nb = K / 32;
-  const int64_t rb = (int64_t)nb * 18;
+  const int64_t rb = (int64_t)nb * (kQ8 ? 34 : 18);
   const int tiles = tiles_m * tiles_n;
   const int t = xcd_remap(blockIdx.x, tiles * split);
   const int z = t / tiles;
@@ -128,7 +138,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
                    : kPairs ? (BN * (KB / 2) + NT - 1) / NT : (BN * KB + NT - 1) / NT;
   constexpr int AI = (BM * KB * 2 + NT - 1) / NT;
   constexpr int SI = (BM * KB + NT - 1) / NT;
-  uint32_t wreg[WI][kRep ? 6 : 9];
+  uint32_t wreg[WI][kQ8 ? 17 : kRep ? 6 : 9];
   const int rtiles = (N + 15) / 16, rphases = (nb + 7) / 8;
   v4i areg[AI];
   float sreg[SI];
@@ -151,21 +161,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
         wreg[u][2] = (uint32_t)q.z; wreg[u][3] = (uint32_t)q.w;
         wreg[u][4] = (uint32_t)d.x; wreg[u][5] = (uint32_t)d.y;
       } else if (kPairs) {
+        // a block pair: 36 bytes (Q4_0) or 68 (Q8_0), 4-byte aligned
+        constexpr int UW = kQ8 ? 17 : 9;
         const int r = (i / (KB / 2)) % BN, pp = i % (KB / 2);
         const int n = n0 + r < N ? n0 + r : N - 1;
         const int b = kb + 2 * pp < kb1 ? kb + 2 * pp : kb0;
         const __attribute__((address_space(1))) uint32_t* p =
-            (const __attribute__((address_space(1))) uint32_t*)(a.w + (int64_t)n * rb + (int64_t)b * 18);
+            (const __attribute__((address_space(1))) uint32_t*)(a.w + (int64_t)n * rb + (int64_t)b * (kQ8 ? 34 : 18));
 #pragma unroll
-        for (int j = 0; j < 9; ++j) wreg[u][j] = p[j];
+        for (int j = 0; j < UW; ++j) wreg[u][j] = p[j];
       } else {
+        // one block as 16-bit words: 18 bytes (Q4_0) or 34 (Q8_0)
+        constexpr int UH = kQ8 ? 17 : 9;
         const int r = (i / KB) % BN, bb = i % KB;
         const int n = n0 + r < N ? n0 + r : N - 1;
         const int b = kb + bb < kb1 ? kb + bb : kb0;
         const __attribute__((address_space(1))) uint16_t* p =
-            (const __attribute__((address_space(1))) uint16_t*)(a.w + (int64_t)n * rb + (int64_t)b * 18);
+            (const __attribute__((address_space(1))) uint16_t*)(a.w + (int64_t)n * rb + (int64_t)b * (kQ8 ? 34 : 18));
 #pragma unroll
-        for (int j = 0; j < 9; ++j) wreg[u][j] = p[j];
+        for (int j = 0; j < UH; ++j) wreg[u][j] = p[j];
       }
     }
 #pragma unroll
@@ -209,6 +223,31 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_q4_wide(Q4Args a, in
             sBd[bb * BN + r] = (okr && kb + bb < kb1) ? (uint16_t)((bb & 1) ? dw >> 16 : dw) : (uint16_t)0;
           }
         }
+      } else if (kPairs && kQ8) {
+        // Q8_0 pair: block 0 = bytes 0-33 (scale, then codes from byte 2:
+        // dwords shifted by 16 bits), block 1 = bytes 34-67 (scale in the high
+        // half of dword 8, codes dword aligned from dword 9); codes are the
+        // int8 operands as stored (0 outside the tile or the K range)
+        if (i >= BN * (KB / 2)) continue;
+        const int r = i / (KB / 2), pp = i % (KB / 2);
+        const int b = kb + 2 * pp;
+        const bool ok0 = n0 + r < N && b < kb1, ok1 = ok0 && b + 1 < kb1;
+        uint32_t q0[8], q1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          q0[j] = ok0 ? __builtin_amdgcn_alignbit(wreg[u][j + 1], wreg[u][j], 16) : 0u;
+          q1[j] = ok1 ? wreg[u][9 + j] : 0u;
+        }
+        put_block8(sB, sBd, BN, r, 2 * pp, ok0 ? wreg[u][0] & 0xFFFFu : 0u, q0);
+        put_block8(sB, sBd, BN, r, 2 * pp + 1, ok1 ? wreg[u][8] >> 16 : 0u, q1);
+      } else if (kQ8) {
+        if (i >= BN * KB) continue;
+        const int r = i / KB, bb = i % KB;
+        const bool ok = n0 + r < N && kb + bb < kb1;
+        uint32_t q[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[j] = ok ? (wreg[u][1 + 2 * j] | (wreg[u][2 + 2 * j] << 16)) : 0u;
+        put_block8(sB, sBd, BN, r, bb, ok ? wreg[u][0] : 0u, q);
       } else if (kPairs) {
         if (i >= BN * (KB / 2)) continue;
         const int r = i / (KB / 2), pp = i % (KB / 2);
@@ -324,6 +363,14 @@ hipError_t launch_cfg(const Plan& p, const Q4Args& a, bool pairs, hipStream_t s)
   if (p.type == MM_TYPE_Q4_0R) {
     if (dump) hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, false, true, true>), grid, block, 0, s, a, tm, tn, kc, sp);
     else hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, false, false, true>), grid, block, 0, s, a, tm, tn, kc, sp);
+  } else if (p.type == MM_TYPE_Q8_0) {
+    if (pairs) {
+      if (dump) hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, true, true, false, true>), grid, block, 0, s, a, tm, tn, kc, sp);
+      else hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, true, false, false, true>), grid, block, 0, s, a, tm, tn, kc, sp);
+    } else {
+      if (dump) hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, false, true, false, true>), grid, block, 0, s, a, tm, tn, kc, sp);
+      else hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, false, false, false, true>), grid, block, 0, s, a, tm, tn, kc, sp);
+    }
   } else if (pairs) {
     if (dump) hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, true, true>), grid, block, 0, s, a, tm, tn, kc, sp);
     else hipLaunchKernelGGL((k_q4_wide<BM, BN, WMS, WNS, true, false>), grid, block, 0, s, a, tm, tn, kc, sp);

@@ -304,3 +304,28 @@ def test_repack_host_checks():
     st = qs.lib.mm_mul_mat_q4_0r_f32(FAKE + 8, FAKE + 2**30, FAKE + 2**31, 4, 256, 512,
                                      FAKE + 2**32, need, None)
     assert st == ALIGN
+
+
+def test_q8_0_weights_host_rules():
+    """Q8_0 weights: the fused kernel at M <= 2 when K/32 is even (one launch,
+    no workspace use), the wide kernel otherwise (INIT, product and maybe a
+    reduce); no skinny variant; 4-byte alignment of src0; K % 32."""
+    d = (ctypes.c_int * 5)()
+    assert qs.lib.mm_dispatch(Q8, 1, 4096, 4096, d) == OK and d[0] == 1 and d[4] == 1
+    assert qs.lib.mm_dispatch(Q8, 2, 11008, 4096, d) == OK and d[0] == 1 and d[2] == 2 and d[4] == 1
+    assert qs.lib.mm_dispatch(Q8, 1, 100, 96, d) == OK and d[0] == 2           # K/32 odd
+    assert qs.lib.mm_dispatch(Q8, 3, 4096, 4096, d) == OK and d[0] == 2 and d[4] >= 2
+    assert qs.lib.mm_dispatch(Q8, 512, 14336, 4096, d) == OK and d[0] == 2 and (d[2], d[3]) == (128, 64)
+    assert qs.lib.mm_dispatch(Q8, 1, 64, 48, d) == SHAPE
+    assert qs.lib.mm_debug_workspace_size(Q8, 4, 64, 64, 3) == 0                 # no skinny kernel
+    assert qs.lib.mm_debug_mul_mat(Q8, FAKE, FAKE, FAKE, None, 4, 64, 64, 0, 0, 3, None, 0, None) == ARG
+    assert qs.lib.mm_debug_mul_mat(Q8, FAKE, FAKE, FAKE, None, 4, 64, 96, 0, 0, 1, None, 0, None) == ARG
+    ws = qs.workspace_size(Q8, 8, 256, 512)
+    assert ws > 0
+    call = qs.lib.mm_mul_mat_q8_0_f32
+    assert call(FAKE + 2, FAKE + 2**30, FAKE + 2**31, 8, 256, 512, FAKE + 2**32, ws, None) == ALIGN
+    assert call(FAKE, FAKE + 2**30 + 4, FAKE + 2**31, 8, 256, 512, FAKE + 2**32, ws, None) == ALIGN
+    assert call(FAKE, FAKE + 2**30, FAKE + 2**31, 8, 256, 512, FAKE + 2**32, ws - 1, None) == WS
+    assert call(FAKE, FAKE + 2**30, FAKE + 2**31, 8, 256, 48, FAKE + 2**32, ws, None) == SHAPE
+    assert call(None, FAKE + 2**30, FAKE + 2**31, 8, 256, 512, FAKE + 2**32, ws, None) == NULL
+    assert qs.row_bytes(Q8, 4096) == 4096 // 32 * 34
