@@ -501,12 +501,16 @@ def cpu_baseline(budget_s: float = 8.0, max_workers: int = 16):
 BENCH_READ_LIB = os.path.join(ROOT, "bench_read.so")
 
 
-def read_ceiling(st, reps: int, s, grid: int = 1024):
+READ_GRIDS = (768, 1024, 1536, 2048, 3072, 4096)
+
+
+def read_ceiling(st, reps: int, s, grids=READ_GRIDS):
     """A plain streaming read (bench_read.so, not the library) of the same
     weight buffers in the same launch pattern as the grouped step: per layer
     q,k,v in one launch, o, gate,up in one, down; 128 launches per step as one
-    HIP graph.  Returns the whole-step GB/s (weight bytes only) and the
-    average us per launch of each kind."""
+    HIP graph, at each grid size in `grids`.  Returns the best whole-step GB/s
+    (weight bytes only) with its grid, the average us per launch of each kind
+    at that grid, and the step time at every grid."""
     import ctypes
     torch = st["torch"]
     if not os.path.exists(BENCH_READ_LIB):
@@ -516,27 +520,33 @@ def read_ceiling(st, reps: int, s, grid: int = 1024):
                                          ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
                                          ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     rl.qsg_bench_stream_read.restype = ctypes.c_int
-    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(max(grids), dtype=torch.int32, device="cuda")
     keep = []
-    kinds = {}
-    step = []
-    for row in st["weights"]:
-        for kind, slots in (("qkv", [0, 1, 2]), ("o", [3]), ("gate_up", [4, 5]), ("down", [6])):
-            ptrs = (ctypes.c_void_p * len(slots))(*[row[sl].data_ptr() for sl in slots])
-            nb = (ctypes.c_int64 * len(slots))(*[row[sl].numel() for sl in slots])
-            keep.append((ptrs, nb))
-            c = (kind, rl.qsg_bench_stream_read,
-                 (ptrs, nb, len(slots), sink.data_ptr(), grid, s.cuda_stream),
-                 float(sum(row[sl].numel() for sl in slots)))
-            step.append(c)
-            kinds.setdefault(kind, []).append(c)
-    ms = time_graph(torch, s, step, reps)
-    total = sum(c[3] for c in step)
+    by_grid = {}
+    best = None
+    for grid in grids:
+        kinds = {}
+        step = []
+        for row in st["weights"]:
+            for kind, slots in (("qkv", [0, 1, 2]), ("o", [3]), ("gate_up", [4, 5]), ("down", [6])):
+                ptrs = (ctypes.c_void_p * len(slots))(*[row[sl].data_ptr() for sl in slots])
+                nb = (ctypes.c_int64 * len(slots))(*[row[sl].numel() for sl in slots])
+                keep.append((ptrs, nb))
+                c = (kind, rl.qsg_bench_stream_read,
+                     (ptrs, nb, len(slots), sink.data_ptr(), grid, s.cuda_stream),
+                     float(sum(row[sl].numel() for sl in slots)))
+                step.append(c)
+                kinds.setdefault(kind, []).append(c)
+        ms = time_graph(torch, s, step, reps)
+        by_grid[grid] = round(ms, 5)
+        if best is None or ms < best[1]:
+            best = (grid, ms, kinds, sum(c[3] for c in step))
+    grid, ms, kinds, total = best
     per = {k: round(time_graph(torch, s, v, reps) * 1e3 / len(v), 4) for k, v in kinds.items()}
     return {"GBs": round(total / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 5),
-            "per_kind_us": per, "grid": grid,
+            "per_kind_us": per, "grid": grid, "ms_per_step_by_grid": by_grid,
             "what": "plain 16-byte streaming read of the step's weight buffers, same 128-launch "
-                    "graph (bench_read.hip)"}
+                    "graph (bench_read.hip), best grid of those tried"}
 
 
 # ------------------------------------------------------------------ main

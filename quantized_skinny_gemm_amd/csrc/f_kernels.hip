@@ -5,19 +5,21 @@
 // and widened to fp32 in registers; src1 stays fp32; fp32 FMA accumulation;
 // 64-lane butterfly reduction.  At M = 1 a wave owns one weight row and
 // issues the loads of several 16-byte chunks per lane before their FMAs
-// (four rows per wave for F16 beyond 8192 rows).  Rows of src1 beyond 16
-// are handled by further passes (grid.y).
+// (four rows per wave for F16 beyond 8192 rows).  With few rows the waves of
+// a workgroup split K over the same rows and add their partial sums in LDS
+// in slice order.  Rows of src1 beyond 16 are handled by further passes
+// (grid.y).
 //
 // Skinny MFMA kernel (F16 at 2 <= M <= 16 and, with at most 8192 weight
 // rows, up to 64; F32 from M = 2; operands 16-byte aligned): one workgroup
 // per 16 weight rows and pass of 16 src1 rows, its waves splitting K and
 // adding their partial tiles in LDS at the end, so one launch does the whole
-// product.  The weights are the MFMA's A operand as stored (16-byte loads, no
-// conversion); src1 is the B operand, loaded straight into registers.  F16
-// uses v_mfma_f32_16x16x32_f16 with src1 split into two binary16 terms
-// hi + lo after a power-of-two scale per row and sub-slice (about 22
-// significant bits at any fp32 magnitude; each f16 x f16 product is exact in
-// fp32), F32 uses v_mfma_f32_16x16x4_f32 on the values as they are.
+// product.  The products run on v_mfma_f32_16x16x4_f32: F16 weights are
+// widened to fp32 in registers (exact) and src1 is used as given, so every
+// product is an exact fp32 product and no magnitude of src1 is lost to a
+// narrower format.  (Rounding src1 to binary16 for the fp16 matrix
+// instruction saves about 5% of a call at M = 2-8 and nothing at 16-32:
+// this kernel is not bound by its matrix instructions.)
 //
 // Wide f16 kernel (M beyond that): a dense contraction on
 // v_mfma_f32_32x32x16_f16; src1 is rounded to binary16 once per call after a
@@ -61,13 +63,21 @@ struct WLoad<float> {
   static __device__ __forceinline__ float load1(const float* p) { return *p; }
 };
 
-template <typename WT, int MT, int R, bool kVec>
+// Narrow kernel: 4 waves per workgroup, R weight rows and MT src1 rows per
+// wave, each lane 8 values of K per load.  With KS > 1 the waves form 4 / KS
+// row groups of KS waves that split K into contiguous slices over the same
+// rows (more waves in flight when the rows alone give too few) and add their
+// partial results in LDS in slice order.
+template <typename WT, int MT, int R, bool kVec, int KS>
 __global__ __launch_bounds__(256) void k_f_narrow(const WT* __restrict__ w,
                                                   const float* __restrict__ x,
                                                   float* __restrict__ dst, int M, int N, int K) {
+  static_assert(KS == 1 || KS == 2 || KS == 4, "K slices per row group");
+  constexpr int GPW = 4 / KS;                        // row groups per workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave / KS, ks = wave % KS;
   const int m0 = blockIdx.y * MT;
-  const int nw = (blockIdx.x * 4 + wave) * R;
+  const int nw = (blockIdx.x * GPW + grp) * R;
   const WT* rowp[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rowp[r] = w + (int64_t)((nw + r < N) ? nw + r : N - 1) * K;
@@ -86,8 +96,12 @@ __global__ __launch_bounds__(256) void k_f_narrow(const WT* __restrict__ w,
     // FMAs: one row per wave keeps few bytes in flight per step otherwise
     constexpr int U = R == 1 ? (sizeof(WT) == 2 ? 4 : 2) : 1;
     const int nchunks = K / 8;
-    int c = lane;
-    for (; c + 64 * (U - 1) < nchunks; c += 64 * U) {
+    // this wave's chunks [cs, ce): slices of whole 64-chunk rounds
+    const int per = ((nchunks + 64 * KS - 1) / (64 * KS)) * 64;
+    const int cs = ks * per < nchunks ? ks * per : nchunks;
+    const int ce = cs + per < nchunks ? cs + per : nchunks;
+    int c = cs + lane;
+    for (; c + 64 * (U - 1) < ce; c += 64 * U) {
       float wv[U][R][8];
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -106,7 +120,7 @@ __global__ __launch_bounds__(256) void k_f_narrow(const WT* __restrict__ w,
             for (int e = 0; e < 8; ++e) acc[r][m] = fmaf(wv[u][r][e], xv[e], acc[r][m]);
         }
     }
-    for (; c < nchunks; c += 64) {
+    for (; c < ce; c += 64) {
       float wv[R][8];
 #pragma unroll
       for (int r = 0; r < R; ++r) WLoad<WT>::load8(rowp[r] + 8 * c, wv[r]);
@@ -123,7 +137,8 @@ __global__ __launch_bounds__(256) void k_f_narrow(const WT* __restrict__ w,
     }
     kdone = nchunks * 8;
   }
-  for (int k = kdone + lane; k < K; k += 64) {
+  // the values past the last whole chunk (all of K without kVec): slice 0
+  for (int k = kdone + lane; ks == 0 && k < K; k += 64) {
     float wv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) wv[r] = WLoad<WT>::load1(rowp[r] + k);
@@ -143,6 +158,15 @@ __global__ __launch_bounds__(256) void k_f_narrow(const WT* __restrict__ w,
       const float v = wave_sum(acc[r][m]);
       if (lane == r * MT + m) mine = v;
     }
+  if constexpr (KS > 1) {
+    __shared__ float part[4][R * MT];
+    if (ks > 0 && lane < R * MT) part[wave][lane] = mine;
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int j = 1; j < KS; ++j)
+      if (lane < R * MT) mine += part[wave + j][lane];
+  }
   const int r = lane / MT, m = lane % MT;
   if (lane < R * MT && m0 + m < M && nw + r < N) dst[(int64_t)(m0 + m) * N + nw + r] = mine;
 }
@@ -150,9 +174,21 @@ __global__ __launch_bounds__(256) void k_f_narrow(const WT* __restrict__ w,
 template <typename WT, int MT, int R>
 hipError_t launch_f_mt(const Plan& p, const WT* w, const float* x, float* dst, int M, int N,
                        int K, bool vec, hipStream_t s) {
-  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m);
-  if (vec) hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
-  else hipLaunchKernelGGL((k_f_narrow<WT, MT, R, false>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
+  // K slices only on the vector path (the scalar path is one wave's)
+  const int ks = vec ? p.kslices : 1;
+  const int64_t rows_per_wg = (int64_t)(4 / ks) * R;
+  const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)p.tiles_m);
+  if (!vec) {
+    hipLaunchKernelGGL((k_f_narrow<WT, MT, R, false, 1>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
+  } else if (ks == 4) {
+    hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true, 4>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
+  } else if (ks == 2) {
+    hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true, 2>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
+  } else if (ks == 1) {
+    hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true, 1>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -65,6 +65,7 @@ struct Plan {
   bool fuse = false;        // narrow Q4_0: quantize src1 inside the product kernel
   int fuse_rpw = 2, fuse_waves = 8;  // fused kernel: rows per wave and waves per workgroup
   int64_t fuse_grid = 0;    // fused kernel: workgroups along N
+  int kslices = 1;          // narrow F kernel: waves of a workgroup splitting K over the same rows
   int64_t kchunk = 0;       // K per split (Q4 narrow: units; Q4 wide / skinny: blocks;
                             // skinny F: MFMA steps per wave)
   // workspace layout (bytes)

@@ -533,3 +533,22 @@ def test_f16_m2_aligned(n):
     assert_close(y, mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 M=2 N={n}")
     y1, _ = qs.debug_mul_mat(qs.MM_TYPE_F16, to_dev(wh), to_dev(x), 1)
     assert_close(to_host(y1), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 M=2 N={n} narrow")
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("n,k", [(100, 4096), (300, 2056), (1000, 1032), (8191, 4096), (100, 1001)])
+def test_f_narrow_k_slices(m, n, k):
+    """The narrow F16 / F32 kernel (variant 1) with its waves splitting K
+    over the same rows: two or four slices, uneven and empty last slices
+    (K / 8 = 257, 129), clamped rows past N, and K % 8 != 0 (one slice, the
+    scalar path) against the oracle."""
+    qs = _qs()
+    rng = np.random.default_rng(m * 104729 + n * 13 + k)
+    w = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    wh = w.astype(np.float16)
+    say("f narrow k slices", m, n, k)
+    y, _ = qs.debug_mul_mat(qs.MM_TYPE_F16, to_dev(wh), to_dev(x), 1)
+    assert_close(to_host(y), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 narrow {m}x{n}x{k}")
+    y, _ = qs.debug_mul_mat(qs.MM_TYPE_F32, to_dev(w), to_dev(x), 1)
+    assert_close(to_host(y), mul_mat.mul_mat_f32(w, x), TOL_F, f"f32 narrow {m}x{n}x{k}")
