@@ -110,6 +110,9 @@ Q4Mats single_mat(const void* src0, float* dst, int64_t N) {
 
 // The product kernel (x != NULL: INIT fused), then the split-K reduction.
 int q4_product(const Plan& p, const Q4Args& a, const float* x, hipStream_t s) {
+  // Q8_0 weights have no staged-chunk fallback for the skinny plan
+  if (p.type == MM_TYPE_Q8_0 && p.kind == KK_Q4_MMA && !(a.sq && q4_skinny_ok(a.K, a.w)))
+    return MM_ERR_ARG;
   hipError_t e = p.kind == KK_Q4_NARROW    ? launch_q4_narrow(p, a, single_mat(a.w, a.dst, a.N), x, s)
                  : p.kind == KK_Q4_MMA     ? (a.sq && q4_skinny_ok(a.K, a.w) ? launch_q4_skinny(p, a, s)
                                                                        : launch_q4_mma(p, a, s))

@@ -57,7 +57,8 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   const bool q8 = type == MM_TYPE_Q8_0;
   if ((type == MM_TYPE_Q4_0 || type == MM_TYPE_Q4_0R || q8) && (K % kQK)) return MM_ERR_SHAPE;
   if (type == MM_TYPE_Q4_0R && variant == 1) return MM_ERR_ARG;   // no narrow kernel for it
-  if (q8 && variant == 3) return MM_ERR_ARG;                      // no skinny kernel for Q8_0
+  // Q8_0 weights: the skinny kernel takes block pairs (K / 32 even)
+  if (q8 && variant == 3 && (K / kQK) % 2) return MM_ERR_ARG;
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
   if (K == 0) { p->kind = KK_ZERO; return MM_OK; }
   if (variant == 0) {
@@ -75,7 +76,8 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     // a multiple of 64, and src1 staged whole in LDS) for M <= 2 or when
     // forced (passes of two src1 rows), the wide kernel otherwise.
     const bool q8_fusable = q8 && nb % 2 == 0 && 2 * nb * 40 <= kNarrowMaxLds;
-    const bool mma = !q8 && (variant == 3 || (variant == 0 && (rep || M > kFuseMaxM) && M <= kMmaMaxM));
+    const bool mma = q8 ? nb % 2 == 0 && (variant == 3 || (variant == 0 && M > kFuseMaxM && M <= 8))
+                        : variant == 3 || (variant == 0 && (rep || M > kFuseMaxM) && M <= kMmaMaxM);
     const bool narrow = q8 ? q8_fusable && (variant == 1 || (variant == 0 && M <= kFuseMaxM))
                            : !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
     if (q8 && variant == 1 && !narrow) return MM_ERR_ARG;
@@ -117,7 +119,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       // 8 src1 rows (two blocks per MFMA), 16 or 32.
       p->kind = KK_Q4_MMA;
       p->variant = 3;
-      p->mt = M <= 8 ? 8 : M <= 16 ? 16 : 32;
+      p->mt = (q8 || M <= 8) ? 8 : M <= 16 ? 16 : 32;   // Q8_0: passes of 8 rows only
       // 16 weight rows per workgroup (and per wave).  (32, two MFMA row
       // tiles sharing each activation load, measured no faster at 14336 rows
       // and slower at 4096: half the workgroups.)

@@ -42,6 +42,7 @@
 //     scale products and the epilogue per block, and reads no padding rows.
 #include "device.h"
 #include "kernels.h"
+#include "../../include/mm.h"
 
 namespace qsg {
 
@@ -313,20 +314,37 @@ hipError_t launch_mp(const Plan& p, const Q4Args& a, hipStream_t s) {
 // B operand of column (m, e) is zero outside block e, so output (n, (m, e))
 // is the block dot of block e alone.  Lane (row i, group g) of A holds half
 // g & 1 of block g >> 1 of its row.
+//
+// kQ8: Q8_0 weights.  A unit (block pair) is 68 bytes, 17 dwords: block 0's
+// scale in the low half of dword 0 and its codes from byte 2 (dwords shifted
+// by 16 bits), block 1's scale in the high half of dword 8 and its codes
+// dword-aligned from dword 9.  The codes are the A operand as stored (the
+// MFMA gives S_b, not 16 S_b), so the weight scale enters the scale product
+// as 16 d_w (exact) against the stored d_a / 16.
+template <bool kQ8>
+struct Unit8 {
+  static constexpr int kDwords = kQ8 ? 17 : 9;          // dwords per block pair
+  static constexpr int kPitch = kPH * 4 * kDwords + 4;  // LDS row pitch (odd dword count)
+  static constexpr int kBytes = 16 * kPitch;            // one wave's patch
+};
+
+template <bool kQ8>
 struct Phase8 {
-  uint32_t w[9];
+  uint32_t w[Unit8<kQ8>::kDwords];
   v4i act[kPH];
   v4i da;                     // d_a / 16 of pair j's block for this column (zero elsewhere)
 };
 
-__device__ __forceinline__ void load_phase8(Phase8& P, const Q4Args& a, const uint8_t* wrow,
+template <bool kQ8>
+__device__ __forceinline__ void load_phase8(Phase8<kQ8>& P, const Q4Args& a, const uint8_t* wrow,
                                             int j0, int pairs, int ty) {
+  constexpr int UW = Unit8<kQ8>::kDwords;
   const int lane = threadIdx.x & 63;
   int pc = j0 + (lane & 3);
   pc = pc < pairs ? pc : pairs - 1;
-  const uint8_t* wp = wrow + 36 * (int64_t)pc;
+  const uint8_t* wp = wrow + 4 * UW * (int64_t)pc;
 #pragma unroll
-  for (int i = 0; i < 9; ++i) P.w[i] = gload32(wp + 4 * i);
+  for (int i = 0; i < UW; ++i) P.w[i] = gload32(wp + 4 * i);
   const __amdgpu_buffer_rsrc_t rq = wdata_rsrc(a.sq, a.sq_bytes);
   const __amdgpu_buffer_rsrc_t rs = wdata_rsrc(a.ss, a.ss_bytes);
   const int tp = ty * a.sk_phases + j0 / kPH;
@@ -339,35 +357,53 @@ __device__ __forceinline__ void load_phase8(Phase8& P, const Q4Args& a, const ui
   P.da = bload128(rs, (mv && g == e) ? (tp * 16 + c) * 16 : kSkip);
 }
 
-template <bool kDump>
-__device__ __forceinline__ void compute_phase8(const Phase8& P, float (&acc)[4], uint8_t* stage,
+template <bool kDump, bool kQ8>
+__device__ __forceinline__ void compute_phase8(const Phase8<kQ8>& P, float (&acc)[4], uint8_t* stage,
                                                int j0, int j1, int n0, int m0, const Q4Args& a) {
+  constexpr int UW = Unit8<kQ8>::kDwords, RP = Unit8<kQ8>::kPitch;
   const int lane = threadIdx.x & 63;
   const int i16 = lane & 15, g = lane >> 4;
   {
-    uint32_t* d = reinterpret_cast<uint32_t*>(stage + (lane >> 2) * kRP + 36 * (lane & 3));
+    uint32_t* d = reinterpret_cast<uint32_t*>(stage + (lane >> 2) * RP + 4 * UW * (lane & 3));
 #pragma unroll
-    for (int i = 0; i < 9; ++i) d[i] = P.w[i];
+    for (int i = 0; i < UW; ++i) d[i] = P.w[i];
   }
   // Code dwords of this lane's half block: block 0's codes start 2 bytes into
   // the unit (a funnel shift by 16 of dwords b .. b+2), block 1's are dword
   // aligned (shift 0, so dword b+2 -- for g = 3 the row's pad dword after the
   // last pair -- is read but not used).
-  const int b = g < 2 ? 2 * g : 2 * g + 1;
-  const int sh = g < 2 ? 16 : 0;
-  // Weight scale of block g & 1 (unit bytes 0-1 or 18-19): the scale MFMA's
-  // k = g; for g = 2, 3 the B operand is zero there, any finite value works.
-  const int ds = (g & 1) ? 4 : 0, dsh = (g & 1) * 16;
+  // Q4_0: code bytes 8s .. 8s + 7 of block g >> 1 (s = g & 1), whose low and
+  // high nibbles are elements 8s .. 8s+7 and 16+8s .. 23+8s.  Q8_0: code
+  // dwords 2s, 4+2s, 2s+1, 5+2s of that block (dword q holds elements 4q ..
+  // 4q+3), the same element order as the activation operand.
+  const int b = kQ8 ? ((g >> 1) ? 9 : 0) : (g < 2 ? 2 * g : 2 * g + 1);
+  const int sh = kQ8 ? ((g >> 1) ? 0 : 16) : (g < 2 ? 16 : 0);
+  const int s2 = 2 * (g & 1);
+  // Weight scale of block g & 1 (Q4_0 unit bytes 0-1 or 18-19; Q8_0 bytes
+  // 0-1 or 34-35): the scale MFMA's k = g; for g = 2, 3 the B operand is
+  // zero there, any finite value works.
+  const int ds = kQ8 ? ((g & 1) ? 8 : 0) : ((g & 1) ? 4 : 0), dsh = (g & 1) * 16;
   const int nb = a.K / 32;
 #pragma unroll
   for (int jj = 0; jj < kPH; ++jj) {
-    const uint32_t* u = reinterpret_cast<const uint32_t*>(stage + i16 * kRP) + 9 * jj;
-    const uint32_t x0 = u[b], x1 = u[b + 1], x2 = u[b + 2];
-    const long A0 = nibbles_x16(__builtin_amdgcn_alignbit(x1, x0, sh));
-    const long A1 = nibbles_x16(__builtin_amdgcn_alignbit(x2, x1, sh));
-    const v4i A = v4i{(int)(uint32_t)A0, (int)(uint32_t)((uint64_t)A0 >> 32),
-                      (int)(uint32_t)A1, (int)(uint32_t)((uint64_t)A1 >> 32)};
-    const float dw = f16_bits_to_f32((u[ds] >> dsh) & 0xFFFFu);
+    const uint32_t* u = reinterpret_cast<const uint32_t*>(stage + i16 * RP) + UW * jj;
+    v4i A;
+    float dw;
+    if constexpr (kQ8) {
+      // code dword q of the block: dwords b + q, b + q + 1 shifted by sh (for
+      // block 1, q = 7, the second is the next unit's first dword or the
+      // row's pad: unused, the shift is 0)
+      auto cd = [&](int q) { return (int)__builtin_amdgcn_alignbit(u[b + q + 1], u[b + q], sh); };
+      A = v4i{cd(s2), cd(4 + s2), cd(s2 + 1), cd(5 + s2)};
+      dw = 16.0f * f16_bits_to_f32((u[ds] >> dsh) & 0xFFFFu);
+    } else {
+      const uint32_t x0 = u[b], x1 = u[b + 1], x2 = u[b + 2];
+      const long A0 = nibbles_x16(__builtin_amdgcn_alignbit(x1, x0, sh));
+      const long A1 = nibbles_x16(__builtin_amdgcn_alignbit(x2, x1, sh));
+      A = v4i{(int)(uint32_t)A0, (int)(uint32_t)((uint64_t)A0 >> 32),
+              (int)(uint32_t)A1, (int)(uint32_t)((uint64_t)A1 >> 32)};
+      dw = f16_bits_to_f32((u[ds] >> dsh) & 0xFFFFu);
+    }
     const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, P.act[jj], v4i{0, 0, 0, 0}, 0, 0, 0);
     const v4f sc = __builtin_amdgcn_mfma_f32_16x16x4f32(dw, __int_as_float(P.da[jj]), v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
     acc[0] = fmaf((float)D.x, sc.x, acc[0]);
@@ -382,49 +418,49 @@ __device__ __forceinline__ void compute_phase8(const Phase8& P, float (&acc)[4],
       for (int r = 0; r < 4; ++r) {
         const int n = n0 + 4 * g + r;
         if (m < a.M && n >= a.n0 && n < a.n1)
-          a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + bk] = Dv[r] / 16;
+          a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + bk] = kQ8 ? Dv[r] : Dv[r] / 16;
       }
     }
   }
 }
 
-template <int W, bool kDump>
+template <int W, bool kDump, bool kQ8>
 __global__ __launch_bounds__(64 * W)
 void k_q4_skinny8(Q4Args a, int pp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nb = a.K / 32, pairs = nb / 2;
-  const int64_t rb = (int64_t)nb * 18;
+  const int64_t rb = (int64_t)nb * (kQ8 ? 34 : 18);
   const int n0 = blockIdx.x * 16, ty = blockIdx.y, m0 = ty * 8;
   const int j0w = wave * pp < pairs ? wave * pp : pairs;
   const int j1w = j0w + pp < pairs ? j0w + pp : pairs;
   const int nph = (j1w - j0w + kPH - 1) / kPH;
-  uint8_t* stage = smem + wave * WaveLds<1>::kBytes;
+  uint8_t* stage = smem + wave * Unit8<kQ8>::kBytes;
   int nrow = n0 + (lane >> 2);
   nrow = nrow < a.N ? nrow : a.N - 1;
   const uint8_t* wrow = a.w + nrow * rb;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  Phase8 P0, P1;
+  Phase8<kQ8> P0, P1;
   if (nph > 0) load_phase8(P0, a, wrow, j0w, pairs, ty);
   int f = 0;
   for (; f + 2 < nph; f += 2) {
     load_phase8(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase8<kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase8<kDump, kQ8>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
     __builtin_amdgcn_sched_barrier(0);
     load_phase8(P0, a, wrow, j0w + (f + 2) * kPH, pairs, ty);
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase8<kDump>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+    compute_phase8<kDump, kQ8>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (f + 1 < nph) {
     load_phase8(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase8<kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
-    compute_phase8<kDump>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+    compute_phase8<kDump, kQ8>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase8<kDump, kQ8>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
   } else if (f < nph) {
-    compute_phase8<kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase8<kDump, kQ8>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
   }
   // the W waves' partial tiles, then the two block halves of each column,
   // added in a fixed order
@@ -443,24 +479,29 @@ void k_q4_skinny8(Q4Args a, int pp) {
   }
 }
 
-template <int W>
+template <int W, bool kQ8>
 hipError_t launch_w8(const Plan& p, const Q4Args& a, int pp, hipStream_t s) {
   const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1u);
-  const size_t stage = (size_t)W * WaveLds<1>::kBytes;
+  const size_t stage = (size_t)W * Unit8<kQ8>::kBytes;
   const size_t red = (size_t)W * 4 * 64 * 4;
   const size_t lds = stage > red ? stage : red;
-  if (a.dots) hipLaunchKernelGGL((k_q4_skinny8<W, true>), grid, dim3(64 * W), lds, s, a, pp);
-  else hipLaunchKernelGGL((k_q4_skinny8<W, false>), grid, dim3(64 * W), lds, s, a, pp);
+  if (a.dots) hipLaunchKernelGGL((k_q4_skinny8<W, true, kQ8>), grid, dim3(64 * W), lds, s, a, pp);
+  else hipLaunchKernelGGL((k_q4_skinny8<W, false, kQ8>), grid, dim3(64 * W), lds, s, a, pp);
   return hipGetLastError();
+}
+
+template <bool kQ8>
+hipError_t launch_8q(const Plan& p, const Q4Args& a, int pp, hipStream_t s) {
+  if (p.waves == 4) return launch_w8<4, kQ8>(p, a, pp, s);
+  if (p.waves == 8) return launch_w8<8, kQ8>(p, a, pp, s);
+  if (p.waves == 16) return launch_w8<16, kQ8>(p, a, pp, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_8(const Plan& p, const Q4Args& a, hipStream_t s) {
   const int pp = (int)p.kchunk;
   if (!a.sq || pp % kPH) return hipErrorInvalidValue;
-  if (p.waves == 4) return launch_w8<4>(p, a, pp, s);
-  if (p.waves == 8) return launch_w8<8>(p, a, pp, s);
-  if (p.waves == 16) return launch_w8<16>(p, a, pp, s);
-  return hipErrorInvalidValue;
+  return p.type == MM_TYPE_Q8_0 ? launch_8q<true>(p, a, pp, s) : launch_8q<false>(p, a, pp, s);
 }
 
 // ---- Repacked weights (Q4_0R, repack.hip): per 16-row tile and phase of 8
@@ -649,6 +690,7 @@ bool q4_skinny_ok(int K, const void* w) {
 hipError_t launch_q4_skinny(const Plan& p, const Q4Args& a, hipStream_t s) {
   if (p.split != 1 || !q4_skinny_ok(a.K, a.w)) return hipErrorInvalidValue;
   if (p.mt == 8 && p.rpw == 16) return launch_8(p, a, s);
+  if (p.type == MM_TYPE_Q8_0) return hipErrorInvalidValue;   // 8-row passes only
   if (p.mt == 16 && p.rpw == 16) return launch_mp<1, 1>(p, a, s);
   if (p.mt == 32 && p.rpw == 16) return launch_mp<2, 1>(p, a, s);
   if (p.mt == 16 && p.rpw == 32) return launch_mp<1, 2>(p, a, s);

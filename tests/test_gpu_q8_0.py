@@ -134,14 +134,15 @@ def test_q8_0_decode_shapes_and_batch_vs_alone(j):
 
 
 def test_q8_0_debug_rules():
-    """No skinny kernel for Q8_0 weights, and block dots only from the wide
-    kernel: both are argument errors that launch nothing."""
+    """The skinny kernel needs K/32 even, and the fused kernel writes no
+    block dots: both are argument errors that launch nothing."""
     import torch
     qs = _qs()
     wq, x = _case(1, 64, 512, 9)
     wq_dev, x_dev = to_dev(wq), to_dev(x)
     MM_ERR_ARG = -8
-    st, _, _ = _debug(wq_dev, x_dev, 64, 3, 0, 0)
+    wq3, x3 = _case(1, 64, 96, 10)
+    st, _, _ = _debug(to_dev(wq3), to_dev(x3), 64, 3, 0, 0)
     assert st == MM_ERR_ARG
     st, _, _ = _debug(wq_dev, x_dev, 64, 0, 0, 8)          # M = 1: the fused kernel
     assert st == MM_ERR_ARG
@@ -149,3 +150,52 @@ def test_q8_0_debug_rules():
     assert st == 0
     torch.cuda.synchronize()
     assert_close(to_host(y), mul_mat.mul_mat_q8_0_f32(wq, x), TOL_Q4_0, "q8_0 forced narrow")
+
+
+# The 8-row skinny kernel on Q8_0 weights (2 < M <= 8 by default; passes of
+# 8 rows when forced): ragged N, a last phase of fewer than 4 block pairs
+# (K = 2112: 33 pairs), one pair (K = 64), several passes over M.
+@pytest.mark.parametrize("m,n,k", [(3, 300, 512), (8, 4096, 4096), (5, 37, 64), (7, 129, 2112),
+                                   (8, 14336, 4096), (20, 100, 1024), (4, 4096, 14336)])
+def test_q8_0_skinny_products_and_dots(m, n, k):
+    import torch
+    qs = _qs()
+    wq, x = _case(m, n, k, 4000 + m * 31 + n + k)
+    wq_dev, x_dev = to_dev(wq), to_dev(x)
+    say("q8_0 skinny", m, n, k, qs.dispatch(qs.MM_TYPE_Q8_0, m, n, k))
+    cols = (max(0, n - 40), n)
+    st, y, dots = _debug(wq_dev, x_dev, n, 3, *cols)
+    assert st == 0, qs.status_string(st)
+    ref = mul_mat.mul_mat_q8_0_f32(wq, x)
+    assert_close(to_host(y), ref, TOL_Q4_0, f"q8_0 skinny {m}x{n}x{k}")
+    want = codec.block_dots_q8(wq[cols[0]:cols[1]], codec.quantize_q8_0(x), k)
+    assert np.array_equal(to_host(dots), want)
+    if qs.dispatch(qs.MM_TYPE_Q8_0, m, n, k)[0] == 3:
+        assert bool(torch.equal(y, qs.mul_mat_q8_0_f32(wq_dev, x_dev)))
+
+
+def test_q8_0_skinny_extremes():
+    """Codes -128 and 127 and scales from a binary16 subnormal to its
+    largest value through the skinny kernel: exact block dots, dst within
+    the bound."""
+    qs = _qs()
+    rng = np.random.default_rng(6)
+    n, k, m = 48, 1024, 6
+    nb = k // 32
+    codes = rng.integers(-128, 128, size=(n, nb, 32))
+    codes[0] = -128
+    codes[1] = 127
+    d_bits = rng.choice(np.array([0x0001, 0x03FF, 0x3C00, 0x7BFF, 0x0400, 0xBC00], dtype=np.uint16),
+                        size=(n, nb))
+    blk = np.empty((n, nb, 34), dtype=np.uint8)
+    blk[..., 0] = d_bits & 0xFF
+    blk[..., 1] = d_bits >> 8
+    blk[..., 2:] = codes.astype(np.int8).view(np.uint8)
+    wq = blk.reshape(n, nb * 34)
+    x = rng.standard_normal((m, k)).astype(np.float32) * np.float32(1e-3)
+    x[0, :32] = -127.0
+    say("q8_0 skinny extremes")
+    st, y, dots = _debug(to_dev(wq), to_dev(x), n, 3, 0, n)
+    assert st == 0, qs.status_string(st)
+    assert np.array_equal(to_host(dots), codec.block_dots_q8(wq, codec.quantize_q8_0(x), k))
+    assert_close(to_host(y), mul_mat.mul_mat_q8_0_f32(wq, x), TOL_Q4_0, "q8_0 skinny extremes")
