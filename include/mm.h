@@ -209,10 +209,10 @@ int mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst,
  * dst[m][n] = sum_b f32(d_w[n][b]) * f32(d_a[m][b]) * S_b[m][n], with the
  * int32 block dot S_b = sum_j qw * qa of the two signed code sets (|S_b| <=
  * 32 * 128 * 128), accumulated in fp32.  M <= 2 with K a multiple of 64:
- * one kernel that quantizes src1 itself; 2 < M <= 8 with K a multiple of
- * 64: INIT, then the skinny int8 MFMA kernel (16 weight rows per
- * workgroup, two blocks per MFMA); otherwise INIT, then the tiled int8 MFMA
- * kernel.
+ * one kernel that quantizes src1 itself; 2 < M <= 32 with K a multiple
+ * of 64: INIT, then the skinny int8 MFMA kernel (16 weight rows per
+ * workgroup, passes of 8, 16 or 32 src1 rows); otherwise INIT, then the
+ * tiled int8 MFMA kernel.
  */
 int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
                         int64_t M, int64_t N, int64_t K,

@@ -76,7 +76,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     // a multiple of 64, and src1 staged whole in LDS) for M <= 2 or when
     // forced (passes of two src1 rows), the wide kernel otherwise.
     const bool q8_fusable = q8 && nb % 2 == 0 && 2 * nb * 40 <= kNarrowMaxLds;
-    const bool mma = q8 ? nb % 2 == 0 && (variant == 3 || (variant == 0 && M > kFuseMaxM && M <= 8))
+    const bool mma = q8 ? nb % 2 == 0 && (variant == 3 || (variant == 0 && M > kFuseMaxM && M <= kMmaMaxM))
                         : variant == 3 || (variant == 0 && (rep || M > kFuseMaxM) && M <= kMmaMaxM);
     const bool narrow = q8 ? q8_fusable && (variant == 1 || (variant == 0 && M <= kFuseMaxM))
                            : !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
@@ -119,7 +119,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       // 8 src1 rows (two blocks per MFMA), 16 or 32.
       p->kind = KK_Q4_MMA;
       p->variant = 3;
-      p->mt = (q8 || M <= 8) ? 8 : M <= 16 ? 16 : 32;   // Q8_0: passes of 8 rows only
+      p->mt = M <= 8 ? 8 : M <= 16 ? 16 : 32;
       // 16 weight rows per workgroup (and per wave).  (32, two MFMA row
       // tiles sharing each activation load, measured no faster at 14336 rows
       // and slower at 4096: half the workgroups.)

@@ -51,15 +51,18 @@ namespace {
 constexpr int kPH = kSkinnyPairs;        // block pairs per phase (16 rows x 4 = 64 units)
 constexpr int kRP = kPH * 36 + 4;        // LDS row pitch: 37 dwords, odd, so rows spread the banks
 
-// LDS of one wave: its patch of RT x 16 weight rows.
-template <int RT>
+// LDS of one wave: its patch of RT x 16 weight rows (kQ8: 68-byte units,
+// row pitch 69 dwords).
+template <int RT, bool kQ8 = false>
 struct WaveLds {
-  static constexpr int kBytes = RT * 16 * kRP;
+  static constexpr int kUnit = kQ8 ? 17 : 9;             // dwords per block pair
+  static constexpr int kPitch = kQ8 ? kPH * 68 + 4 : kRP;
+  static constexpr int kBytes = RT * 16 * kPitch;
 };
 
-template <int MP, int RT>
+template <int MP, int RT, bool kQ8 = false>
 struct Phase {
-  uint32_t w[RT][9];          // this lane's units: one row's block pair per row tile
+  uint32_t w[RT][kQ8 ? 17 : 9];  // this lane's units: one row's block pair per row tile
   v4i act[MP][kPH];           // B operands of pair j: blocks 2j and 2j+1
   float da[MP][2 * kPH];      // activation scale per m tile and block
 };
@@ -90,18 +93,19 @@ __device__ __forceinline__ v4i bload128(__amdgpu_buffer_rsrc_t r, int off) {
 // load scales: the scale MFMA reads its B operand from k = 0 alone, so the
 // other lanes' zeros keep it a plain outer product.  Blocks past K hold
 // zeros in the wdata.
-template <int MP, int RT>
-__device__ __forceinline__ void load_phase(Phase<MP, RT>& P, const Q4Args& a,
+template <int MP, int RT, bool kQ8>
+__device__ __forceinline__ void load_phase(Phase<MP, RT, kQ8>& P, const Q4Args& a,
                                            const uint8_t* const (&wrow)[RT], int j0, int pairs,
                                            int ty) {
+  constexpr int UW = WaveLds<RT, kQ8>::kUnit;
   const int lane = threadIdx.x & 63;
   int pc = j0 + (lane & 3);
   pc = pc < pairs ? pc : pairs - 1;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const uint8_t* wp = wrow[rt] + 36 * (int64_t)pc;
+    const uint8_t* wp = wrow[rt] + 4 * UW * (int64_t)pc;
 #pragma unroll
-    for (int i = 0; i < 9; ++i) P.w[rt][i] = gload32(wp + 4 * i);
+    for (int i = 0; i < UW; ++i) P.w[rt][i] = gload32(wp + 4 * i);
   }
   const int f = j0 / kPH;
   const __amdgpu_buffer_rsrc_t rq = wdata_rsrc(a.sq, a.sq_bytes);
@@ -140,18 +144,19 @@ __device__ __forceinline__ v4f scale_tile(float dw_row, float da_col) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(dw_row, da_col, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 }
 
-template <int MP, int RT, bool kDump>
-__device__ __forceinline__ void compute_phase(const Phase<MP, RT>& P, float (&acc)[RT][MP][4],
+template <int MP, int RT, bool kDump, bool kQ8>
+__device__ __forceinline__ void compute_phase(const Phase<MP, RT, kQ8>& P, float (&acc)[RT][MP][4],
                                               uint8_t* stage, int j0, int j1, int n0, int m0,
                                               const Q4Args& a) {
+  constexpr int UW = WaveLds<RT, kQ8>::kUnit, RP = WaveLds<RT, kQ8>::kPitch;
   const int lane = threadIdx.x & 63;
   const int i16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     // this lane's unit -> row 16 rt + lane / 4, pair lane % 4 of the patch
-    uint32_t* d = reinterpret_cast<uint32_t*>(stage + (16 * rt + (lane >> 2)) * kRP + 36 * (lane & 3));
+    uint32_t* d = reinterpret_cast<uint32_t*>(stage + (16 * rt + (lane >> 2)) * RP + 4 * UW * (lane & 3));
 #pragma unroll
-    for (int i = 0; i < 9; ++i) d[i] = P.w[rt][i];
+    for (int i = 0; i < UW; ++i) d[i] = P.w[rt][i];
   }
   // LDS operations of one wave complete in order: the reads below see the
   // writes above, and the next phase's writes come after these reads.
@@ -164,11 +169,22 @@ __device__ __forceinline__ void compute_phase(const Phase<MP, RT>& P, float (&ac
     float dw[RT][2];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const uint32_t* u = reinterpret_cast<const uint32_t*>(stage + (16 * rt + i16) * kRP) + 9 * jj;
-      A[rt][0] = nibbles_x16(__builtin_amdgcn_alignbit(u[g + 1], u[g], 16));   // even block
-      A[rt][1] = nibbles_x16(u[5 + g]);                                       // odd block
-      dw[rt][0] = f16_bits_to_f32(u[0]);                                      // row 16 rt + i16
-      dw[rt][1] = f16_bits_to_f32(u[4] >> 16);
+      const uint32_t* u = reinterpret_cast<const uint32_t*>(stage + (16 * rt + i16) * RP) + UW * jj;
+      if constexpr (kQ8) {
+        // elements 4g .. 4g+3 and 16+4g .. 19+4g of each block: code dwords g
+        // and 4 + g (even block: bytes from 2, shifted by 16 bits; odd block:
+        // dword aligned from dword 9); the MFMA yields S_b, so 16 d_w
+        auto c0 = [&](int q) { return (uint64_t)__builtin_amdgcn_alignbit(u[q + 1], u[q], 16); };
+        A[rt][0] = (long)(c0(g) | (c0(4 + g) << 32));
+        A[rt][1] = (long)((uint64_t)u[9 + g] | ((uint64_t)u[13 + g] << 32));
+        dw[rt][0] = 16.0f * f16_bits_to_f32(u[0] & 0xFFFFu);
+        dw[rt][1] = 16.0f * f16_bits_to_f32(u[8] >> 16);
+      } else {
+        A[rt][0] = nibbles_x16(__builtin_amdgcn_alignbit(u[g + 1], u[g], 16));   // even block
+        A[rt][1] = nibbles_x16(u[5 + g]);                                       // odd block
+        dw[rt][0] = f16_bits_to_f32(u[0]);                                      // row 16 rt + i16
+        dw[rt][1] = f16_bits_to_f32(u[4] >> 16);
+      }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -195,7 +211,7 @@ __device__ __forceinline__ void compute_phase(const Phase<MP, RT>& P, float (&ac
             for (int r = 0; r < 4; ++r) {
               const int n = n0 + 16 * rt + 4 * g + r;
               if (m < a.M && n >= a.n0 && n < a.n1)
-                a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + b] = Dv[r] / 16;
+                a.dots[((int64_t)m * (a.n1 - a.n0) + (n - a.n0)) * nb + b] = kQ8 ? Dv[r] : Dv[r] / 16;
             }
           }
         }
@@ -206,20 +222,20 @@ __device__ __forceinline__ void compute_phase(const Phase<MP, RT>& P, float (&ac
 
 // Workgroup: RT x 16 weight rows; its W waves split K into runs of pp block
 // pairs (a multiple of the phase).
-template <int MP, int RT, int W, bool kDump>
+template <int MP, int RT, int W, bool kDump, bool kQ8>
 __global__ __launch_bounds__(64 * W)
 void k_q4_skinny(Q4Args a, int pp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nb = a.K / 32, pairs = nb / 2;
-  const int64_t rb = (int64_t)nb * 18;
+  const int64_t rb = (int64_t)nb * (kQ8 ? 34 : 18);
   const int n0 = blockIdx.x * 16 * RT, ty = blockIdx.y, m0 = ty * 16 * MP;
   // this wave's block pairs [j0w, j1w)
   const int j0w = wave * pp < pairs ? wave * pp : pairs;
   const int j1w = j0w + pp < pairs ? j0w + pp : pairs;
   const int nph = (j1w - j0w + kPH - 1) / kPH;
-  uint8_t* stage = smem + wave * WaveLds<RT>::kBytes;
+  uint8_t* stage = smem + wave * WaveLds<RT, kQ8>::kBytes;
   const uint8_t* wrow[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -240,26 +256,26 @@ void k_q4_skinny(Q4Args a, int pp) {
   // last one or two phases are computed after it.
   // (The scheduling barriers keep the loads of one set from being hoisted
   // above the computation of the other, which would hold three sets.)
-  Phase<MP, RT> P0, P1;
-  if (nph > 0) load_phase<MP, RT>(P0, a, wrow, j0w, pairs, ty);
+  Phase<MP, RT, kQ8> P0, P1;
+  if (nph > 0) load_phase<MP, RT, kQ8>(P0, a, wrow, j0w, pairs, ty);
   int f = 0;
   for (; f + 2 < nph; f += 2) {
-    load_phase<MP, RT>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
+    load_phase<MP, RT, kQ8>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase<MP, RT, kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump, kQ8>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
     __builtin_amdgcn_sched_barrier(0);
-    load_phase<MP, RT>(P0, a, wrow, j0w + (f + 2) * kPH, pairs, ty);
+    load_phase<MP, RT, kQ8>(P0, a, wrow, j0w + (f + 2) * kPH, pairs, ty);
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase<MP, RT, kDump>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump, kQ8>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (f + 1 < nph) {
-    load_phase<MP, RT>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
+    load_phase<MP, RT, kQ8>(P1, a, wrow, j0w + (f + 1) * kPH, pairs, ty);
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase<MP, RT, kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
-    compute_phase<MP, RT, kDump>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump, kQ8>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump, kQ8>(P1, acc, stage, j0w + (f + 1) * kPH, j1w, n0, m0, a);
   } else if (f < nph) {
-    compute_phase<MP, RT, kDump>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
+    compute_phase<MP, RT, kDump, kQ8>(P0, acc, stage, j0w + f * kPH, j1w, n0, m0, a);
   }
 
   // ---- add the W waves' partial tiles in a fixed order (LDS reused)
@@ -285,15 +301,21 @@ void k_q4_skinny(Q4Args a, int pp) {
   }
 }
 
-template <int MP, int RT, int W>
-hipError_t launch_w(const Plan& p, const Q4Args& a, int pp, hipStream_t s) {
+template <int MP, int RT, int W, bool kQ8>
+hipError_t launch_wq(const Plan& p, const Q4Args& a, int pp, hipStream_t s) {
   const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, 1u);
-  const size_t stage = (size_t)W * WaveLds<RT>::kBytes;
+  const size_t stage = (size_t)W * WaveLds<RT, kQ8>::kBytes;
   const size_t red = (size_t)W * RT * MP * 4 * 64 * 4;
   const size_t lds = stage > red ? stage : red;
-  if (a.dots) hipLaunchKernelGGL((k_q4_skinny<MP, RT, W, true>), grid, dim3(64 * W), lds, s, a, pp);
-  else hipLaunchKernelGGL((k_q4_skinny<MP, RT, W, false>), grid, dim3(64 * W), lds, s, a, pp);
+  if (a.dots) hipLaunchKernelGGL((k_q4_skinny<MP, RT, W, true, kQ8>), grid, dim3(64 * W), lds, s, a, pp);
+  else hipLaunchKernelGGL((k_q4_skinny<MP, RT, W, false, kQ8>), grid, dim3(64 * W), lds, s, a, pp);
   return hipGetLastError();
+}
+
+template <int MP, int RT, int W>
+hipError_t launch_w(const Plan& p, const Q4Args& a, int pp, hipStream_t s) {
+  return p.type == MM_TYPE_Q8_0 ? launch_wq<MP, RT, W, true>(p, a, pp, s)
+                                : launch_wq<MP, RT, W, false>(p, a, pp, s);
 }
 
 template <int MP, int RT>
@@ -690,7 +712,7 @@ bool q4_skinny_ok(int K, const void* w) {
 hipError_t launch_q4_skinny(const Plan& p, const Q4Args& a, hipStream_t s) {
   if (p.split != 1 || !q4_skinny_ok(a.K, a.w)) return hipErrorInvalidValue;
   if (p.mt == 8 && p.rpw == 16) return launch_8(p, a, s);
-  if (p.type == MM_TYPE_Q8_0) return hipErrorInvalidValue;   // 8-row passes only
+  if (p.type == MM_TYPE_Q8_0 && p.rpw != 16) return hipErrorInvalidValue;
   if (p.mt == 16 && p.rpw == 16) return launch_mp<1, 1>(p, a, s);
   if (p.mt == 32 && p.rpw == 16) return launch_mp<2, 1>(p, a, s);
   if (p.mt == 16 && p.rpw == 32) return launch_mp<1, 2>(p, a, s);

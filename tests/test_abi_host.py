@@ -308,10 +308,10 @@ def test_repack_host_checks():
 
 def test_q8_0_weights_host_rules():
     """Q8_0 weights: the fused kernel at M <= 2 when K/32 is even (one launch,
-    no workspace use), the 8-row skinny kernel at 2 < M <= 8 (INIT, then the
-    product), the wide kernel otherwise (INIT, product and maybe a reduce);
-    the forced skinny kernel (variant 3) takes passes of 8 rows and needs
-    K/32 even; 4-byte alignment of src0; K % 32."""
+    no workspace use), the skinny kernel at 2 < M <= 32 (INIT, then the
+    product; passes of 8, 16 or 32 rows), the wide kernel otherwise (INIT,
+    product and maybe a reduce); the skinny kernel needs K/32 even; 4-byte
+    alignment of src0; K % 32."""
     d = (ctypes.c_int * 5)()
     assert qs.lib.mm_dispatch(Q8, 1, 4096, 4096, d) == OK and d[0] == 1 and d[4] == 1
     assert qs.lib.mm_dispatch(Q8, 2, 11008, 4096, d) == OK and d[0] == 1 and d[2] == 2 and d[4] == 1
@@ -319,10 +319,12 @@ def test_q8_0_weights_host_rules():
     assert qs.lib.mm_dispatch(Q8, 3, 4096, 4096, d) == OK and d[0] == 3 and d[4] == 2
     assert qs.lib.mm_dispatch(Q8, 8, 14336, 4096, d) == OK and d[0] == 3 and d[4] == 2
     assert qs.lib.mm_dispatch(Q8, 5, 300, 96, d) == OK and d[0] == 2           # K/32 odd: wide
-    assert qs.lib.mm_dispatch(Q8, 9, 4096, 4096, d) == OK and d[0] == 2
+    assert qs.lib.mm_dispatch(Q8, 9, 4096, 4096, d) == OK and d[0] == 3 and d[2] == 16
+    assert qs.lib.mm_dispatch(Q8, 32, 4096, 4096, d) == OK and d[0] == 3 and d[2] == 32
+    assert qs.lib.mm_dispatch(Q8, 33, 4096, 4096, d) == OK and d[0] == 2
     assert qs.lib.mm_dispatch(Q8, 512, 14336, 4096, d) == OK and d[0] == 2 and (d[2], d[3]) == (128, 64)
     assert qs.lib.mm_dispatch(Q8, 1, 64, 48, d) == SHAPE
-    assert qs.lib.mm_debug_workspace_size(Q8, 20, 64, 64, 3) > 0                # 8-row passes
+    assert qs.lib.mm_debug_workspace_size(Q8, 40, 64, 64, 3) > 0                # 32-row passes
     assert qs.lib.mm_debug_mul_mat(Q8, FAKE, FAKE, FAKE, None, 4, 64, 96, 0, 0, 3, None, 0, None) == ARG
     assert qs.lib.mm_debug_mul_mat(Q8, FAKE, FAKE, FAKE, None, 4, 64, 96, 0, 0, 1, None, 0, None) == ARG
     ws = qs.workspace_size(Q8, 8, 256, 512)

@@ -152,11 +152,13 @@ def test_q8_0_debug_rules():
     assert_close(to_host(y), mul_mat.mul_mat_q8_0_f32(wq, x), TOL_Q4_0, "q8_0 forced narrow")
 
 
-# The 8-row skinny kernel on Q8_0 weights (2 < M <= 8 by default; passes of
-# 8 rows when forced): ragged N, a last phase of fewer than 4 block pairs
-# (K = 2112: 33 pairs), one pair (K = 64), several passes over M.
+# The skinny kernels on Q8_0 weights (8-, 16- and 32-row passes; 2 < M <= 32
+# by default, any M when forced): ragged N, a last phase of fewer than 4
+# block pairs (K = 2112: 33 pairs), one pair (K = 64), several passes over M.
 @pytest.mark.parametrize("m,n,k", [(3, 300, 512), (8, 4096, 4096), (5, 37, 64), (7, 129, 2112),
-                                   (8, 14336, 4096), (20, 100, 1024), (4, 4096, 14336)])
+                                   (8, 14336, 4096), (20, 100, 1024), (4, 4096, 14336),
+                                   (12, 300, 2112), (16, 4096, 4096), (31, 129, 1024),
+                                   (32, 1000, 4096), (40, 64, 512)])
 def test_q8_0_skinny_products_and_dots(m, n, k):
     import torch
     qs = _qs()
