@@ -224,8 +224,9 @@ int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
  * (src0 F16, src1 and dst F32; no INIT stage).
  *   src0: IEEE binary16 [N][K], 2-byte aligned.  src1: f32 [M][K], 4-byte
  *   aligned.  dst: f32, 4-byte aligned.  Any K >= 0.
- *   Precision: M = 1 (and any M whose operands are not 16-byte aligned or
- *   whose K is not a multiple of 8): fp32 FMA of src1 as given and the
+ *   Precision: M = 1, M = 2 where the dispatch table picks the narrow
+ *   kernel (4096 x 4096), and any M whose operands are not 16-byte aligned
+ *   or whose K is not a multiple of 8: fp32 FMA of src1 as given and the
  *   widened weights.  2 <= M <= 16, and up to 64 with at most 8192 weight
  *   rows: the same exact fp32 products on the fp32 matrix cores.  Both
  *   hold for every finite src1 in the fp32 range.  Larger M: src1 is
