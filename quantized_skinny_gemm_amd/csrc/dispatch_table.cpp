@@ -13,6 +13,8 @@
 // kernel of the nearer one in log M.  A missing file, a malformed line or a
 // variant the type has no kernel for leaves that shape to the built-in
 // rules.  MM_VERBOSE=1 prints the file read and every decision on stderr.
+// MM_NARROW_MAX_M and MM_SPLIT_K, read with the table, override the narrow
+// kernel's M range and the K split for experiments (plan.h).
 #include "plan.h"
 
 #include <dlfcn.h>
@@ -39,6 +41,8 @@ struct Entry {
 std::once_flag g_once;
 std::vector<Entry> g_table;
 bool g_verbose = false;
+int g_narrow_max_m = -1;   // MM_NARROW_MAX_M, -1 unset
+int g_split_k = -1;        // MM_SPLIT_K, -1 unset
 
 int type_of(const char* s) {
   if (!strcmp(s, "f32")) return MM_TYPE_F32;
@@ -66,9 +70,27 @@ std::string default_path() {
   return "dispatch_table.txt";
 }
 
+// A positive integer from the environment, or -1 (unset or not a number).
+int env_count(const char* name) {
+  const char* v = getenv(name);
+  if (!v || !v[0]) return -1;
+  char* end = nullptr;
+  const long x = strtol(v, &end, 10);
+  if (*end || x < 0 || x > (1 << 20)) {
+    if (g_verbose) fprintf(stderr, "[mm] %s=%s ignored\n", name, v);
+    return -1;
+  }
+  return (int)x;
+}
+
 void load() {
   const char* v = getenv("MM_VERBOSE");
   g_verbose = v && v[0] && strcmp(v, "0") != 0;
+  g_narrow_max_m = env_count("MM_NARROW_MAX_M");
+  g_split_k = env_count("MM_SPLIT_K");
+  if (g_split_k == 0) g_split_k = -1;
+  if (g_verbose && (g_narrow_max_m >= 0 || g_split_k > 0))
+    fprintf(stderr, "[mm] overrides: MM_NARROW_MAX_M %d, MM_SPLIT_K %d\n", g_narrow_max_m, g_split_k);
   const char* env = getenv("MM_DISPATCH_TABLE");
   const std::string path = env && env[0] ? std::string(env) : default_path();
   FILE* f = fopen(path.c_str(), "r");
@@ -102,6 +124,16 @@ void load() {
 }
 
 }  // namespace
+
+int env_narrow_max_m() {
+  std::call_once(g_once, load);
+  return g_narrow_max_m;
+}
+
+int env_split_k() {
+  std::call_once(g_once, load);
+  return g_split_k;
+}
 
 int dispatch_table_variant(int type, int64_t M, int64_t N, int64_t K) {
   std::call_once(g_once, load);

@@ -62,7 +62,10 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
   if (K == 0) { p->kind = KK_ZERO; return MM_OK; }
   if (variant == 0) {
-    const int tv = dispatch_table_variant(type, M, N, K);
+    int tv = dispatch_table_variant(type, M, N, K);
+    const int nm = env_narrow_max_m();
+    if (nm >= 0 && type == MM_TYPE_Q4_0)             // experiment override
+      tv = M <= nm ? 1 : (tv > 1 ? tv : (M <= kMmaMaxM ? 3 : 2));
     dispatch_log(type, M, N, K, tv, tv != 0);
     variant = tv;
   }
@@ -180,6 +183,10 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
         if (split > 16) split = 16;
         if (split < 1) split = 1;
       }
+      if (allow_split && env_split_k() > 0) {         // experiment override
+        const int64_t max_split = units / 64 > 1 ? units / 64 : 1;
+        split = env_split_k() < max_split ? env_split_k() : max_split;
+      }
       p->kchunk = ceil_div(units, split);
       p->split = (int)ceil_div(units, p->kchunk);
       // At most kNarrowMaxGrid workgroups along N, each walking an equal
@@ -264,6 +271,8 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
         if (split > 16) split = 16;
         if (split < 1) split = 1;
       }
+      if (allow_split && env_split_k() > 0)            // experiment override
+        split = env_split_k() < stages ? env_split_k() : stages;
       p->kchunk = ceil_div(stages, split) * kWideI8KB;   // blocks per split
       p->split = (int)ceil_div(nb, p->kchunk);
     }

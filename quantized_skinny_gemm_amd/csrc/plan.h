@@ -83,6 +83,13 @@ struct Plan {
 // (type, N, K) at this M, or 0 when the table has none (or no table was
 // found).  The file is read once per process.
 int dispatch_table_variant(int type, int64_t M, int64_t N, int64_t K);
+// Experiment overrides from the environment, read once per process with the
+// table; -1 when unset.  MM_NARROW_MAX_M: Q4_0 products with M up to this
+// value take the narrow kernel and larger ones never do (0: never).
+// MM_SPLIT_K: the K split of the narrow and wide kernels (clamped to what
+// the shape allows).
+int env_narrow_max_m();
+int env_split_k();
 // Logs a dispatch decision on stderr when MM_VERBOSE is set.
 void dispatch_log(int type, int64_t M, int64_t N, int64_t K, int variant, bool from_table);
 

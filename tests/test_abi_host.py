@@ -336,3 +336,51 @@ def test_q8_0_weights_host_rules():
     assert call(FAKE, FAKE + 2**30, FAKE + 2**31, 8, 256, 48, FAKE + 2**32, ws, None) == SHAPE
     assert call(None, FAKE + 2**30, FAKE + 2**31, 8, 256, 512, FAKE + 2**32, ws, None) == NULL
     assert qs.row_bytes(Q8, 4096) == 4096 // 32 * 34
+
+
+def _dispatch_in_subprocess(env, shapes):
+    """mm_dispatch for (type, M, N, K) shapes in a fresh process with `env`
+    set (the library reads its environment overrides once per process)."""
+    import json
+    import os
+    import subprocess
+    import sys
+    code = ("import json, sys, ctypes\n"
+            "import quantized_skinny_gemm_amd as qs\n"
+            "out = []\n"
+            "for t, m, n, k in json.loads(sys.argv[1]):\n"
+            "    d = (ctypes.c_int * 5)()\n"
+            "    st = qs.lib.mm_dispatch(t, m, n, k, d)\n"
+            "    out.append([st] + list(d))\n"
+            "print(json.dumps(out))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    e = dict(os.environ, **env)
+    r = subprocess.run([sys.executable, "-c", code, json.dumps(shapes)], capture_output=True,
+                       text=True, env=e, cwd=root, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def test_env_overrides_narrow_max_m_and_split_k():
+    """MM_NARROW_MAX_M moves the narrow kernel's M range for Q4_0 (0: never);
+    MM_SPLIT_K sets the K split of the narrow and wide kernels (clamped);
+    values that are not counts are ignored."""
+    Q4 = qs.MM_TYPE_Q4_0
+    shapes = [[Q4, 5, 4096, 4096], [Q4, 9, 4096, 4096], [Q4, 1, 4096, 4096], [Q4, 512, 14336, 4096]]
+    base = _dispatch_in_subprocess({}, shapes)
+    assert [r[1] for r in base] == [3, 3, 1, 2]
+    wide_split = base[3][2]
+    got = _dispatch_in_subprocess({"MM_NARROW_MAX_M": "8"}, shapes)
+    assert [r[1] for r in got] == [1, 3, 1, 2]
+    got = _dispatch_in_subprocess({"MM_NARROW_MAX_M": "0"}, shapes)
+    assert got[2][1] == 3                                # M = 1 off the narrow kernel
+    got = _dispatch_in_subprocess({"MM_SPLIT_K": "4", "MM_NARROW_MAX_M": "8"},
+                                  shapes + [[Q4, 5, 4096, 16384]])
+    assert got[0][1] == 1 and got[0][2] == 1             # K = 4096: one pair per lane, no split
+    assert got[4][1] == 1 and got[4][2] == 4             # narrow, split 4
+    assert got[3][1] == 2 and got[3][2] == 4             # wide, split 4
+    got = _dispatch_in_subprocess({"MM_SPLIT_K": "1000000"}, [[Q4, 512, 14336, 4096]])
+    assert got[0][2] == 4096 // 32 // 4                  # at most one split per stage
+    got = _dispatch_in_subprocess({"MM_SPLIT_K": "two", "MM_NARROW_MAX_M": "-3"}, shapes)
+    assert got == base
+    assert wide_split >= 1

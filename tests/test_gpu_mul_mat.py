@@ -552,3 +552,46 @@ def test_f_narrow_k_slices(m, n, k):
     assert_close(to_host(y), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, f"f16 narrow {m}x{n}x{k}")
     y, _ = qs.debug_mul_mat(qs.MM_TYPE_F32, to_dev(w), to_dev(x), 1)
     assert_close(to_host(y), mul_mat.mul_mat_f32(w, x), TOL_F, f"f32 narrow {m}x{n}x{k}")
+
+
+def test_env_overrides_products():
+    """Products planned under MM_NARROW_MAX_M and MM_SPLIT_K (a child
+    process: the library reads them once) against the oracle: the narrow
+    kernel at M = 5 with its K split 4 ways, the wide kernel split 4 ways."""
+    import json
+    import os
+    import subprocess
+    import sys
+    import tempfile
+    cases = [(5, 300, 16384), (128, 256, 2048)]
+    rng = np.random.default_rng(99)
+    with tempfile.TemporaryDirectory() as d:
+        ins = []
+        for i, (m, n, k) in enumerate(cases):
+            wq = codec.quantize_q4_0((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+            x = rng.standard_normal((m, k)).astype(np.float32)
+            np.save(os.path.join(d, f"w{i}.npy"), wq)
+            np.save(os.path.join(d, f"x{i}.npy"), x)
+            ins.append((wq, x))
+        code = ("import json, os, sys, numpy as np, torch\n"
+                "import quantized_skinny_gemm_amd as qs\n"
+                "d = sys.argv[1]\n"
+                "plans = []\n"
+                "for i in range(int(sys.argv[2])):\n"
+                "    w = torch.from_numpy(np.load(os.path.join(d, f'w{i}.npy'))).cuda()\n"
+                "    x = torch.from_numpy(np.load(os.path.join(d, f'x{i}.npy'))).cuda()\n"
+                "    y = qs.mul_mat_q4_0_f32(w, x)\n"
+                "    np.save(os.path.join(d, f'y{i}.npy'), y.cpu().numpy())\n"
+                "    plans.append(list(qs.dispatch(qs.MM_TYPE_Q4_0, x.shape[0], w.shape[0], x.shape[1])))\n"
+                "print(json.dumps(plans))\n")
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        env = dict(os.environ, MM_NARROW_MAX_M="8", MM_SPLIT_K="4")
+        say("env overrides child")
+        r = subprocess.run([sys.executable, "-c", code, d, str(len(cases))], capture_output=True,
+                           text=True, env=env, cwd=root, timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        plans = json.loads(r.stdout.strip().splitlines()[-1])
+        assert plans[0][:2] == [1, 4] and plans[1][:2] == [2, 4], plans
+        for i, (wq, x) in enumerate(ins):
+            y = np.load(os.path.join(d, f"y{i}.npy"))
+            assert_close(y, mul_mat.mul_mat_q4_0_f32(wq, x), TOL_Q4_0, f"override case {i}")
