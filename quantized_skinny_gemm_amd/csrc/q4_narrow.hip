@@ -46,7 +46,24 @@ struct ActView {
   int64_t dpitch;       // entries between rows of scales / bias
   int boff;             // first block held
   int rows;             // valid rows (>= 1)
+  bool swz;             // codes in LDS, chunks swizzled (act_chunk); rows of
+                        // whole block pairs only
 };
+
+// Byte offset of 16-byte code chunk h (0, 1) of block bl within a row of
+// activation codes in LDS.  A lane reads its K unit (two blocks, 64 bytes)
+// at a 64-byte stride from its neighbours; with the chunks in place every
+// 16-byte read of a wave would land four lanes on the same banks.  The
+// chunk's slot within its 64-byte unit is therefore XORed with bits 1-4 of
+// the unit index, which puts any 8 or 16 consecutive units' reads of one
+// chunk on distinct banks (32- or 64-bank LDS).  Writers and readers both go
+// through this function; code in global memory is not swizzled, and neither
+// are rows of an odd number of blocks (a last, unpaired block would be moved
+// into the next row's first).
+__device__ __forceinline__ int act_chunk(int bl, int h, bool swz) {
+  const int x = swz ? (((bl >> 2) ^ (bl >> 4)) & 3) << 4 : 0;
+  return (bl * 32 + 16 * h) ^ x;
+}
 
 // kMask: lanes with !valid hold a clamped (valid) unit whose contribution
 // is dropped; they still compute, so every loaded register is consumed on
@@ -68,8 +85,9 @@ __device__ __forceinline__ void block_mac(const uint32_t (&q)[R][4], const float
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int mm = m < av.rows ? m : av.rows - 1;
-    const v4i* ap = reinterpret_cast<const v4i*>(av.q + mm * av.qpitch + (int64_t)bl * 32);
-    const v4i a0 = ap[0], a1 = ap[1];
+    const int8_t* ar = av.q + mm * av.qpitch;
+    const v4i a0 = *reinterpret_cast<const v4i*>(ar + act_chunk(bl, 0, av.swz));
+    const v4i a1 = *reinterpret_cast<const v4i*>(ar + act_chunk(bl, 1, av.swz));
     const float da = av.d[mm * av.dpitch + bl];
     const int bias = av.bias[mm * av.dpitch + bl];
 #pragma unroll
@@ -189,8 +207,9 @@ __device__ __forceinline__ void unit_mac8(const uint32_t (&wv)[R][17], int64_t u
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int mm = m < av.rows ? m : av.rows - 1;
-      const v4i* ap = reinterpret_cast<const v4i*>(av.q + mm * av.qpitch + (int64_t)bl * 32);
-      const v4i a0 = ap[0], a1 = ap[1];
+      const int8_t* ar = av.q + mm * av.qpitch;
+      const v4i a0 = *reinterpret_cast<const v4i*>(ar + act_chunk(bl, 0, av.swz));
+      const v4i a1 = *reinterpret_cast<const v4i*>(ar + act_chunk(bl, 1, av.swz));
       const float da = av.d[mm * av.dpitch + bl];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -250,7 +269,7 @@ __device__ __forceinline__ void quant_load(const Slice& sl, const float* __restr
   }
 }
 
-template <int NT, int kBatch, int MT>
+template <int NT, int kBatch, int MT, bool kSwz>
 __device__ __forceinline__ void quant_store(const Slice& sl, int it0, int rounds,
                                             float (&v)[kBatch][16], const bool (&ok)[kBatch],
                                             int8_t* sq, float* sd, int32_t* sb) {
@@ -271,7 +290,7 @@ __device__ __forceinline__ void quant_store(const Slice& sl, int it0, int rounds
     int sum;
     q8_0_pair(v[j], packed, dbits, sum);
     if (ok[j]) {
-      *reinterpret_cast<uint4*>(sq + (int64_t)m * sl.kbmax * 32 + bl * 32 + 16 * h) =
+      *reinterpret_cast<uint4*>(sq + (int64_t)m * sl.kbmax * 32 + act_chunk(bl, h, kSwz)) =
           make_uint4(packed[0], packed[1], packed[2], packed[3]);
       if (h == 0) {
         sd[m * sl.kbmax + bl] = f16_bits_to_f32(dbits);
@@ -301,7 +320,7 @@ __device__ __forceinline__ void copy_load(const Slice& sl, const Q4Args& a, int 
   }
 }
 
-template <int NT, int kBatch, int MT>
+template <int NT, int kBatch, int MT, bool kSwz>
 __device__ __forceinline__ void copy_store(const Slice& sl, int it0, const v4i (&c)[kBatch],
                                            const float (&d)[kBatch], const int (&bi)[kBatch],
                                            const bool (&ok)[kBatch], int8_t* sq, float* sd,
@@ -313,7 +332,7 @@ __device__ __forceinline__ void copy_store(const Slice& sl, int it0, const v4i (
     split_blk<MT>(i >> 1, sl.kbmax, m, bl);
     const int cc = 2 * bl + (i & 1);
     if (ok[j]) {
-      *reinterpret_cast<v4i*>(sq + (int64_t)m * sl.kbmax * 32 + bl * 32 + (cc & 1) * 16) = c[j];
+      *reinterpret_cast<v4i*>(sq + (int64_t)m * sl.kbmax * 32 + act_chunk(bl, cc & 1, kSwz)) = c[j];
       if ((cc & 1) == 0) {
         sd[m * sl.kbmax + bl] = d[j];
         sb[m * sl.kbmax + bl] = bi[j];
@@ -413,13 +432,13 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
       bool ok[kBatch];
       quant_load<NT, kBatch, MT>(sl, x, 0, rounds, v, ok);
       load_unit<R, kPairs>(wv, rp, ufirst);          // after the slice's loads
-      quant_store<NT, kBatch, MT>(sl, 0, rounds, v, ok, sq, sd, sb);
+      quant_store<NT, kBatch, MT, kPairs>(sl, 0, rounds, v, ok, sq, sd, sb);
     }
     for (int it0 = kBatch; it0 < rounds; it0 += kBatch) {
       float v[kBatch][16];
       bool ok[kBatch];
       quant_load<NT, kBatch, MT>(sl, x, it0, rounds, v, ok);
-      quant_store<NT, kBatch, MT>(sl, it0, rounds, v, ok, sq, sd, sb);
+      quant_store<NT, kBatch, MT, kPairs>(sl, it0, rounds, v, ok, sq, sd, sb);
     }
     lds_barrier();
   } else if (kAct == kActCopy) {
@@ -434,7 +453,7 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
       bool ok[kBatch];
       copy_load<NT, kBatch, MT>(sl, a, 0, rounds, c, d, bi, ok);
       load_unit<R, kPairs>(wv, rp, ufirst);          // after the slice's loads
-      copy_store<NT, kBatch, MT>(sl, 0, c, d, bi, ok, sq, sd, sb);
+      copy_store<NT, kBatch, MT, kPairs>(sl, 0, c, d, bi, ok, sq, sd, sb);
     }
     for (int it0 = kBatch; it0 < rounds; it0 += kBatch) {
       v4i c[kBatch];
@@ -442,7 +461,7 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
       int bi[kBatch];
       bool ok[kBatch];
       copy_load<NT, kBatch, MT>(sl, a, it0, rounds, c, d, bi, ok);
-      copy_store<NT, kBatch, MT>(sl, it0, c, d, bi, ok, sq, sd, sb);
+      copy_store<NT, kBatch, MT, kPairs>(sl, it0, c, d, bi, ok, sq, sd, sb);
     }
     lds_barrier();
   } else {
@@ -453,10 +472,10 @@ void k_q4_narrow(Q4Args a, Q4Mats mats, const float* __restrict__ x, int64_t kch
     av.q = a.aq + (int64_t)m0 * K;
     av.d = a.ad + (int64_t)m0 * nb;
     av.bias = a.ab + (int64_t)m0 * nb;
-    av.qpitch = K; av.dpitch = nb; av.boff = 0;
+    av.qpitch = K; av.dpitch = nb; av.boff = 0; av.swz = false;
   } else {
     av.q = sq; av.d = sd; av.bias = sb;
-    av.qpitch = (int64_t)kbmax * 32; av.dpitch = kbmax; av.boff = b0;
+    av.qpitch = (int64_t)kbmax * 32; av.dpitch = kbmax; av.boff = b0; av.swz = kPairs;
   }
 
   float acc[R][MT];
@@ -643,17 +662,17 @@ void k_q4_fused(const float* __restrict__ x, const uint8_t* w0, const uint8_t* w
   }
   // the first weights are in flight before src1 is waited for
   __builtin_amdgcn_sched_barrier(0);
-  quant_store<NT, NR, MT>(sl, 0, rounds, v, ok, sq, sd, sb);
+  quant_store<NT, NR, MT, true>(sl, 0, rounds, v, ok, sq, sd, sb);
   for (int it0 = NR; it0 < rounds; it0 += NR) {
     quant_load<NT, NR, MT>(sl, x, it0, rounds, v, ok);
-    quant_store<NT, NR, MT>(sl, it0, rounds, v, ok, sq, sd, sb);
+    quant_store<NT, NR, MT, true>(sl, it0, rounds, v, ok, sq, sd, sb);
   }
   if (!kMany) asm volatile("" ::"s"(d0), "s"(d1), "s"(d2));
   lds_barrier();
 
   ActView av;
   av.q = sq; av.d = sd; av.bias = sb;
-  av.qpitch = (int64_t)nb * 32; av.dpitch = nb; av.boff = 0; av.rows = rows;
+  av.qpitch = (int64_t)nb * 32; av.dpitch = nb; av.boff = 0; av.rows = rows; av.swz = true;
   float acc[R][MT];
 #pragma unroll
   for (int r = 0; r < R; ++r)
