@@ -29,13 +29,15 @@
 //     operand (the Q8_0 codes of src1 row l % 16) holds the same elements.
 //     Nibbles become signed bytes 16 * (q - 8) with a shift and two masked
 //     xors ((q ^ 8) << 4 read as a signed byte is 16 (q - 8)), so the MFMA
-//     ends at 16 S_b exactly and no bias term is needed; the 1/16 joins the
-//     activation scale (exact: a power of two).
+//     ends at 16 S_b exactly and no bias term is needed; every output is
+//     multiplied by 1/16 once, when it is stored (exact: a power of two, and
+//     the scaled partial sums round exactly as the unscaled ones would).
 //   * Output lane l holds src1 row l % 16 and weight rows 4 (l / 16) + r.
-//     The scale of each output, d_w[row] * d_a[col] / 16, comes from a
-//     second MFMA (an outer product on the fp32 matrix cores), already in
-//     the result layout; the epilogue per output and block is a convert and
-//     an fma: acc += f32(16 S_b) * (d_w * d_a / 16).
+//     The scale of each output, d_w[row] * d_a[col], comes from a second
+//     MFMA (an outer product on the fp16 matrix cores: both scales are
+//     binary16 values, so each product is exact in fp32), already in the
+//     result layout; the epilogue per output and block is a convert and an
+//     fma: acc += f32(16 S_b) * (d_w * d_a).
 //   * M <= 8 (k_q4_skinny8): v_mfma_i32_16x16x64_i8 takes two blocks at once,
 //     its 16 columns being 8 src1 rows x the pair's two blocks (the B operand
 //     of column (m, e) is zero outside block e), which halves the MFMAs, the
@@ -135,13 +137,21 @@ __device__ __forceinline__ long nibbles_x16(uint32_t q) {
 }
 
 // The 16 x 16 tile of scale products d_w[row] * d_a[col] in the layout of
-// the MFMA results: an outer product on the fp32 matrix cores (K = 4; the
-// B operand is zero outside k = 0, so each product is rounded once), in
-// place of four multiplies per lane and of a trip through LDS to bring each
-// lane the weight scales of its rows.  Every lane passes its row's weight
-// scale (finite), and only lanes 0-15 a non-zero activation scale.
+// the MFMA results: an outer product on the fp16 matrix cores
+// (v_mfma_f32_16x16x16_f16; lane l supplies k = 4 (l / 16) .. +3 of row or
+// column l % 16, and only k = 4 (l / 16) is set here), in place of four
+// multiplies per lane and of a trip through LDS to bring each lane the
+// weight scales of its rows.  Both scales are binary16 values held widened
+// in fp32: narrowing them back is exact, each product is exact in fp32 and
+// the sum over k adds zeros.  Every lane passes its row's weight scale
+// (finite), and only the lanes of one k group a non-zero activation scale.
+// (Keeping them in fp32 until here costs a convert each, but keeps each
+// scale in one register: operands built from the bits need a zero register
+// beside every scale, which cost the 32-row kernel a wave per SIMD.)
 __device__ __forceinline__ v4f scale_tile(float dw_row, float da_col) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(dw_row, da_col, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+  const v4h A = {(_Float16)dw_row, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+  const v4h B = {(_Float16)da_col, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(A, B, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 }
 
 template <int MP, int RT, bool kDump, bool kQ8>
@@ -173,12 +183,12 @@ __device__ __forceinline__ void compute_phase(const Phase<MP, RT, kQ8>& P, float
       if constexpr (kQ8) {
         // elements 4g .. 4g+3 and 16+4g .. 19+4g of each block: code dwords g
         // and 4 + g (even block: bytes from 2, shifted by 16 bits; odd block:
-        // dword aligned from dword 9); the MFMA yields S_b, so 16 d_w
+        // dword aligned from dword 9); the MFMA yields S_b
         auto c0 = [&](int q) { return (uint64_t)__builtin_amdgcn_alignbit(u[q + 1], u[q], 16); };
         A[rt][0] = (long)(c0(g) | (c0(4 + g) << 32));
         A[rt][1] = (long)((uint64_t)u[9 + g] | ((uint64_t)u[13 + g] << 32));
-        dw[rt][0] = 16.0f * f16_bits_to_f32(u[0] & 0xFFFFu);
-        dw[rt][1] = 16.0f * f16_bits_to_f32(u[8] >> 16);
+        dw[rt][0] = f16_bits_to_f32(u[0] & 0xFFFFu);
+        dw[rt][1] = f16_bits_to_f32(u[8] >> 16);
       } else {
         A[rt][0] = nibbles_x16(__builtin_amdgcn_alignbit(u[g + 1], u[g], 16));   // even block
         A[rt][1] = nibbles_x16(u[5 + g]);                                       // odd block
@@ -197,8 +207,7 @@ __device__ __forceinline__ void compute_phase(const Phase<MP, RT, kQ8>& P, float
           const long B = h ? (long)(((uint64_t)(uint32_t)ac.w << 32) | (uint32_t)ac.z)
                            : (long)(((uint64_t)(uint32_t)ac.y << 32) | (uint32_t)ac.x);
           const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt][h], B, v4i{0, 0, 0, 0}, 0, 0, 0);
-          // d_w * d_a / 16 (INIT stores d_a / 16: the MFMA gives 16 S_b)
-          const v4f sc = scale_tile(dw[rt][h], P.da[t][kb]);
+          const v4f sc = scale_tile(dw[rt][h], P.da[t][kb]);   // d_w * d_a
           acc[rt][t][0] = fmaf((float)D.x, sc.x, acc[rt][t][0]);
           acc[rt][t][1] = fmaf((float)D.y, sc.y, acc[rt][t][1]);
           acc[rt][t][2] = fmaf((float)D.z, sc.z, acc[rt][t][2]);
@@ -297,7 +306,7 @@ void k_q4_skinny(Q4Args a, int pp) {
     for (int w2 = 0; w2 < W; ++w2) s += red[((w2 * NT + tt) * 4 + r) * 64 + l];
     const int m = m0 + 16 * t + (l & 15);
     const int n = n0 + 16 * rt + 4 * (l >> 4) + r;
-    if (m < a.M && n < a.N) a.dst[(int64_t)m * a.N + n] = s;
+    if (m < a.M && n < a.N) a.dst[(int64_t)m * a.N + n] = kQ8 ? s : s * 0.0625f;   // 16 S_b
   }
 }
 
@@ -341,8 +350,7 @@ hipError_t launch_mp(const Plan& p, const Q4Args& a, hipStream_t s) {
 // scale in the low half of dword 0 and its codes from byte 2 (dwords shifted
 // by 16 bits), block 1's scale in the high half of dword 8 and its codes
 // dword-aligned from dword 9.  The codes are the A operand as stored (the
-// MFMA gives S_b, not 16 S_b), so the weight scale enters the scale product
-// as 16 d_w (exact) against the stored d_a / 16.
+// MFMA gives S_b, not 16 S_b), so its outputs take no factor 1/16.
 template <bool kQ8>
 struct Unit8 {
   static constexpr int kDwords = kQ8 ? 17 : 9;          // dwords per block pair
@@ -354,7 +362,7 @@ template <bool kQ8>
 struct Phase8 {
   uint32_t w[Unit8<kQ8>::kDwords];
   v4i act[kPH];
-  v4i da;                     // d_a / 16 of pair j's block for this column (zero elsewhere)
+  v4i da;                     // d_a (fp32 bits) of pair j's block, this column (lanes of group e)
 };
 
 template <bool kQ8>
@@ -402,8 +410,9 @@ __device__ __forceinline__ void compute_phase8(const Phase8<kQ8>& P, float (&acc
   const int sh = kQ8 ? ((g >> 1) ? 0 : 16) : (g < 2 ? 16 : 0);
   const int s2 = 2 * (g & 1);
   // Weight scale of block g & 1 (Q4_0 unit bytes 0-1 or 18-19; Q8_0 bytes
-  // 0-1 or 34-35): the scale MFMA's k = g; for g = 2, 3 the B operand is
-  // zero there, any finite value works.
+  // 0-1 or 34-35): the scale MFMA's k = 4 g, where the B operand of column
+  // (m, e) holds d_a for g = e only; for g = 2, 3 the B operand is zero
+  // there, any finite value works.
   const int ds = kQ8 ? ((g & 1) ? 8 : 0) : ((g & 1) ? 4 : 0), dsh = (g & 1) * 16;
   const int nb = a.K / 32;
 #pragma unroll
@@ -417,7 +426,7 @@ __device__ __forceinline__ void compute_phase8(const Phase8<kQ8>& P, float (&acc
       // row's pad: unused, the shift is 0)
       auto cd = [&](int q) { return (int)__builtin_amdgcn_alignbit(u[b + q + 1], u[b + q], sh); };
       A = v4i{cd(s2), cd(4 + s2), cd(s2 + 1), cd(5 + s2)};
-      dw = 16.0f * f16_bits_to_f32((u[ds] >> dsh) & 0xFFFFu);
+      dw = f16_bits_to_f32((u[ds] >> dsh) & 0xFFFFu);
     } else {
       const uint32_t x0 = u[b], x1 = u[b + 1], x2 = u[b + 2];
       const long A0 = nibbles_x16(__builtin_amdgcn_alignbit(x1, x0, sh));
@@ -427,7 +436,7 @@ __device__ __forceinline__ void compute_phase8(const Phase8<kQ8>& P, float (&acc
       dw = f16_bits_to_f32((u[ds] >> dsh) & 0xFFFFu);
     }
     const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, P.act[jj], v4i{0, 0, 0, 0}, 0, 0, 0);
-    const v4f sc = __builtin_amdgcn_mfma_f32_16x16x4f32(dw, __int_as_float(P.da[jj]), v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    const v4f sc = scale_tile(dw, __int_as_float(P.da[jj]));
     acc[0] = fmaf((float)D.x, sc.x, acc[0]);
     acc[1] = fmaf((float)D.y, sc.y, acc[1]);
     acc[2] = fmaf((float)D.z, sc.z, acc[2]);
@@ -497,7 +506,7 @@ void k_q4_skinny8(Q4Args a, int pp) {
     float s = 0.0f;
     for (int w2 = 0; w2 < W; ++w2) s += red[(w2 * 4 + r) * 64 + l] + red[(w2 * 4 + r) * 64 + l + 8];
     const int n = n0 + 4 * gq + r;
-    if (m0 + m < a.M && n < a.N) a.dst[(int64_t)(m0 + m) * a.N + n] = s;
+    if (m0 + m < a.M && n < a.N) a.dst[(int64_t)(m0 + m) * a.N + n] = kQ8 ? s : s * 0.0625f;
   }
 }
 
@@ -680,7 +689,7 @@ void k_q4r_skinny(Q4Args a, int pp) {
     for (int w2 = 0; w2 < W; ++w2) s += red[((w2 * NT + tt) * 4 + r) * 64 + l];
     const int m = m0 + 16 * t + (l & 15);
     const int n = n0 + 16 * rt + 4 * (l >> 4) + r;
-    if (m < a.M && n < a.N) a.dst[(int64_t)m * a.N + n] = s;
+    if (m < a.M && n < a.N) a.dst[(int64_t)m * a.N + n] = s * 0.0625f;   // 16 S_b
   }
 }
 

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q8_0_skinny(
     // group 2 e + s loads slot 2 c + s (16 bytes) of the pair's 512: elements
     // 8s .. 8s+3, 16+8s .. 19+8s, 8s+4 .. 8s+7, 20+8s .. 23+8s, i.e. this
     // thread's code dword qd (elements 16 h + 4 qd ..) goes to slot
-    // 2 c + qd / 2, dword 2 (qd % 2) + h.  Scales: d_a / 16 at (c, j).
+    // 2 c + qd / 2, dword 2 (qd % 2) + h.  Scales: d_a at (c, j).
     const int t = m >> 3, i = m & 7;
     const int f = b >> 3, kb = b & 7, j = kb >> 1, e = kb & 1;
     const int c = 8 * e + i;
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q8_0_skinny(
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd)
       *reinterpret_cast<uint32_t*>(base + 16 * (2 * c + (qd >> 1)) + 4 * (2 * (qd & 1) + h)) = packed[qd];
-    if (h == 0) ss[(((int64_t)t * phases + f) * 16 + c) * 4 + j] = f16_bits_to_f32(dbits) * 0.0625f;
+    if (h == 0) ss[(((int64_t)t * phases + f) * 16 + c) * 4 + j] = f16_bits_to_f32(dbits);
     return;
   }
   const int t = m >> 4, i = m & 15;
@@ -180,8 +180,9 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q8_0_skinny(
   uint8_t* base = sq + (((int64_t)t * phases + f) * 4 + j) * 1024 + 8 * e + 4 * h;
 #pragma unroll
   for (int g = 0; g < 4; ++g) *reinterpret_cast<uint32_t*>(base + 16 * (16 * g + i)) = packed[g];
-  // d_a / 16 (exact): the skinny kernel's MFMA yields 16 S_b
-  if (h == 0) ss[(((int64_t)t * phases + f) * 16 + i) * 8 + kb] = f16_bits_to_f32(dbits) * 0.0625f;
+  // d_a, widened (the kernel narrows it back to binary16 for its fp16 scale
+  // product, exactly)
+  if (h == 0) ss[(((int64_t)t * phases + f) * 16 + i) * 8 + kb] = f16_bits_to_f32(dbits);
 }
 
 int64_t grid_for(int64_t nblocks, int lanes) { return (nblocks * lanes + kThreads - 1) / kThreads; }

@@ -324,19 +324,23 @@ def test_empty_and_zero_k():
 
 
 def test_zero_blocks_and_extremes():
+    # zero rows and blocks, weight scales near the binary16 top, and a src1
+    # row whose Q8_0 scales are binary16 subnormals; every kernel family
+    # (narrow, wide, and the skinny kernels of 8-, 16- and 32-row passes)
     rng = np.random.default_rng(10)
-    n, k, m = 64, 512, 6
+    n, k = 64, 512
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     w[3] = 0.0
     w[5, :64] = 0.0
     w[7] *= 1e4
-    x = rng.standard_normal((m, k)).astype(np.float32)
-    x[1] = 0.0
-    x[2, 32:96] = 0.0
-    x[4] *= 1e-5
     wq = codec.quantize_q4_0(w)
-    for v in (1, 2):
-        _check_q4_product(to_dev(wq), wq, x, "zeros/extremes", v, (0, n))
+    for m in (6, 12, 20):
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        x[1] = 0.0
+        x[2, 32:96] = 0.0
+        x[4] *= 1e-5
+        for v in (1, 2, 3):
+            _check_q4_product(to_dev(wq), wq, x, f"zeros/extremes M={m}", v, (0, n))
 
 
 def test_deterministic_run_to_run():
