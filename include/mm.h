@@ -224,19 +224,22 @@ int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
  * (src0 F16, src1 and dst F32; no INIT stage).
  *   src0: IEEE binary16 [N][K], 2-byte aligned.  src1: f32 [M][K], 4-byte
  *   aligned.  dst: f32, 4-byte aligned.  Any K >= 0.
- *   Precision: M = 1, M = 2 where the dispatch table picks the narrow
- *   kernel (4096 x 4096), and any M whose operands are not 16-byte aligned
- *   or whose K is not a multiple of 8: fp32 FMA of src1 as given and the
- *   widened weights.  2 <= M <= 16, and up to 64 with at most 8192 weight
- *   rows: the same exact fp32 products on the fp32 matrix cores.  Both
- *   hold for every finite src1 in the fp32 range.  Larger M: src1 is
- *   rounded to binary16 for the fp16 matrix cores after scaling each row
- *   by a power of two that puts its largest magnitude in [2^14, 2^15)
- *   (undone exactly on the outputs), so every row keeps 11 significant bits
- *   whatever its magnitude (row-normwise effect about 1e-4; only elements
- *   below 2^-28 of their row's largest magnitude lose bits, a contribution
- *   far under the bound).  All inside the 1e-3 row-normwise bound of this
- *   kind.
+ *   Precision follows the kernel mm_dispatch reports for the shape.
+ *   Narrow kernel (M = 1, and small M where the dispatch table picks it;
+ *   any M whose operands are not 16-byte aligned or whose K is not a
+ *   multiple of 8): fp32 FMA of src1 as given and the widened weights.
+ *   Skinny kernel (built-in rules: 2 <= M <= 16, and up to 64 with at most
+ *   8192 weight rows; the measured table gives it, e.g., 4096 x 4096 up to
+ *   45 rows): the same exact fp32 products on the fp32 matrix cores.  Both
+ *   hold for every finite src1 in the fp32 range.  Wide kernel (larger M,
+ *   and on the shapes where the table measured it faster, e.g. 14336 x 4096
+ *   from M = 3): src1 is rounded to binary16 for the fp16 matrix cores after
+ *   scaling each row by a power of two that puts its largest magnitude in
+ *   [2^14, 2^15) (undone exactly on the outputs), so every row keeps 11
+ *   significant bits whatever its magnitude (row-normwise effect about
+ *   1e-4; only elements below 2^-28 of their row's largest magnitude lose
+ *   bits, a contribution far under the bound).  All inside the 1e-3
+ *   row-normwise bound of this kind.
  *   ws: mm_mul_mat_workspace_size(MM_TYPE_F16, ...) bytes (0 when that is
  *   0); for the larger M it holds src1 as binary16 and the row exponents.
  */

@@ -27,6 +27,8 @@
 // bf16 is avoided: the pages note that at small sizes converting operands to
 // bf16 costs more than it gains (smallbard "Generer a plusieurs"), and its
 // 8-bit mantissa would also sit too close to the 1e-3 accuracy bound.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 #include "../../include/mm.h"
@@ -395,7 +397,16 @@ __global__ __launch_bounds__(256) void k_f32_to_f16_rows(const float* __restrict
 // barriers per MFMA: M = 512, 4096 x 4096 61.4 -> 45.6 us; M = 64,
 // 14336 x 4096 61.6 -> 45.0 us; 128 x 128 at 14336 / 128256 rows gains
 // nothing from it).
-template <int BM, int BN, bool kVec, int KS>
+// NS: stages whose global loads are in flight in registers.  The 64 x 64
+// tile serves grids of about one workgroup per CU or fewer, where nothing
+// else hides a stage's load latency: with NS = 3 the loads of stage k + 3
+// are issued when stage k goes to LDS (us per call, M = 64: 4096 x 4096
+// 42.4 -> 27.9, 14336 x 4096 47.4 -> 35.6, 4096 x 14336 134.0 -> 81.3; the
+// same within 3% from two workgroups per CU up).  The 128 x 128 tile keeps
+// NS = 1: its second set would take it to 190 VGPRs, two waves per SIMD,
+// and it is slower where its grids fill the device (128256 x 4096, M = 512:
+// 708 -> 779-789 us with NS = 2).
+template <int BM, int BN, bool kVec, int KS, int NS>
 __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w,
                                                   const uint16_t* __restrict__ xh,
                                                   const int* __restrict__ rexp,
@@ -426,7 +437,7 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
   // outside the matrices is zeroed when the registers go to LDS.
   constexpr int XI = BM * (KS / 8) / 256, WI = BN * (KS / 8) / 256;
   static_assert(XI * 256 == BM * (KS / 8) && WI * 256 == BN * (KS / 8), "whole items per thread");
-  uint4 xr[XI], wr[WI];
+  uint4 xr[NS][XI], wr[NS][WI];
   auto load8 = [&](const uint16_t* base, int row, int k) -> uint4 {
     if (kVec) {
       const int kk = k < K ? k : 0;                  // K % 8 == 0: k < K means k + 8 <= K
@@ -453,41 +464,39 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
     }
     return make_uint4(d[0], d[1], d[2], d[3]);
   };
-  auto load = [&](int k0) {
+  // register set S (a std::integral_constant: registers are not indexed at
+  // run time)
+  auto load = [&](auto set, int k0) {
+    constexpr int S = decltype(set)::value;
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
       const int i = tid + 256 * u;
       const int r = i / (KS / 8), c = i % (KS / 8);
-      xr[u] = load8(xh, m0 + r < M ? m0 + r : M - 1, k0 + 8 * c);
+      xr[S][u] = load8(xh, m0 + r < M ? m0 + r : M - 1, k0 + 8 * c);
     }
 #pragma unroll
     for (int u = 0; u < WI; ++u) {
       const int i = tid + 256 * u;
       const int r = i / (KS / 8), c = i % (KS / 8);
-      wr[u] = load8(w, n0 + r < N ? n0 + r : N - 1, k0 + 8 * c);
+      wr[S][u] = load8(w, n0 + r < N ? n0 + r : N - 1, k0 + 8 * c);
     }
   };
-  auto store = [&](int k0) {
+  auto store = [&](auto set, int k0) {
+    constexpr int S = decltype(set)::value;
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
       const int i = tid + 256 * u;
       const int r = i / (KS / 8), c = i % (KS / 8);
-      *reinterpret_cast<uint4*>(sA + r * HP + 8 * c) = mask8(xr[u], m0 + r < M, k0 + 8 * c);
+      *reinterpret_cast<uint4*>(sA + r * HP + 8 * c) = mask8(xr[S][u], m0 + r < M, k0 + 8 * c);
     }
 #pragma unroll
     for (int u = 0; u < WI; ++u) {
       const int i = tid + 256 * u;
       const int r = i / (KS / 8), c = i % (KS / 8);
-      *reinterpret_cast<uint4*>(sB + r * HP + 8 * c) = mask8(wr[u], n0 + r < N, k0 + 8 * c);
+      *reinterpret_cast<uint4*>(sB + r * HP + 8 * c) = mask8(wr[S][u], n0 + r < N, k0 + 8 * c);
     }
   };
-
-  load(0);
-  for (int k0 = 0; k0 < K; k0 += KS) {
-    __syncthreads();                                 // the last stage's MFMAs are done
-    store(k0);
-    __syncthreads();
-    if (k0 + KS < K) load(k0 + KS);                  // uniform over the workgroup
+  auto compute = [&]() {
 #pragma unroll
     for (int s = 0; s < KS / 16; ++s) {
       v8h A[WM], B[WN];
@@ -502,6 +511,51 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
 #pragma unroll
         for (int j = 0; j < WN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  static_assert(NS >= 1 && NS <= 3, "one to three register sets");
+
+  if constexpr (NS == 1) {
+    load(I0{}, 0);
+    for (int k0 = 0; k0 < K; k0 += KS) {
+      __syncthreads();                               // the last stage's MFMAs are done
+      store(I0{}, k0);
+      __syncthreads();
+      if (k0 + KS < K) load(I0{}, k0 + KS);          // uniform over the workgroup
+      compute();
+    }
+  } else {
+    // Stage k comes from set k % NS, whose loads for stage k + NS are issued
+    // once stage k is in LDS.  Loads are unconditional (addresses past K are
+    // clamped, the data unused) and kept in issue order by scheduling
+    // barriers: the same loads are in flight on every path, so the wait
+    // before a stage's store leaves the other sets' loads in flight.
+    load(I0{}, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(I1{}, KS);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NS > 2) {
+      load(I2{}, 2 * KS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    auto step = [&](auto set, int kk) {
+      const bool live = kk < K;                      // uniform
+      if (live) {
+        __syncthreads();                             // the last stage's MFMAs are done
+        store(set, kk);
+        __syncthreads();
+      }
+      load(set, kk + NS * KS);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) compute();
+    };
+    for (int k0 = 0; k0 < K; k0 += NS * KS) {
+      step(I0{}, k0);
+      step(I1{}, k0 + KS);
+      if constexpr (NS > 2) step(I2{}, k0 + 2 * KS);
     }
   }
 #pragma unroll
@@ -564,11 +618,11 @@ hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, flo
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
   if (p.bm == 128) {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true, 64>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<128, 128, false, 64>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true, 64, 1>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<128, 128, false, 64, 1>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
   } else {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true, 128>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<64, 64, false, 128>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true, 128, 3>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
+    else hipLaunchKernelGGL((k_f16_wide<64, 64, false, 128, 1>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
   }
   return hipGetLastError();
 }
