@@ -32,7 +32,8 @@ struct Q4Args {
   const float* ad;       // wdata scales
   const int32_t* ab;     // wdata -8*sum(q)
   const uint8_t* sq;     // skinny kernel: codes in operand order (NULL otherwise)
-  const float* ss;       // skinny kernel: d_a (binary16 values) in operand order
+  const float* ss;       // skinny kernel: d_a in operand order (16-row tiles: binary16
+                         // bits, 8 blocks in 16 bytes per row and phase; 8-row: fp32)
   int sk_phases;         // skinny kernel: phases of 8 blocks per row
   int sq_bytes, ss_bytes; // skinny kernel: sizes of those two ranges
   float* dst;

@@ -66,7 +66,7 @@ template <int MP, int RT, bool kQ8 = false>
 struct Phase {
   uint32_t w[RT][kQ8 ? 17 : 9];  // this lane's units: one row's block pair per row tile
   v4i act[MP][kPH];           // B operands of pair j: blocks 2j and 2j+1
-  float da[MP][2 * kPH];      // activation scale per m tile and block
+  v4i da[MP];                 // d_a (binary16) of the phase's 8 blocks, lanes 0-15
 };
 
 __device__ __forceinline__ uint32_t gload32(const void* p) {
@@ -120,12 +120,7 @@ __device__ __forceinline__ void load_phase(Phase<MP, RT, kQ8>& P, const Q4Args& 
 #pragma unroll
     for (int j = 0; j < kPH; ++j) P.act[t][j] = bload128(rq, rv ? qo + 1024 * j : kSkip);
     const bool sv = rv && lane < 16;
-    const v4i s0 = bload128(rs, sv ? (tp * 16 + lane) * 32 : kSkip);
-    const v4i s1 = bload128(rs, sv ? (tp * 16 + lane) * 32 + 16 : kSkip);
-    P.da[t][0] = __int_as_float(s0[0]); P.da[t][1] = __int_as_float(s0[1]);
-    P.da[t][2] = __int_as_float(s0[2]); P.da[t][3] = __int_as_float(s0[3]);
-    P.da[t][4] = __int_as_float(s1[0]); P.da[t][5] = __int_as_float(s1[1]);
-    P.da[t][6] = __int_as_float(s1[2]); P.da[t][7] = __int_as_float(s1[3]);
+    P.da[t] = bload128(rs, sv ? (tp * 16 + lane) * 16 : kSkip);
   }
 }
 
@@ -154,6 +149,20 @@ __device__ __forceinline__ v4f scale_tile(float dw_row, float da_col) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(A, B, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 }
 
+// The same outer product for block kb of a phase from binary16 bits as
+// loaded: the B operand is the dword pair of d_a (lanes 0-15) that holds
+// blocks 4 (kb / 4) .. +3 at k = 0..3, and the A operand carries the weight
+// scale at k = kb % 4 alone (x: the scale's bits already in the low half for
+// an even block, the high half for an odd one), so one pair of loaded
+// registers serves four blocks and a block's operands cost one mask.
+__device__ __forceinline__ v4f scale_tile_k4(uint32_t x, int kb, const v4i& da) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i a = (kb & 2) ? v2i{0, (int)x} : v2i{(int)x, 0};
+  const v2i b = (kb & 4) ? v2i{da.z, da.w} : v2i{da.x, da.y};
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, a), __builtin_bit_cast(v4h, b),
+                                              v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+}
+
 template <int MP, int RT, bool kDump, bool kQ8>
 __device__ __forceinline__ void compute_phase(const Phase<MP, RT, kQ8>& P, float (&acc)[RT][MP][4],
                                               uint8_t* stage, int j0, int j1, int n0, int m0,
@@ -176,7 +185,8 @@ __device__ __forceinline__ void compute_phase(const Phase<MP, RT, kQ8>& P, float
     const int pair = j0 + jj;
     const bool live = pair < j1;                   // for the dump (uniform over the wave)
     long A[RT][2];
-    float dw[RT][2];
+    uint32_t dw[RT][2];     // binary16 bits of d_w, row 16 rt + i16: low half (even
+                            // block), high half (odd block)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const uint32_t* u = reinterpret_cast<const uint32_t*>(stage + (16 * rt + i16) * RP) + UW * jj;
@@ -187,13 +197,13 @@ __device__ __forceinline__ void compute_phase(const Phase<MP, RT, kQ8>& P, float
         auto c0 = [&](int q) { return (uint64_t)__builtin_amdgcn_alignbit(u[q + 1], u[q], 16); };
         A[rt][0] = (long)(c0(g) | (c0(4 + g) << 32));
         A[rt][1] = (long)((uint64_t)u[9 + g] | ((uint64_t)u[13 + g] << 32));
-        dw[rt][0] = f16_bits_to_f32(u[0] & 0xFFFFu);
-        dw[rt][1] = f16_bits_to_f32(u[8] >> 16);
+        dw[rt][0] = u[0] & 0xFFFFu;
+        dw[rt][1] = u[8] & 0xFFFF0000u;
       } else {
         A[rt][0] = nibbles_x16(__builtin_amdgcn_alignbit(u[g + 1], u[g], 16));   // even block
         A[rt][1] = nibbles_x16(u[5 + g]);                                       // odd block
-        dw[rt][0] = f16_bits_to_f32(u[0]);                                      // row 16 rt + i16
-        dw[rt][1] = f16_bits_to_f32(u[4] >> 16);
+        dw[rt][0] = u[0] & 0xFFFFu;
+        dw[rt][1] = u[4] & 0xFFFF0000u;
       }
     }
 #pragma unroll
@@ -207,7 +217,7 @@ __device__ __forceinline__ void compute_phase(const Phase<MP, RT, kQ8>& P, float
           const long B = h ? (long)(((uint64_t)(uint32_t)ac.w << 32) | (uint32_t)ac.z)
                            : (long)(((uint64_t)(uint32_t)ac.y << 32) | (uint32_t)ac.x);
           const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt][h], B, v4i{0, 0, 0, 0}, 0, 0, 0);
-          const v4f sc = scale_tile(dw[rt][h], P.da[t][kb]);   // d_w * d_a
+          const v4f sc = scale_tile_k4(dw[rt][h], kb, P.da[t]);   // d_w * d_a
           acc[rt][t][0] = fmaf((float)D.x, sc.x, acc[rt][t][0]);
           acc[rt][t][1] = fmaf((float)D.y, sc.y, acc[rt][t][1]);
           acc[rt][t][2] = fmaf((float)D.z, sc.z, acc[rt][t][2]);
@@ -547,7 +557,7 @@ struct PhaseR {
   v4i w[RT][2];               // code dwords of blocks 0..3 and 4..7 of this lane's row
   v4i sc[RT];                 // the row's 8 scales (binary16)
   v4i act[MP][kPH];
-  float da[MP][2 * kPH];
+  v4i da[MP];                 // d_a (binary16) of the phase's 8 blocks, lanes 0-15
 };
 
 template <int MP, int RT>
@@ -571,12 +581,7 @@ __device__ __forceinline__ void load_phase_r(PhaseR<MP, RT>& P, const Q4Args& a,
 #pragma unroll
     for (int j = 0; j < kPH; ++j) P.act[t][j] = bload128(rq, rv ? qo + 1024 * j : kSkip);
     const bool sv = rv && lane < 16;
-    const v4i s0 = bload128(rs, sv ? (tp * 16 + lane) * 32 : kSkip);
-    const v4i s1 = bload128(rs, sv ? (tp * 16 + lane) * 32 + 16 : kSkip);
-    P.da[t][0] = __int_as_float(s0[0]); P.da[t][1] = __int_as_float(s0[1]);
-    P.da[t][2] = __int_as_float(s0[2]); P.da[t][3] = __int_as_float(s0[3]);
-    P.da[t][4] = __int_as_float(s1[0]); P.da[t][5] = __int_as_float(s1[1]);
-    P.da[t][6] = __int_as_float(s1[2]); P.da[t][7] = __int_as_float(s1[3]);
+    P.da[t] = bload128(rs, sv ? (tp * 16 + lane) * 16 : kSkip);
   }
 }
 
@@ -593,14 +598,14 @@ __device__ __forceinline__ void compute_phase_r(const PhaseR<MP, RT>& P, float (
     for (int rt = 0; rt < RT; ++rt) {
       const long A = nibbles_x16((uint32_t)P.w[rt][kb >> 2][kb & 3]);
       const uint32_t sw = (uint32_t)P.sc[rt][kb >> 1];
-      const float dw = f16_bits_to_f32((kb & 1) ? sw >> 16 : sw);
+      const uint32_t dw = (kb & 1) ? sw & 0xFFFF0000u : sw & 0xFFFFu;
 #pragma unroll
       for (int t = 0; t < MP; ++t) {
         const v4i& ac = P.act[t][kb >> 1];
         const long B = (kb & 1) ? (long)(((uint64_t)(uint32_t)ac.w << 32) | (uint32_t)ac.z)
                                 : (long)(((uint64_t)(uint32_t)ac.y << 32) | (uint32_t)ac.x);
         const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, v4i{0, 0, 0, 0}, 0, 0, 0);
-        const v4f sc = scale_tile(dw, P.da[t][kb]);
+        const v4f sc = scale_tile_k4(dw, kb, P.da[t]);
         acc[rt][t][0] = fmaf((float)D.x, sc.x, acc[rt][t][0]);
         acc[rt][t][1] = fmaf((float)D.y, sc.y, acc[rt][t][1]);
         acc[rt][t][2] = fmaf((float)D.z, sc.z, acc[rt][t][2]);

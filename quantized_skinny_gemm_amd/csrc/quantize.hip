@@ -180,9 +180,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q8_0_skinny(
   uint8_t* base = sq + (((int64_t)t * phases + f) * 4 + j) * 1024 + 8 * e + 4 * h;
 #pragma unroll
   for (int g = 0; g < 4; ++g) *reinterpret_cast<uint32_t*>(base + 16 * (16 * g + i)) = packed[g];
-  // d_a, widened (the kernel narrows it back to binary16 for its fp16 scale
-  // product, exactly)
-  if (h == 0) ss[(((int64_t)t * phases + f) * 16 + i) * 8 + kb] = f16_bits_to_f32(dbits);
+  // d_a as binary16 bits, the 8 blocks of the phase in 16 bytes per row (the
+  // kernel's fp16 scale product takes them as loaded: dword q = blocks 2q,
+  // 2q + 1)
+  if (h == 0)
+    reinterpret_cast<uint16_t*>(ss)[(((int64_t)t * phases + f) * 16 + i) * 8 + kb] = (uint16_t)dbits;
 }
 
 int64_t grid_for(int64_t nblocks, int lanes) { return (nblocks * lanes + kThreads - 1) / kThreads; }
