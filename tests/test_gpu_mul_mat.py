@@ -234,6 +234,29 @@ def test_fused_m2_long_k():
     assert np.array_equal(to_host(qs.mul_mat_q4_0_f32(wq_dev, to_dev(x))), y)
 
 
+# The fused kernel quantizes src1 with four lanes per block where that takes
+# one round of its threads (8-wave workgroups: K <= 4096 at M = 1, 2048 at
+# M = 2), else with two (and always two with 16-wave workgroups, K > 8192):
+# on both sides of each bound, the production call against the oracle and
+# bit for bit against the narrow kernel's dump instantiation (block dots
+# exact), whose codes come from the two-lane routine.
+@pytest.mark.parametrize("m,k", [(1, 4096), (1, 4160), (1, 8192), (1, 8256), (1, 11008),
+                                 (2, 2048), (2, 2112), (2, 4096)])
+def test_fused_src1_lanes_per_block(m, k):
+    qs = _qs()
+    n = 2100                          # enough rows that K is not split
+    rng = np.random.default_rng(1000 * m + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[0, :64] *= 1e-5                 # binary16-subnormal scales in the first blocks
+    wq = codec.quantize_q4_0(w)
+    wq_dev = to_dev(wq)
+    v, split, _, _, launches = qs.dispatch(qs.MM_TYPE_Q4_0, m, n, k)
+    assert (v, split, launches) == (1, 1, 1), "the fused kernel, one launch"
+    y = _check_q4_product(wq_dev, wq, x, f"fused lanes M={m} K={k}", 1, (0, 300))
+    assert np.array_equal(to_host(qs.mul_mat_q4_0_f32(wq_dev, to_dev(x))), y)
+
+
 def test_misaligned_src0_uses_generic_path():
     """src0 at a 2-byte (not 4-byte) offset: the kernels fall back to 16-bit loads."""
     import torch
