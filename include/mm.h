@@ -280,7 +280,8 @@ const char* mm_status_string(int status);
  *   out[3] output tile columns (wide), src0 rows per wave (narrow) or
  *          waves per workgroup (skinny)
  *   out[4] kernels one call launches on the stream (for Q4_0 at small M
- *          the INIT stage is fused into the product kernel: 1)
+ *          the INIT stage is fused into the product kernel: 1; the wide F16
+ *          kernel adds its src1 pre-pass, a K split the reduce)
  * Returns MM_OK or MM_ERR_SHAPE / MM_ERR_ARG.
  */
 int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);

@@ -446,8 +446,11 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
     out[2] = tiled ? p.bm : p.mt;
     out[3] = tiled ? p.bn : p.variant == 3 ? p.waves : p.kind == KK_Q4_NARROW && p.fuse ? p.fuse_rpw : p.rpw;
     const bool q4 = p.type == MM_TYPE_Q4_0 || p.type == MM_TYPE_Q4_0R || p.type == MM_TYPE_Q8_0;
+    // INIT (quantized kinds, unless fused), the src1 pre-pass of the wide
+    // F16 kernel, the product, the split-K reduce
     const int init = (q4 && !(p.kind == KK_Q4_NARROW && p.fuse)) ? 1 : 0;
-    out[4] = init + 1 + (p.split > 1 ? 1 : 0);
+    const int pre = p.kind == KK_F16_WIDE ? 1 : 0;
+    out[4] = init + pre + 1 + (p.split > 1 ? 1 : 0);
   }
   return MM_OK;
 }

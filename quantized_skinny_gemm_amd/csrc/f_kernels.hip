@@ -411,7 +411,7 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
                                                   const uint16_t* __restrict__ xh,
                                                   const int* __restrict__ rexp,
                                                   float* __restrict__ dst, int M, int N, int K,
-                                                  int tiles_m, int tiles_n) {
+                                                  int tiles_m, int tiles_n, int kchunk) {
   constexpr int HP = KS + 8;         // halves per LDS row (pad)
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int WM = WTM / 32, WN = WTN / 32;
@@ -421,6 +421,9 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
   const int t = xcd_remap(blockIdx.x, tiles);
   const int tm = t % tiles_m, tn = t / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
+  // K range of this workgroup (blockIdx.y of a K split; kchunk a multiple of KS)
+  const int kb = (int)blockIdx.y * kchunk;
+  const int ke = kb + kchunk < K ? kb + kchunk : K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / 2, wn = wave % 2;
   const int h = lane >> 5, l32 = lane & 31;
@@ -440,26 +443,26 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
   uint4 xr[NS][XI], wr[NS][WI];
   auto load8 = [&](const uint16_t* base, int row, int k) -> uint4 {
     if (kVec) {
-      const int kk = k < K ? k : 0;                  // K % 8 == 0: k < K means k + 8 <= K
+      const int kk = k < ke ? k : kb;                // K % 8 == 0: k < ke means k + 8 <= ke
       const v4i v = *(const __attribute__((address_space(1))) v4i*)(base + (int64_t)row * K + kk);
       return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
     }
     uint32_t hw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) hw[e] = base[(int64_t)row * K + (k + e < K ? k + e : 0)];
+    for (int e = 0; e < 8; ++e) hw[e] = base[(int64_t)row * K + (k + e < ke ? k + e : kb)];
     return make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16),
                       hw[6] | (hw[7] << 16));
   };
   auto mask8 = [&](uint4 v, bool okrow, int k) -> uint4 {
     if (kVec) {
-      const bool ok = okrow && k < K;
+      const bool ok = okrow && k < ke;
       return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
     }
     uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = (okrow && k + 2 * e < K) ? (d[e] & 0xffffu) : 0u;
-      const uint32_t hi = (okrow && k + 2 * e + 1 < K) ? (d[e] >> 16) : 0u;
+      const uint32_t lo = (okrow && k + 2 * e < ke) ? (d[e] & 0xffffu) : 0u;
+      const uint32_t hi = (okrow && k + 2 * e + 1 < ke) ? (d[e] >> 16) : 0u;
       d[e] = lo | (hi << 16);
     }
     return make_uint4(d[0], d[1], d[2], d[3]);
@@ -519,12 +522,12 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
   static_assert(NS >= 1 && NS <= 3, "one to three register sets");
 
   if constexpr (NS == 1) {
-    load(I0{}, 0);
-    for (int k0 = 0; k0 < K; k0 += KS) {
+    load(I0{}, kb);
+    for (int k0 = kb; k0 < ke; k0 += KS) {
       __syncthreads();                               // the last stage's MFMAs are done
       store(I0{}, k0);
       __syncthreads();
-      if (k0 + KS < K) load(I0{}, k0 + KS);          // uniform over the workgroup
+      if (k0 + KS < ke) load(I0{}, k0 + KS);         // uniform over the workgroup
       compute();
     }
   } else {
@@ -533,16 +536,16 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
     // clamped, the data unused) and kept in issue order by scheduling
     // barriers: the same loads are in flight on every path, so the wait
     // before a stage's store leaves the other sets' loads in flight.
-    load(I0{}, 0);
+    load(I0{}, kb);
     __builtin_amdgcn_sched_barrier(0);
-    load(I1{}, KS);
+    load(I1{}, kb + KS);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NS > 2) {
-      load(I2{}, 2 * KS);
+      load(I2{}, kb + 2 * KS);
       __builtin_amdgcn_sched_barrier(0);
     }
     auto step = [&](auto set, int kk) {
-      const bool live = kk < K;                      // uniform
+      const bool live = kk < ke;                     // uniform
       if (live) {
         __syncthreads();                             // the last stage's MFMAs are done
         store(set, kk);
@@ -552,12 +555,15 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
       __builtin_amdgcn_sched_barrier(0);
       if (live) compute();
     };
-    for (int k0 = 0; k0 < K; k0 += NS * KS) {
+    for (int k0 = kb; k0 < ke; k0 += NS * KS) {
       step(I0{}, k0);
       step(I1{}, k0 + KS);
       if constexpr (NS > 2) step(I2{}, k0 + 2 * KS);
     }
   }
+  // with a K split: this slice's partial tile (scaled back, exact), added by
+  // the split-K reduce
+  float* const out = dst + (int64_t)blockIdx.y * M * N;
 #pragma unroll
   for (int i = 0; i < WM; ++i)
 #pragma unroll
@@ -566,7 +572,7 @@ __global__ __launch_bounds__(256) void k_f16_wide(const uint16_t* __restrict__ w
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * WTM + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-        if (m < M && n < N) dst[(int64_t)m * N + n] = __builtin_amdgcn_ldexpf(acc[i][j][r], -rexp[m]);
+        if (m < M && n < N) out[(int64_t)m * N + n] = __builtin_amdgcn_ldexpf(acc[i][j][r], -rexp[m]);
       }
     }
 }
@@ -615,16 +621,19 @@ hipError_t launch_f16_wide(const Plan& p, const uint16_t* w, const float* x, flo
   if (cvec) hipLaunchKernelGGL((k_f32_to_f16_rows<true>), dim3((unsigned)M), dim3(256), 0, s, x, xh, rexp, K);
   else hipLaunchKernelGGL((k_f32_to_f16_rows<false>), dim3((unsigned)M), dim3(256), 0, s, x, xh, rexp, K);
   const bool vec = (K % 8 == 0) && ((uintptr_t)w % 16 == 0);    // xh is 256-byte aligned
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
-  const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)p.split);
+  const int tm = (int)p.tiles_m, tn = (int)p.tiles_n, kc = (int)p.kchunk;
+  float* out = p.split > 1 ? reinterpret_cast<float*>((uint8_t*)ws + p.off_part) : dst;
   if (p.bm == 128) {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true, 64, 1>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<128, 128, false, 64, 1>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<128, 128, true, 64, 1>), grid, dim3(256), 0, s, w, xh, rexp, out, M, N, K, tm, tn, kc);
+    else hipLaunchKernelGGL((k_f16_wide<128, 128, false, 64, 1>), grid, dim3(256), 0, s, w, xh, rexp, out, M, N, K, tm, tn, kc);
   } else {
-    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true, 128, 3>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
-    else hipLaunchKernelGGL((k_f16_wide<64, 64, false, 128, 1>), grid, dim3(256), 0, s, w, xh, rexp, dst, M, N, K, tm, tn);
+    if (vec) hipLaunchKernelGGL((k_f16_wide<64, 64, true, 128, 3>), grid, dim3(256), 0, s, w, xh, rexp, out, M, N, K, tm, tn, kc);
+    else hipLaunchKernelGGL((k_f16_wide<64, 64, false, 128, 1>), grid, dim3(256), 0, s, w, xh, rexp, out, M, N, K, tm, tn, kc);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && p.split > 1) e = launch_splitk_reduce(out, dst, (int64_t)M * N, p.split, s);
+  return e;
 }
 
 bool f_mma_ok(int type, const void* w, const float* x, int64_t K) {

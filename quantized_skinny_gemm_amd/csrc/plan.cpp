@@ -361,12 +361,38 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
       p->tiles_m = ceil_div(M, p->bm);
       p->tiles_n = ceil_div(N, p->bn);
     }
-    p->kchunk = K;
+    // At most one tile per two CUs: split K (slices of whole k stages, at
+    // least four stages each) for about two workgroups per CU, the partial
+    // tiles added by the split-K reduce (us per call, M = 4 / 64 / 128:
+    // 4096 x 4096 25.9 / 28.1 / 29.1 -> 17.9 / 22.1 / 24.9; 4096 x 14336
+    // 77.2 / 81.0 / 81.8 -> 37.6 / 43.6 / 55.8).  With 172 or 224 tiles
+    // (11008 / 14336 rows) the reduce costs more than it gains (14336 x 4096,
+    // M = 64: 35.3 -> 41.7).
+    const int64_t ks = p->bm == 128 ? 64 : 128;       // k per stage
+    const int64_t stages = ceil_div(K, ks);
+    const int64_t tiles = p->tiles_m * p->tiles_n;
+    int64_t split = 1;
+    if (allow_split && 2 * tiles <= kCUs) {
+      split = ceil_div(2 * kCUs, tiles);
+      if (split > stages / 4) split = stages / 4;
+      if (split > 8) split = 8;
+      if (split < 1) split = 1;
+    }
+    if (allow_split && env_split_k() > 0)              // experiment override
+      split = env_split_k() < stages ? env_split_k() : stages;
+    p->kchunk = ceil_div(stages, split) * ks;
+    p->split = (int)ceil_div(K, p->kchunk);
+    if (p->split < 1) p->split = 1;
     // src1 as binary16 [M][K], converted once (not per tile and stage), and
-    // its power-of-two exponent per row
+    // its power-of-two exponent per row; then the split partials
     p->off_ah = 0;
     p->off_rexp = align_up((size_t)M * (size_t)K * 2, 256);
-    p->ws_bytes = align_up(p->off_rexp + (size_t)M * 4, 256);
+    size_t off = align_up(p->off_rexp + (size_t)M * 4, 256);
+    if (p->split > 1) {
+      p->off_part = off;
+      off = align_up(off + (size_t)p->split * (size_t)M * (size_t)N * 4, 256);
+    }
+    p->ws_bytes = off;
     return MM_OK;
   }
   p->ws_bytes = 0;

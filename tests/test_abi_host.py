@@ -171,8 +171,11 @@ def test_dispatch_threshold_and_workspace(m):
             assert qs.workspace_size(t, m, 4100, 4096) == 0
         elif fv == 2:
             # the wide F16 kernel converts src1 to binary16 in the workspace,
-            # with one power-of-two exponent per row
-            assert fsplit == 1 and qs.workspace_size(t, m, 4100, 4096) >= m * 4096 * 2 + 4 * m
+            # with one power-of-two exponent per row, and with a K split (few
+            # tiles) the partial tiles too
+            part = fsplit * m * 4100 * 4 if fsplit > 1 else 0
+            assert qs.workspace_size(t, m, 4100, 4096) >= m * 4096 * 2 + 4 * m + part
+            assert flaunch == 2 + (1 if fsplit > 1 else 0)
         else:
             assert fsplit == 1 and qs.workspace_size(t, m, 4100, 4096) == 0
 
@@ -261,6 +264,15 @@ def test_measured_tile_and_wave_choices():
     assert qs.dispatch(F16, 16, 11008 + 16, 4096)[:4:3] == (3, 8)
     assert qs.dispatch(F16, 40, 4096 + 16, 4096)[:4:3] == (3, 4)
     assert qs.dispatch(F16, 4, 100, 64)[3] == 4
+    # wide F16: the src1 pre-pass, the product, and with at most one 64 x 64
+    # tile per two CUs a K split (at least four 128-k stages a slice) and its
+    # reduce
+    assert qs.dispatch(F16, 512, 14336 + 16, 4096)[:2] == (2, 1)
+    assert qs.dispatch(F16, 512, 14336 + 16, 4096)[4] == 2
+    v, split, rows, cols, launches = qs.dispatch(F16, 100, 2048 + 16, 4096)   # 66 tiles
+    assert (v, rows, cols) == (2, 64, 64) and 2 <= split <= 8 and launches == 3
+    assert qs.dispatch(F16, 100, 4096 + 16, 4096)[1] == 1        # 130 tiles: no split
+    assert qs.dispatch(F16, 100, 2048 + 16, 512)[1] == 1         # 4 stages: no split
 
 
 def test_noalloc_entry_point_host_checks():
