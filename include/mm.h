@@ -290,7 +290,11 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);
  * mm_debug_mul_mat -- test entry: the same product as mm_mul_mat_<type>,
  * with the kernel forced (variant 0 = as dispatched, 1 = narrow, 2 = wide
  * (Q4_0, Q4_0R, Q8_0 and F16), 3 = skinny MFMA (not Q8_0);
- * MM_ERR_ARG for a variant the type does not have)
+ * MM_ERR_ARG for a variant the type does not have; MM_ERR_SHAPE for the
+ * narrow or skinny kernel of a block type forced on more than 65535 src1
+ * rows, which those kernels' grids cannot hold: mm_mul_mat_* takes the
+ * wide kernel there, and F16 / F32 run such products as several launches
+ * over consecutive row ranges)
  * and, for Q4_0 and Q4_0R, the int32 block dots S_b[m][n][b] of output
  * columns n0 <= n < n1 also written to `dots` ([M][n1-n0][K/32] int32, may
  * be NULL) by the production kernel itself; for Q8_0 by the wide kernel

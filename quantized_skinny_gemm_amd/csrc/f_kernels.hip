@@ -178,20 +178,28 @@ hipError_t launch_f_mt(const Plan& p, const WT* w, const float* x, float* dst, i
                        int K, bool vec, hipStream_t s) {
   // K slices only on the vector path (the scalar path is one wave's)
   const int ks = vec ? p.kslices : 1;
+  if (ks != 1 && ks != 2 && ks != 4) return hipErrorInvalidValue;
   const int64_t rows_per_wg = (int64_t)(4 / ks) * R;
-  const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)p.tiles_m);
-  if (!vec) {
-    hipLaunchKernelGGL((k_f_narrow<WT, MT, R, false, 1>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
-  } else if (ks == 4) {
-    hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true, 4>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
-  } else if (ks == 2) {
-    hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true, 2>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
-  } else if (ks == 1) {
-    hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true, 1>), grid, dim3(256), 0, s, w, x, dst, M, N, K);
-  } else {
-    return hipErrorInvalidValue;
+  // src1 passes of MT rows go in the grid's y dimension: more than
+  // kMaxGridY of them run as launches over consecutive row ranges
+  const int64_t rows = kMaxGridY * MT;
+  for (int64_t r0 = 0; r0 < M; r0 += rows) {
+    const int mc = (int)(M - r0 < rows ? M - r0 : rows);
+    const float* xc = x + r0 * K;
+    float* dc = dst + r0 * N;
+    const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)((mc + MT - 1) / MT));
+    if (!vec)
+      hipLaunchKernelGGL((k_f_narrow<WT, MT, R, false, 1>), grid, dim3(256), 0, s, w, xc, dc, mc, N, K);
+    else if (ks == 4)
+      hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true, 4>), grid, dim3(256), 0, s, w, xc, dc, mc, N, K);
+    else if (ks == 2)
+      hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true, 2>), grid, dim3(256), 0, s, w, xc, dc, mc, N, K);
+    else
+      hipLaunchKernelGGL((k_f_narrow<WT, MT, R, true, 1>), grid, dim3(256), 0, s, w, xc, dc, mc, N, K);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <typename WT>
@@ -645,10 +653,17 @@ bool f_mma_ok(int type, const void* w, const float* x, int64_t K) {
 template <bool kF16, int W, int S, int RT>
 hipError_t launch_f_mma_cfg(const Plan& p, const void* w, const float* x, float* dst, int M, int N,
                             int K, hipStream_t s) {
-  const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m);
-  hipLaunchKernelGGL((k_f_skinny<kF16, W, S, RT>), grid, dim3(64 * W), 0, s, w, x, dst, M, N, K,
-                     (int)p.kchunk);
-  return hipGetLastError();
+  // 16-row src1 passes in the grid's y dimension, at most kMaxGridY per launch
+  const int64_t rows = kMaxGridY * 16;
+  for (int64_t r0 = 0; r0 < M; r0 += rows) {
+    const int mc = (int)(M - r0 < rows ? M - r0 : rows);
+    const dim3 grid((unsigned)p.tiles_n, (unsigned)((mc + 15) / 16));
+    hipLaunchKernelGGL((k_f_skinny<kF16, W, S, RT>), grid, dim3(64 * W), 0, s, w, x + r0 * K,
+                       dst + r0 * N, mc, N, K, (int)p.kchunk);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_f_mma(const Plan& p, int type, const void* w, const float* x, float* dst, int M,

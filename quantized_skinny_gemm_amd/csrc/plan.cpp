@@ -61,7 +61,12 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
   if (q8 && variant == 3 && (K / kQK) % 2) return MM_ERR_ARG;
   if (M == 0 || N == 0) { p->kind = KK_NONE; return MM_OK; }
   if (K == 0) { p->kind = KK_ZERO; return MM_OK; }
-  if (variant == 0) {
+  // The narrow and skinny kernels put src1 row tiles in the grid's y
+  // dimension (at most kMaxGridY workgroups): products of more rows keep to
+  // the built-in rules, which give the block types the wide kernel there
+  // (a one-dimensional grid); the F16 / F32 launchers run such grids as
+  // several launches over consecutive row ranges.
+  if (variant == 0 && M <= kMaxGridY) {
     int tv = dispatch_table_variant(type, M, N, K);
     const int nm = env_narrow_max_m();
     if (nm >= 0 && type == MM_TYPE_Q4_0)             // experiment override
@@ -84,6 +89,7 @@ int make_plan(int type, int64_t M, int64_t N, int64_t K, int variant, Plan* p, b
     const bool narrow = q8 ? q8_fusable && (variant == 1 || (variant == 0 && M <= kFuseMaxM))
                            : !mma && (variant == 1 || (variant == 0 && M <= kNarrowQ4MaxM));
     if (q8 && variant == 1 && !narrow) return MM_ERR_ARG;
+    if ((mma || narrow) && M > kMaxGridY) return MM_ERR_SHAPE;   // forced on too many rows
     // wdata: codes, scales, bias; the codes and scales are followed by 256
     // spare bytes (the skinny kernel's last phase may read up to 7 blocks past
     // the end, and drops them)

@@ -30,6 +30,7 @@ constexpr int kNarrowMaxGrid = 768;  // narrow workgroups along N (3 per CU)
 constexpr int kMmaMaxM = 32;       // largest M the skinny MFMA kernel takes by default
 constexpr int kSkinnyPairs = 4;    // skinny kernel: block pairs per wave phase
 constexpr int64_t kFMmaMaxK = 1 << 23;  // skinny F kernel: 32-bit buffer offsets over 32 rows
+constexpr int64_t kMaxGridY = 65535; // documented limit of a grid's y dimension (workgroups)
 constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;  // mm_mul_mat_q4_0_f32_noalloc's array
 constexpr int kMmaWaves = 8;       // waves per workgroup of the skinny kernel for unaligned
                                    // weights or K % 64 != 0 (32 rows per workgroup)

@@ -134,6 +134,31 @@ def test_debug_entry_argument_checks():
     assert qs.lib.mm_debug_mul_mat(9, FAKE, FAKE, FAKE, None, 1, 64, 64, 0, 0, 0, None, 0, None) == ARG
 
 
+
+def test_tall_products_keep_the_grid_y_limit():
+    """The narrow and skinny kernels put src1 row tiles in the grid's y
+    dimension (at most 65535 workgroups): beyond 65535 rows the block types
+    take the wide kernel whatever the table says, forcing the narrow or
+    skinny kernel there is a shape error (before any HIP call), and F16 /
+    F32 keep their kernels (launched over row ranges)."""
+    R4 = qs.MM_TYPE_Q4_0R
+    Q8 = qs.MM_TYPE_Q8_0
+    for t in (Q4, R4, Q8):
+        assert qs.dispatch(t, 65536, 4096, 4096)[0] == 2
+        for v in (1, 3):
+            assert qs.lib.mm_debug_workspace_size(t, 65536, 4096, 4096, v) == 0
+            assert qs.lib.mm_debug_mul_mat(t, FAKE, FAKE, FAKE, None, 65536, 4096, 4096, 0, 0,
+                                           v, None, 0, None) in (SHAPE, ARG)
+        assert qs.lib.mm_debug_workspace_size(t, 65536, 4096, 4096, 2) > 0
+    # the measured table still applies up to 65535 rows (4096 x 4096: skinny)
+    assert qs.dispatch(Q4, 65535, 4096, 4096)[0] == 3
+    assert qs.lib.mm_debug_workspace_size(Q4, 65535, 4096, 4096, 1) > 0
+    assert qs.dispatch(F32, 2 * 65535 * 16 + 5, 40, 64)[0] == 3
+    assert qs.dispatch(F16, 70000, 40, 64)[0] == 2
+    d = (ctypes.c_int * 5)()
+    assert qs.lib.mm_dispatch(F32, 2 * 65535 * 16 + 5, 40, 64, d) == 0
+
+
 # The built-in rules, at shapes the measured dispatch table does not list
 # (4100 rows); the table itself is tested in test_dispatch_table.py.
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64, 100, 128, 512])

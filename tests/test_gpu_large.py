@@ -58,7 +58,16 @@ def _free():
 
 
 def _check_sampled(y, rows_dev, ref, tol, what):
+    """Output columns rows_dev (sampled weight rows) against ref."""
+    assert int(rows_dev.max()) < y.shape[1] and ref.shape == (y.shape[0], rows_dev.numel())
     ysel = to_host(y[:, rows_dev])
+    assert_close(ysel, ref, tol, what)
+
+
+def _check_rows(y, rows_dev, ref, tol, what):
+    """Output rows rows_dev (sampled src1 rows) against ref."""
+    assert int(rows_dev.max()) < y.shape[0] and ref.shape == (rows_dev.numel(), y.shape[1])
+    ysel = to_host(y[rows_dev])
     assert_close(ysel, ref, tol, what)
 
 
@@ -165,4 +174,54 @@ def test_f16_f32_weights_past_4gib(kind):
         _free()
     assert ({1, 2, 3} if f16 else {1, 3}) <= kinds
     del w
+    _free()
+
+
+@pytest.mark.parametrize("kind", ["f16", "f32"])
+def test_tall_f_products_run_over_row_ranges(kind):
+    """More than 65535 src1 passes: the narrow and skinny F16 / F32 kernels
+    (16-row passes in the grid's y dimension) run as launches over
+    consecutive row ranges of 65535 * 16 rows.  Sampled rows on both sides
+    of each range boundary and the last rows against the oracle, for the
+    kernel the plan picks, each kernel forced, and src1 off its 16-byte
+    alignment (the skinny kernel's fallback to the narrow one)."""
+    import torch
+    qs = _qs()
+    f16 = kind == "f16"
+    mm_type = qs.MM_TYPE_F16 if f16 else qs.MM_TYPE_F32
+    n, k = 40, 64
+    span = 65535 * 16
+    m = 2 * span + 5
+    rng = np.random.default_rng(91 if f16 else 92)
+    w = (rng.standard_normal((n, k)) * 0.5).astype(np.float32)
+    if f16:
+        w = w.astype(np.float16)
+    say("tall f products", kind, f"M={m} N={n} K={k}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(61)
+    xb = torch.randn((m * k + 4,), generator=g, device="cuda")
+    x = xb[:m * k].view(m, k)
+    xm = xb[1:1 + m * k].view(m, k)                  # the same values shifted by one element
+    assert x.data_ptr() % 16 == 0 and xm.data_ptr() % 16 == 4
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(span - 8, span + 8),
+                                     np.arange(2 * span - 8, m)]))
+    rows_dev = torch.from_numpy(rows).cuda()
+    ref_fn = mul_mat.mul_mat_f16_f32 if f16 else mul_mat.mul_mat_f32
+    ref = ref_fn(w, to_host(x[rows_dev]))
+    ref_m = ref_fn(w, to_host(xm[rows_dev]))
+    wd = to_dev(w)
+    for v in (0, 1, 3):
+        what = f"{kind} M={m} variant {v} dispatch={qs.dispatch(mm_type, m, n, k)}"
+        say("tall f products", what)
+        y, _ = qs.debug_mul_mat(mm_type, wd, x, v)
+        _check_rows(y, rows_dev, ref, TOL_F, what)
+        assert bool(torch.isfinite(y).all()), f"{what}: non-finite output"
+        del y
+        _free()
+    say("tall f products", kind, "misaligned src1")
+    fn = qs.mul_mat_f16_f32 if f16 else qs.mul_mat_f32
+    y = fn(wd, xm)
+    _check_rows(y, rows_dev, ref_m, TOL_F, f"{kind} misaligned src1")
+    assert bool(torch.isfinite(y).all())
+    del y, xb, x, xm
     _free()
