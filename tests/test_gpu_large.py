@@ -225,3 +225,58 @@ def test_tall_f_products_run_over_row_ranges(kind):
     assert bool(torch.isfinite(y).all())
     del y, xb, x, xm
     _free()
+
+
+def _host_blocks(n: int, nb: int, block: int, rng) -> np.ndarray:
+    """n x nb random blocks of `block` bytes, bytes 0-1 of each a finite
+    binary16 scale in (-0.01, 0.01)."""
+    w = rng.integers(0, 256, (n, nb, block), dtype=np.uint8)
+    d = ((rng.random((n, nb)) - 0.5) * 0.02).astype(np.float16)
+    w[:, :, 0:2] = d.view(np.uint8).reshape(n, nb, 2)
+    return w.reshape(n, nb * block)
+
+
+@pytest.mark.parametrize("kind,k", [("q4_0", 1 << 20), ("q4_0", (1 << 19) + 32),
+                                    ("q8_0", 1 << 20), ("q8_0", (1 << 19) + 32),
+                                    ("f16", (1 << 20) + 8), ("f32", (1 << 23) + 64)])
+def test_long_k(kind, k):
+    """K from half a million to past 2^23: the narrow kernel's 16-way K split
+    and its reduce, the wide kernel's K split, the skinny kernels' long
+    per-wave K runs, an odd block count (K / 32 odd: no block pairs), and for
+    F32 past 2^23 the skinny kernel's fallback to the narrow one.  Whole
+    outputs against the oracle; Q4_0 block dots of four columns bit for bit."""
+    qs = _qs()
+    n = 24
+    rng = np.random.default_rng(k % 1000 + len(kind))
+    ms = (1, 2, 8, 40, 64) if k == (1 << 20) else (1, 8, 64) if k < (1 << 21) else (1, 2, 8)
+    if kind in ("q4_0", "q8_0"):
+        q8 = kind == "q8_0"
+        mm_type = qs.MM_TYPE_Q8_0 if q8 else qs.MM_TYPE_Q4_0
+        w = _host_blocks(n, k // 32, 34 if q8 else 18, rng)
+        ref_fn = mul_mat.mul_mat_q8_0_f32_dequant if q8 else mul_mat.mul_mat_q4_0_f32_dequant
+        fn = qs.mul_mat_q8_0_f32 if q8 else qs.mul_mat_q4_0_f32
+        tol = TOL_Q4_0
+    else:
+        f16 = kind == "f16"
+        mm_type = qs.MM_TYPE_F16 if f16 else qs.MM_TYPE_F32
+        w = rng.standard_normal((n, k)).astype(np.float16 if f16 else np.float32)
+        ref_fn = mul_mat.mul_mat_f16_f32 if f16 else mul_mat.mul_mat_f32
+        fn = qs.mul_mat_f16_f32 if f16 else qs.mul_mat_f32
+        tol = TOL_F
+    wd = to_dev(w)
+    for m in ms:
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        what = f"{kind} M={m} N={n} K={k} dispatch={qs.dispatch(mm_type, m, n, k)}"
+        say("long k", what)
+        xd = to_dev(x)
+        ref = ref_fn(w, x)
+        assert_close(to_host(fn(wd, xd)), ref, tol, what)
+        if kind == "q4_0":
+            say("long k dots", what)
+            y, dots = qs.debug_mul_mat(mm_type, wd, xd, 0, n - 4, n)
+            assert_close(to_host(y), ref, tol, f"{what} debug")
+            want = codec.block_dots(w[n - 4:], codec.quantize_q8_0(x), k)
+            assert np.array_equal(to_host(dots), want), f"{what}: block dots"
+            del y, dots
+        del xd
+        _free()
