@@ -226,8 +226,8 @@ int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
  *   aligned.  dst: f32, 4-byte aligned.  Any K >= 0.
  *   Precision follows the kernel mm_dispatch reports for the shape.
  *   Narrow kernel (M = 1, and small M where the dispatch table picks it;
- *   any M whose operands are not 16-byte aligned or whose K is not a
- *   multiple of 8): fp32 FMA of src1 as given and the widened weights.
+ *   any M up to the wide kernel's whose operands are not 16-byte aligned
+ *   or whose K is not a multiple of 8 or exceeds 2^23): fp32 FMA of src1 as given and the widened weights.
  *   Skinny kernel (built-in rules: 2 <= M <= 16, and up to 64 with at most
  *   8192 weight rows; the measured table gives it, e.g., 4096 x 4096 up to
  *   45 rows): the same exact fp32 products on the fp32 matrix cores.  Both
@@ -251,8 +251,8 @@ int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst,
  * mm_mul_mat_f32 -- dst[M][N] = src1[M][K] . src0[N][K]^T, all f32 products,
  *   fp32 accumulation.  The F32 x F32 kind of llama.cpp PR 1632 "mulmat
  *   tune", Introduction.  Vector FMA at M = 1; from M = 2 the fp32 MFMA when
- *   src0 and src1 are 16-byte aligned and K is a multiple of 4 (else the
- *   vector kernel).  All pointers 4-byte aligned.  Any K >= 0.
+ *   src0 and src1 are 16-byte aligned and K is a multiple of 4 of at most
+ *   2^23 (else the vector kernel).  All pointers 4-byte aligned.  Any K >= 0.
  *   ws: mm_mul_mat_workspace_size(MM_TYPE_F32, ...) bytes (0 at every shape
  *   today; pass it anyway).
  */
