@@ -76,7 +76,7 @@ typedef enum mm_type {
  * x must be 16-byte aligned; y needs 2-byte alignment.  y must not overlap
  * x.
  */
-int mm_quantize_q4_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream);
+mm_status mm_quantize_q4_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream);
 
 /*
  * mm_quantize_q8_0 -- x[nrows][k] (f32) -> y[nrows][k/32] Q8_0 blocks (34 B each).
@@ -85,7 +85,7 @@ int mm_quantize_q4_0(const float* x, void* y, int64_t nrows, int64_t k, void* st
  * mm_mul_mat_q4_0_f32 computes internally.  k % 32 == 0.  x 16-byte aligned,
  * y 2-byte aligned, no overlap.
  */
-int mm_quantize_q8_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream);
+mm_status mm_quantize_q8_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream);
 
 /*
  * mm_mul_mat_q4_0_f32 -- dst[M][N] (f32) = Q8_0(src1)[M][K] . Q4_0 src0[N][K]^T.
@@ -99,9 +99,9 @@ int mm_quantize_q8_0(const float* x, void* y, int64_t nrows, int64_t k, void* st
  * dst[m][n] = sum_b f32(d_w[n][b]) * f32(d_a[m][b]) * S_b[m][n], with the
  * int32 block dot S_b = sum_j (q4 - 8) * q8, accumulated in fp32.
  */
-int mm_mul_mat_q4_0_f32(const void* src0, const float* src1, float* dst,
-                        int64_t M, int64_t N, int64_t K,
-                        void* ws, size_t ws_bytes, void* stream);
+mm_status mm_mul_mat_q4_0_f32(const void* src0, const float* src1, float* dst,
+                              int64_t M, int64_t N, int64_t K,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mm_mul_mat_q4_0_f32_noalloc -- mm_mul_mat_q4_0_f32 without a caller
@@ -118,8 +118,8 @@ int mm_mul_mat_q4_0_f32(const void* src0, const float* src1, float* dst,
  *   calls that may overlap in time on one GPU (different streams, or
  *   different host threads) race and must be serialised by the caller.
  */
-int mm_mul_mat_q4_0_f32_noalloc(const void* src0, const float* src1, float* dst,
-                                int64_t M, int64_t N, int64_t K, void* stream);
+mm_status mm_mul_mat_q4_0_f32_noalloc(const void* src0, const float* src1, float* dst,
+                                      int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * The two stages of mm_mul_mat_q4_0_f32, exposed separately (llama.cpp PR
@@ -138,10 +138,10 @@ int mm_mul_mat_q4_0_f32_noalloc(const void* src0, const float* src1, float* dst,
  *   (e.g. the q, k and v projections of one activation).  Calls that share a
  *   workspace must not overlap in time.
  */
-int mm_q4_0_init(const float* src1, void* ws, int64_t M, int64_t N, int64_t K,
-                 size_t ws_bytes, void* stream);
-int mm_q4_0_compute(const void* src0, float* dst, int64_t M, int64_t N, int64_t K,
-                    const void* ws, size_t ws_bytes, void* stream);
+mm_status mm_q4_0_init(const float* src1, void* ws, int64_t M, int64_t N, int64_t K,
+                       size_t ws_bytes, void* stream);
+mm_status mm_q4_0_compute(const void* src0, float* dst, int64_t M, int64_t N, int64_t K,
+                          const void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mm_mul_mat_q4_0_f32_group -- several Q4_0 products that share src1, in as
@@ -153,9 +153,9 @@ int mm_q4_0_compute(const void* src0, float* dst, int64_t M, int64_t N, int64_t 
  * each other or any src0.  Results equal count separate mm_mul_mat_q4_0_f32
  * calls.  ws: mm_mul_mat_q4_0_group_workspace_size(count, Ns, M, K) bytes.
  */
-int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const* dsts,
-                              const int64_t* Ns, const float* src1, int64_t M, int64_t K,
-                              void* ws, size_t ws_bytes, void* stream);
+mm_status mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const* dsts,
+                                    const int64_t* Ns, const float* src1, int64_t M, int64_t K,
+                                    void* ws, size_t ws_bytes, void* stream);
 size_t mm_mul_mat_q4_0_group_workspace_size(int count, const int64_t* Ns, int64_t M, int64_t K);
 
 /*
@@ -189,11 +189,11 @@ size_t mm_mul_mat_q4_0_group_workspace_size(int count, const int64_t* Ns, int64_
  * Errors as for the other entry points (MM_ERR_SHAPE for K % 32 != 0).
  */
 int64_t mm_repacked_q4_0_bytes(int64_t N, int64_t K);
-int mm_repack_q4_0(const void* src0, void* dst, int64_t N, int64_t K, void* stream);
-int mm_unpack_q4_0(const void* src0r, void* dst, int64_t N, int64_t K, void* stream);
-int mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst,
-                         int64_t M, int64_t N, int64_t K,
-                         void* ws, size_t ws_bytes, void* stream);
+mm_status mm_repack_q4_0(const void* src0, void* dst, int64_t N, int64_t K, void* stream);
+mm_status mm_unpack_q4_0(const void* src0r, void* dst, int64_t N, int64_t K, void* stream);
+mm_status mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst,
+                               int64_t M, int64_t N, int64_t K,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mm_mul_mat_q8_0_f32 -- dst[M][N] (f32) = Q8_0(src1)[M][K] . Q8_0 src0[N][K]^T.
@@ -214,9 +214,9 @@ int mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst,
  * workgroup, passes of 8, 16 or 32 src1 rows); otherwise INIT, then the
  * tiled int8 MFMA kernel.
  */
-int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
-                        int64_t M, int64_t N, int64_t K,
-                        void* ws, size_t ws_bytes, void* stream);
+mm_status mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
+                              int64_t M, int64_t N, int64_t K,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mm_mul_mat_f16_f32 -- dst[M][N] = src1[M][K] . f32(src0[N][K])^T, fp32 accumulation.
@@ -227,7 +227,8 @@ int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
  *   Precision follows the kernel mm_dispatch reports for the shape.
  *   Narrow kernel (M = 1, and small M where the dispatch table picks it;
  *   any M up to the wide kernel's whose operands are not 16-byte aligned
- *   or whose K is not a multiple of 8 or exceeds 2^23): fp32 FMA of src1 as given and the widened weights.
+ *   or whose K is not a multiple of 8 or exceeds 2^23): fp32 FMA of src1
+ *   as given and the widened weights.
  *   Skinny kernel (built-in rules: 2 <= M <= 16, and up to 64 with at most
  *   8192 weight rows; the measured table gives it, e.g., 4096 x 4096 up to
  *   45 rows): the same exact fp32 products on the fp32 matrix cores.  Both
@@ -243,9 +244,9 @@ int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
  *   ws: mm_mul_mat_workspace_size(MM_TYPE_F16, ...) bytes (0 when that is
  *   0); for the larger M it holds src1 as binary16 and the row exponents.
  */
-int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst,
-                       int64_t M, int64_t N, int64_t K,
-                       void* ws, size_t ws_bytes, void* stream);
+mm_status mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst,
+                             int64_t M, int64_t N, int64_t K,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * mm_mul_mat_f32 -- dst[M][N] = src1[M][K] . src0[N][K]^T, all f32 products,
@@ -256,9 +257,9 @@ int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst,
  *   ws: mm_mul_mat_workspace_size(MM_TYPE_F32, ...) bytes (0 at every shape
  *   today; pass it anyway).
  */
-int mm_mul_mat_f32(const float* src0, const float* src1, float* dst,
-                   int64_t M, int64_t N, int64_t K,
-                   void* ws, size_t ws_bytes, void* stream);
+mm_status mm_mul_mat_f32(const float* src0, const float* src1, float* dst,
+                         int64_t M, int64_t N, int64_t K,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace the product of `type` (F32, F16, Q4_0, Q8_0 or Q4_0R)
  * needs at this shape; 0 for an invalid shape or type.  Pure host function. */
@@ -284,7 +285,7 @@ const char* mm_status_string(int status);
  *          kernel adds its src1 pre-pass, a K split the reduce)
  * Returns MM_OK or MM_ERR_SHAPE / MM_ERR_ARG.
  */
-int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);
+mm_status mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);
 
 /*
  * mm_debug_mul_mat -- test entry: the same product as mm_mul_mat_<type>,
@@ -301,10 +302,10 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out);
  * only (MM_ERR_ARG when the call would take the fused narrow kernel).
  * Workspace: mm_debug_workspace_size().
  */
-int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst,
-                     int32_t* dots, int64_t M, int64_t N, int64_t K,
-                     int64_t n0, int64_t n1, int variant,
-                     void* ws, size_t ws_bytes, void* stream);
+mm_status mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst,
+                           int32_t* dots, int64_t M, int64_t N, int64_t K,
+                           int64_t n0, int64_t n1, int variant,
+                           void* ws, size_t ws_bytes, void* stream);
 
 size_t mm_debug_workspace_size(int type, int64_t M, int64_t N, int64_t K, int variant);
 

@@ -208,97 +208,111 @@ int repack(const void* src, void* dst, int64_t N, int64_t K, bool to_repacked, v
 
 }  // namespace
 
+// Status codes travel as int inside the library; the C entry points return
+// them as the header's enum.
+inline mm_status as_status(int st) { return static_cast<mm_status>(st); }
+
 extern "C" {
 
-int mm_quantize_q4_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream) {
-  return quantize(MM_TYPE_Q4_0, x, y, nrows, k, stream);
+mm_status mm_quantize_q4_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream) {
+  return as_status(quantize(MM_TYPE_Q4_0, x, y, nrows, k, stream));
 }
 
-int mm_quantize_q8_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream) {
-  return quantize(MM_TYPE_Q8_0, x, y, nrows, k, stream);
+mm_status mm_quantize_q8_0(const float* x, void* y, int64_t nrows, int64_t k, void* stream) {
+  return as_status(quantize(MM_TYPE_Q8_0, x, y, nrows, k, stream));
 }
 
-int mm_mul_mat_q4_0_f32(const void* src0, const float* src1, float* dst, int64_t M, int64_t N,
-                        int64_t K, void* ws, size_t ws_bytes, void* stream) {
-  return mul_mat(MM_TYPE_Q4_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+mm_status mm_mul_mat_q4_0_f32(const void* src0, const float* src1, float* dst,
+                              int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return as_status(
+      mul_mat(MM_TYPE_Q4_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream));
 }
 
-int mm_mul_mat_q4_0_f32_noalloc(const void* src0, const float* src1, float* dst, int64_t M,
-                                int64_t N, int64_t K, void* stream) {
+mm_status mm_mul_mat_q4_0_f32_noalloc(const void* src0, const float* src1, float* dst, int64_t M,
+                                      int64_t N, int64_t K, void* stream) {
   // the plan first: a shape whose workspace does not fit the array is
   // rejected before any HIP call
   Plan p;
   int st = make_plan(MM_TYPE_Q4_0, M, N, K, 0, &p);
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   if (p.ws_bytes > kNoAllocScratchBytes) return MM_ERR_WORKSPACE;
   if (p.kind == KK_NONE) return MM_OK;
   st = validate_mul_mat(MM_TYPE_Q4_0, src0, src1, dst, M, N, K, nullptr, 0, p, STAGE_ALL,
                         /*check_ws=*/false);
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   st = check_device();
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   void* ws = scratch_ptr(&st);
-  if (!ws) return st;
-  return mul_mat(MM_TYPE_Q4_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws,
-                 kNoAllocScratchBytes, stream);
+  if (!ws) return as_status(st);
+  return as_status(mul_mat(MM_TYPE_Q4_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws,
+                 kNoAllocScratchBytes, stream));
 }
 
-int mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst, int64_t M, int64_t N,
-                        int64_t K, void* ws, size_t ws_bytes, void* stream) {
-  return mul_mat(MM_TYPE_Q8_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+mm_status mm_mul_mat_q8_0_f32(const void* src0, const float* src1, float* dst,
+                              int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return as_status(
+      mul_mat(MM_TYPE_Q8_0, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream));
 }
 
-int mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst, int64_t M, int64_t N,
-                         int64_t K, void* ws, size_t ws_bytes, void* stream) {
-  return mul_mat(MM_TYPE_Q4_0R, src0r, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+mm_status mm_mul_mat_q4_0r_f32(const void* src0r, const float* src1, float* dst,
+                               int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                               void* stream) {
+  return as_status(
+      mul_mat(MM_TYPE_Q4_0R, src0r, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream));
 }
 
 int64_t mm_repacked_q4_0_bytes(int64_t N, int64_t K) { return repacked_bytes(N, K); }
 
-int mm_repack_q4_0(const void* src0, void* dst, int64_t N, int64_t K, void* stream) {
-  return repack(src0, dst, N, K, /*to_repacked=*/true, stream);
+mm_status mm_repack_q4_0(const void* src0, void* dst, int64_t N, int64_t K, void* stream) {
+  return as_status(repack(src0, dst, N, K, /*to_repacked=*/true, stream));
 }
 
-int mm_unpack_q4_0(const void* src0r, void* dst, int64_t N, int64_t K, void* stream) {
-  return repack(src0r, dst, N, K, /*to_repacked=*/false, stream);
+mm_status mm_unpack_q4_0(const void* src0r, void* dst, int64_t N, int64_t K, void* stream) {
+  return as_status(repack(src0r, dst, N, K, /*to_repacked=*/false, stream));
 }
 
-int mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst, int64_t M,
-                       int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
-  return mul_mat(MM_TYPE_F16, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+mm_status mm_mul_mat_f16_f32(const uint16_t* src0, const float* src1, float* dst, int64_t M,
+                             int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  return as_status(
+      mul_mat(MM_TYPE_F16, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream));
 }
 
-int mm_mul_mat_f32(const float* src0, const float* src1, float* dst, int64_t M, int64_t N,
-                   int64_t K, void* ws, size_t ws_bytes, void* stream) {
-  return mul_mat(MM_TYPE_F32, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream);
+mm_status mm_mul_mat_f32(const float* src0, const float* src1, float* dst,
+                         int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return as_status(
+      mul_mat(MM_TYPE_F32, src0, src1, dst, nullptr, M, N, K, 0, 0, 0, ws, ws_bytes, stream));
 }
 
-int mm_q4_0_init(const float* src1, void* ws, int64_t M, int64_t N, int64_t K, size_t ws_bytes,
-                 void* stream) {
+mm_status mm_q4_0_init(const float* src1, void* ws, int64_t M, int64_t N, int64_t K,
+                       size_t ws_bytes, void* stream) {
   Plan p;
   int st = make_plan(MM_TYPE_Q4_0, M, N, K, 0, &p);
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   st = validate_mul_mat(MM_TYPE_Q4_0, nullptr, src1, nullptr, M, N, K, ws, ws_bytes, p, STAGE_INIT);
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   if (p.kind == KK_NONE || p.kind == KK_ZERO) return MM_OK;
   st = check_device();
-  if (st != MM_OK) return st;
-  return q4_init(p, src1, M, K, ws, (hipStream_t)stream);
+  if (st != MM_OK) return as_status(st);
+  return as_status(q4_init(p, src1, M, K, ws, (hipStream_t)stream));
 }
 
-int mm_q4_0_compute(const void* src0, float* dst, int64_t M, int64_t N, int64_t K,
-                    const void* ws, size_t ws_bytes, void* stream) {
+mm_status mm_q4_0_compute(const void* src0, float* dst, int64_t M, int64_t N, int64_t K,
+                          const void* ws, size_t ws_bytes, void* stream) {
   Plan p;
   int st = make_plan(MM_TYPE_Q4_0, M, N, K, 0, &p);
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   st = validate_mul_mat(MM_TYPE_Q4_0, src0, nullptr, dst, M, N, K, ws, ws_bytes, p, STAGE_COMPUTE);
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   if (p.kind == KK_NONE) return MM_OK;
   st = check_device();
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   hipStream_t s = (hipStream_t)stream;
-  if (p.kind == KK_ZERO) return hip_status(launch_zero(dst, M * N, s));
-  return q4_product(p, q4_args(p, src0, dst, nullptr, M, N, K, 0, 0, (void*)ws), nullptr, s);
+  if (p.kind == KK_ZERO) return as_status(hip_status(launch_zero(dst, M * N, s)));
+  return as_status(
+      q4_product(p, q4_args(p, src0, dst, nullptr, M, N, K, 0, 0, (void*)ws), nullptr, s));
 }
 
 namespace {
@@ -350,14 +364,14 @@ size_t mm_mul_mat_q4_0_group_workspace_size(int count, const int64_t* Ns, int64_
   return ws;
 }
 
-int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const* dsts,
-                              const int64_t* Ns, const float* src1, int64_t M, int64_t K,
-                              void* ws, size_t ws_bytes, void* stream) {
+mm_status mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const* dsts,
+                                    const int64_t* Ns, const float* src1, int64_t M, int64_t K,
+                                    void* ws, size_t ws_bytes, void* stream) {
   Plan whole;
   int64_t ntot = 0;
   size_t need = 0;
   int st = group_plan(count, Ns, M, K, &whole, &ntot, &need);
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   if (!src0s || !dsts) return MM_ERR_NULL;
   if (M == 0 || ntot == 0) return MM_OK;
   // each product on its own, then the group as a whole
@@ -367,7 +381,7 @@ int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const*
     Plan pi = whole;
     pi.ws_bytes = need;
     st = validate_mul_mat(MM_TYPE_Q4_0, src0s[i], src1, dsts[i], M, Ns[i], K, ws, ws_bytes, pi);
-    if (st != MM_OK) return st;
+    if (st != MM_OK) return as_status(st);
     for (int j = 0; j < count; ++j) {
       if (j == i || Ns[j] == 0) continue;
       if (ranges_overlap(dsts[i], (size_t)M * Ns[i] * 4, dsts[j], (size_t)M * Ns[j] * 4) ||
@@ -376,13 +390,13 @@ int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const*
     }
   }
   st = check_device();
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   hipStream_t s = (hipStream_t)stream;
   if (K == 0) {
     for (int i = 0; i < count; ++i) {
       if (Ns[i] == 0) continue;
       st = hip_status(launch_zero(dsts[i], M * Ns[i], s));
-      if (st != MM_OK) return st;
+      if (st != MM_OK) return as_status(st);
     }
     return MM_OK;
   }
@@ -403,20 +417,20 @@ int mm_mul_mat_q4_0_f32_group(int count, const void* const* src0s, float* const*
     const Q4Args a = q4_args(whole, mats.w[0], mats.dst[0], nullptr, M, ntot, K, 0, 0, ws);
     if (!whole.fuse) {
       st = q4_init(whole, src1, M, K, ws, s);
-      if (st != MM_OK) return st;
+      if (st != MM_OK) return as_status(st);
     }
-    return hip_status(launch_q4_narrow(whole, a, mats, whole.fuse ? src1 : nullptr, s));
+    return as_status(hip_status(launch_q4_narrow(whole, a, mats, whole.fuse ? src1 : nullptr, s)));
   }
   // wide and skinny MFMA: one INIT, then one product per matrix (same wdata
   // layout at the front of every per-matrix plan)
   st = q4_init(whole, src1, M, K, ws, s);
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   for (int i = 0; i < count; ++i) {
     if (Ns[i] == 0) continue;
     Plan pi;
     make_plan(MM_TYPE_Q4_0, M, Ns[i], K, whole.variant, &pi);
     st = q4_product(pi, q4_args(pi, src0s[i], dsts[i], nullptr, M, Ns[i], K, 0, 0, ws), nullptr, s);
-    if (st != MM_OK) return st;
+    if (st != MM_OK) return as_status(st);
   }
   return MM_OK;
 }
@@ -435,10 +449,10 @@ size_t mm_debug_workspace_size(int type, int64_t M, int64_t N, int64_t K, int va
 
 int64_t mm_row_bytes(int type, int64_t K) { return row_bytes(type, K); }
 
-int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
+mm_status mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
   Plan p;
   const int st = make_plan(type, M, N, K, 0, &p);
-  if (st != MM_OK) return st;
+  if (st != MM_OK) return as_status(st);
   if (out) {
     out[0] = p.variant;
     out[1] = p.split;
@@ -455,9 +469,9 @@ int mm_dispatch(int type, int64_t M, int64_t N, int64_t K, int* out) {
   return MM_OK;
 }
 
-int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* dots,
-                     int64_t M, int64_t N, int64_t K, int64_t n0, int64_t n1, int variant,
-                     void* ws, size_t ws_bytes, void* stream) {
+mm_status mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst, int32_t* dots,
+                           int64_t M, int64_t N, int64_t K, int64_t n0, int64_t n1, int variant,
+                           void* ws, size_t ws_bytes, void* stream) {
   if (variant < 0 || variant > 3) return MM_ERR_ARG;
   if (n0 < 0 || n1 < n0 || n1 > N) return MM_ERR_SHAPE;
   if ((type != MM_TYPE_Q4_0 && type != MM_TYPE_Q4_0R && type != MM_TYPE_Q8_0) || n1 == n0)
@@ -467,10 +481,11 @@ int mm_debug_mul_mat(int type, const void* src0, const float* src1, float* dst, 
     // Q8_0 weights: only the wide kernel writes block dots
     Plan p;
     const int st = make_plan(type, M, N, K, variant, &p);
-    if (st != MM_OK) return st;
+    if (st != MM_OK) return as_status(st);
     if (p.kind == KK_Q4_NARROW) return MM_ERR_ARG;
   }
-  return mul_mat(type, src0, src1, dst, dots, M, N, K, n0, n1, variant, ws, ws_bytes, stream);
+  return as_status(
+      mul_mat(type, src0, src1, dst, dots, M, N, K, n0, n1, variant, ws, ws_bytes, stream));
 }
 
 const char* mm_status_string(int status) {

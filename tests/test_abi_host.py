@@ -33,6 +33,31 @@ def test_header_declares_the_five_entry_points():
         assert n in names
 
 
+def test_header_is_plain_c_and_returns_mm_status():
+    """include/mm.h compiles as C99 (plain pointers and sizes, no C++ or HIP
+    types), and every call that reports a status declares the mm_status enum."""
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        with open(c, "w") as f:
+            f.write('#include "mm.h"\nint main(void) { return mm_status_string(MM_OK) == 0; }\n')
+        r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                            "-I", os.path.dirname(HEADER), c], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for n in ("mm_quantize_q4_0", "mm_quantize_q8_0", "mm_mul_mat_q4_0_f32",
+              "mm_mul_mat_q4_0_f32_noalloc", "mm_q4_0_init", "mm_q4_0_compute",
+              "mm_mul_mat_q4_0_f32_group", "mm_repack_q4_0", "mm_unpack_q4_0",
+              "mm_mul_mat_q4_0r_f32", "mm_mul_mat_q8_0_f32", "mm_mul_mat_f16_f32",
+              "mm_mul_mat_f32", "mm_dispatch", "mm_debug_mul_mat"):
+        assert re.search(r"\bmm_status\s+%s\s*\(" % n, src), n
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(qs.LIB_PATH)
     for n in _declared():
