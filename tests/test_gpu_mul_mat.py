@@ -379,6 +379,39 @@ def test_deterministic_run_to_run():
         assert bool(torch.equal(a, b)), m
 
 
+def test_concurrent_streams_match_serial():
+    """Products of every kernel kind issued on two streams at once (each call
+    with its own dst and workspace) give the same bits as the same calls run
+    one after another: no kernel keeps state outside the caller's buffers."""
+    import torch
+    qs = _qs()
+    n, k = 4096, 4096
+    wq_dev, _ = _q4_weights(3, 1, n, k)
+    w16 = to_dev(workloads.weights_f16(workloads.weight_seed(2, 0), n, k))
+    cases = []
+    for m in (1, 2, 8, 40, 512):
+        x = to_dev(workloads.activations(workloads.activation_seed(3, m), m, k))
+        cases.append((qs.mul_mat_q4_0_f32, wq_dev, x))
+    for m in (1, 4, 100):
+        x = to_dev(workloads.activations(workloads.activation_seed(2, m), m, k))
+        cases.append((qs.mul_mat_f16_f32, w16, x))
+    say("concurrent streams", len(cases), "calls")
+    serial = [fn(w, x) for fn, w, x in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(y) for y in serial]
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for i, (fn, w, x) in enumerate(cases):
+            with torch.cuda.stream(streams[i % 2]):
+                fn(w, x, out=outs[i])
+        torch.cuda.synchronize()
+        for i, (y, o) in enumerate(zip(serial, outs)):
+            assert bool(torch.equal(y, o)), f"call {i} (rep {rep}) differs on its own stream"
+
+
 def test_batch_vs_alone():
     """Row m of a batched product equals the M=1 product of that row (within
     tolerance across kernels; the Q8_0 wdata of the row is identical)."""
