@@ -412,6 +412,65 @@ def test_concurrent_streams_match_serial():
             assert bool(torch.equal(y, o)), f"call {i} (rep {rep}) differs on its own stream"
 
 
+def test_graph_capture_replays_match_eager():
+    """Every launch sequence the library issues (fused; INIT + skinny; INIT +
+    wide + split-K reduce; INIT + wide; F16 pre-pass + wide + reduce; F16
+    pre-pass + wide; skinny F16 / F32; narrow F16) captured once into a HIP
+    graph and replayed three times, with other products run eagerly on the
+    same buffers' neighbours between the replays: every replay gives the
+    eager bits."""
+    import torch
+    qs = _qs()
+    rng = np.random.default_rng(5)
+    mats = {}
+
+    def weights(kind, n, k):
+        key = (kind, n, k)
+        if key not in mats:
+            w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+            mats[key] = (qs.quantize_q4_0(to_dev(w)) if kind == "q4_0"
+                         else to_dev(w.astype(np.float16)) if kind == "f16" else to_dev(w))
+        return mats[key]
+
+    shapes = [("q4_0", 1, 4096, 4096), ("q4_0", 8, 4096, 14336), ("q4_0", 128, 4096, 14336),
+              ("q4_0", 512, 14336, 4096), ("f16", 100, 4096, 14336), ("f16", 64, 14336, 4096),
+              ("f16", 4, 4096, 4096), ("f32", 16, 4096, 4096), ("f16", 1, 4096, 4096)]
+    fns = {"q4_0": (qs.mul_mat_q4_0_f32, qs.MM_TYPE_Q4_0), "f16": (qs.mul_mat_f16_f32, qs.MM_TYPE_F16),
+           "f32": (qs.mul_mat_f32, qs.MM_TYPE_F32)}
+    calls = []
+    for kind, m, n, k in shapes:
+        fn, t = fns[kind]
+        x = to_dev(rng.standard_normal((m, k)).astype(np.float32))
+        out = torch.empty((m, n), device="cuda")
+        ws = torch.empty(max(qs.workspace_size(t, m, n, k), 1), dtype=torch.uint8, device="cuda")
+        calls.append((fn, weights(kind, n, k), x, out, ws, f"{kind} M={m} {n}x{k} {qs.dispatch(t, m, n, k)}"))
+    say("graph capture", len(calls), "calls")
+    eager = []
+    for fn, w, x, out, ws, what in calls:
+        fn(w, x, out=out, ws=ws)
+        eager.append(out.clone())
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for fn, w, x, out, ws, what in calls:
+            fn(w, x, out=out, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for _, _, _, out, ws, _ in calls:
+            out.fill_(float("nan"))
+            ws.fill_(0xA5)
+        # other eager products between the replays
+        for fn, w, x, _, _, _ in calls[:3]:
+            fn(w, x)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (_, _, _, out, _, what), ref in zip(calls, eager):
+            assert bool(torch.equal(out, ref)), f"replay {rep}: {what}"
+
+
 def test_batch_vs_alone():
     """Row m of a batched product equals the M=1 product of that row (within
     tolerance across kernels; the Q8_0 wdata of the row is identical)."""
