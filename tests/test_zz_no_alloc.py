@@ -51,6 +51,49 @@ def test_noalloc_equals_workspace_entry_point():
         assert_close(to_host(got), ref, TOL_Q4_0, f"noalloc call {i}")
 
 
+def test_noalloc_calls_replayed_from_a_hip_graph():
+    """The callers this entry point is for capture it: calls captured into a
+    HIP graph (the wide kernel with split-K partials and the skinny kernel
+    with its operand-order wdata, both in the shared array) replayed three
+    times, with eager no-allocation calls of other shapes rewriting the array
+    between the replays, give the workspace entry point's bits every time."""
+    import torch
+    import quantized_skinny_gemm_amd as qs
+    rng = np.random.default_rng(977)
+    cap = []
+    for m, n, k in ((128, 4096, 14336), (8, 2000, 2048)):
+        wq = codec.quantize_q4_0((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+        x_dev = to_dev(rng.standard_normal((m, k)).astype(np.float32))
+        wq_dev = to_dev(wq)
+        want = qs.mul_mat_q4_0_f32(wq_dev, x_dev)
+        cap.append((wq_dev, x_dev, torch.empty((m, n), device="cuda"), want,
+                    f"M={m} {n}x{k} {qs.dispatch(qs.MM_TYPE_Q4_0, m, n, k)}"))
+    others = []
+    for m, n, k in ((512, 4096, 4096), (16, 3000, 1024)):
+        wq_dev = to_dev(codec.quantize_q4_0((rng.standard_normal((n, k)) * 0.02).astype(np.float32)))
+        others.append((wq_dev, to_dev(rng.standard_normal((m, k)).astype(np.float32)),
+                       torch.empty((m, n), device="cuda")))
+    say("noalloc graph", [c[4] for c in cap])
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for wq_dev, x_dev, out, _, _ in cap:
+            _call_noalloc(qs, wq_dev, x_dev, out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for _, _, out, _, _ in cap:
+            out.fill_(float("nan"))
+        for wq_dev, x_dev, out in others:
+            _call_noalloc(qs, wq_dev, x_dev, out)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for _, _, out, want, what in cap:
+            assert bool(torch.equal(out, want)), f"replay {rep}: {what}"
+
+
 def test_noalloc_rejects_oversize_shape_and_launches_nothing():
     import torch
     import quantized_skinny_gemm_amd as qs
