@@ -300,6 +300,12 @@ def test_misaligned_f16_f32_operands(m):
     assert fv.data_ptr() % 16 == 4
     assert_close(to_host(qs.mul_mat_f16_f32(hv, xv)), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, "f16")
     assert_close(to_host(qs.mul_mat_f32(fv, xv)), mul_mat.mul_mat_f32(w, x), TOL_F, "f32")
+    # the wide F16 kernel forced on the same operands: element-wise weight
+    # loads (src0 off 16 bytes) and src1 conversion (src1 off 16 bytes)
+    y, _ = qs.debug_mul_mat(qs.MM_TYPE_F16, hv, xv, 2)
+    assert_close(to_host(y), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, "f16 wide")
+    y, _ = qs.debug_mul_mat(qs.MM_TYPE_F16, to_dev(wh), xv, 2)
+    assert_close(to_host(y), mul_mat.mul_mat_f16_f32(wh, x), TOL_F, "f16 wide, aligned src0")
     # aligned weights, misaligned src1 only
     assert_close(to_host(qs.mul_mat_f16_f32(to_dev(wh), xv)), mul_mat.mul_mat_f16_f32(wh, x), TOL_F,
                  "f16 aligned src0")
