@@ -263,14 +263,19 @@ def test_misaligned_src0_uses_generic_path():
     rng = np.random.default_rng(9)
     n, k = 96, 1024
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
-    x = rng.standard_normal((5, k)).astype(np.float32)
     wq = codec.quantize_q4_0(w)
     buf = torch.zeros(wq.size + 16, dtype=torch.uint8, device="cuda")
     view = buf[2:2 + wq.size].view(n, wq.shape[1])
     view.copy_(torch.from_numpy(wq).cuda())
     assert view.data_ptr() % 4 == 2
-    for v in (1, 2, 3):
-        _check_q4_product(view, wq, x, "misaligned", v, (0, 8))
+    # M <= 2: the fused kernel needs 4-byte aligned weights, so the general
+    # narrow kernel quantizes src1 in LDS instead
+    for m in (1, 2, 5):
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        for v in (0, 1, 2, 3):
+            _check_q4_product(view, wq, x, f"misaligned M={m}", v, (0, 8))
+        y = to_host(_qs().mul_mat_q4_0_f32(view, to_dev(x)))
+        assert_close(y, mul_mat.mul_mat_q4_0_f32_dequant(wq, x), TOL_Q4_0, f"misaligned M={m}")
 
 
 @pytest.mark.parametrize("m", [5, 40])
